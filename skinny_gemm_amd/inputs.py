@@ -1,0 +1,124 @@
+"""Seeded synthetic inputs for the quantized skinny-GEMV path.
+
+This module only draws random numbers and stores them in the byte layouts the
+library takes.  It holds none of the method's arithmetic: no quantizer, no
+decode, no dot product.  Format encodings it needs to *produce* weights
+(binary16 and E4M3 rounding of drawn reals) are library casts (numpy's
+float16, torch's float8_e4m3fn), after clamping to the finite E4M3 range.
+Both the GPU tests and the oracle side take their inputs from here.
+
+Distributions (one per workload):
+  * Q4_0 weights: 4-bit codes uniform over 0..15 (a uniform random byte is
+    two independent uniform codes), scales d ~ U[0.002, 0.02] rounded to
+    binary16.
+  * Q8_1 source activations: float32 N(0, 1), one independent row per M.
+  * NVFP4 weights: E2M1 codes uniform over all 16 code points (uniform
+    bytes), one E4M3 scale per 16 elements with scale = e4m3(u / 6),
+    u ~ U[0.01, 0.1], so the largest decodable magnitude 6 * scale spans
+    U[0.01, 0.1]; per-tensor scale 1.0.
+  * FP8 weights: E4M3 of N(0, 0.05) (clamped to +-448, round to nearest
+    even); per-output-channel float32 scales ~ U[0.5, 2].
+  * binary16 activations: N(0, 1) drawn in float64, rounded to binary16.
+
+Seeds: ``seed(config, shape, tensor)`` = 1000*config + 10*shape + tensor,
+tensor 0 = codes/weights, 1 = scales, 2 = activations.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+E4M3_MAX = 448.0
+
+
+def seed(config: int, shape: int, tensor: int) -> int:
+    return 1000 * int(config) + 10 * int(shape) + int(tensor)
+
+
+def _rng(s: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(int(s)))
+
+
+def _e4m3_bytes(v: np.ndarray) -> np.ndarray:
+    """Round reals to E4M3 (torch's round-to-nearest-even cast) after
+    clamping to the finite range, returned as raw bytes."""
+    import torch
+
+    v = np.clip(np.asarray(v, np.float32), -E4M3_MAX, E4M3_MAX)
+    t = torch.from_numpy(np.ascontiguousarray(v)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy().copy()
+
+
+# ---------------------------------------------------------------- host (numpy)
+
+def q4_0_weights(N: int, K: int, base_seed: int):
+    """-> (w_qs uint8 [N][K/2], w_d uint16 [N][K/32] binary16 bits)."""
+    w_qs = _rng(base_seed + 0).integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    d = _rng(base_seed + 1).uniform(0.002, 0.02, size=(N, K // 32))
+    w_d = d.astype(np.float16).view(np.uint16)
+    return w_qs, w_d
+
+
+def normal_f32(M: int, K: int, s: int) -> np.ndarray:
+    return _rng(s).standard_normal(size=(M, K), dtype=np.float32)
+
+
+def normal_f16_bits(M: int, K: int, s: int, std: float = 1.0) -> np.ndarray:
+    x = _rng(s).standard_normal(size=(M, K)) * std
+    return x.astype(np.float16).view(np.uint16)
+
+
+def nvfp4_weights(N: int, K: int, base_seed: int, global_scale: float = 1.0):
+    """-> (codes uint8 [N][K/2], scales uint8 E4M3 [N][K/16], g float)."""
+    codes = _rng(base_seed + 0).integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    u = _rng(base_seed + 1).uniform(0.01, 0.1, size=(N, K // 16))
+    scales = _e4m3_bytes(u / 6.0)
+    return codes, scales, float(global_scale)
+
+
+def fp8_weights(N: int, K: int, base_seed: int):
+    """-> (w uint8 E4M3 [N][K], cs float32 [N])."""
+    w = _e4m3_bytes(_rng(base_seed + 0).normal(0.0, 0.05, size=(N, K)))
+    cs = _rng(base_seed + 1).uniform(0.5, 2.0, size=(N,)).astype(np.float32)
+    return w, cs
+
+
+def q8_1_unit_scale_source(M: int, K: int, s: int) -> np.ndarray:
+    """float32 integer-valued activations for the exact-integer gate.
+
+    Every 32-block holds one entry of +-127 and 31 entries in [-60, 60], so
+    its Q8_1 scale is exactly 1, its codes equal the inputs, and the code
+    sum (|sum| <= 127 + 31*60 = 1987) is an integer binary16 holds exactly.
+    """
+    r = _rng(s)
+    x = r.integers(-60, 61, size=(M, K)).astype(np.float32)
+    nb = K // 32
+    pos = r.integers(0, 32, size=(M, nb))
+    sign = np.where(r.integers(0, 2, size=(M, nb)) == 0, -127.0, 127.0)
+    rows = np.repeat(np.arange(M), nb)
+    cols = (np.tile(np.arange(nb), M) * 32 + pos.ravel())
+    x[rows, cols] = sign.ravel()
+    return x
+
+
+# ---------------------------------------------------------------- device (torch)
+
+def q4_0_weights_torch(N: int, K: int, base_seed: int, device):
+    """Device-side draw with the same distributions as ``q4_0_weights`` (a
+    different stream of numbers), for weight sets too large to draw on the
+    host.  -> (w_qs uint8 [N][K/2], w_d int16 [N][K/32] binary16 bits)."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(base_seed))
+    w_qs = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device=device, generator=g)
+    u = torch.rand((N, K // 32), dtype=torch.float32, device=device, generator=g)
+    w_d = (0.002 + 0.018 * u).to(torch.float16).view(torch.int16)
+    return w_qs, w_d
+
+
+def normal_f32_torch(M: int, K: int, s: int, device):
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(s))
+    return torch.randn((M, K), dtype=torch.float32, device=device, generator=g)
