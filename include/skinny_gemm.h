@@ -1,0 +1,150 @@
+/*
+ * skinny_gemm.h -- C ABI of libskinny_gemm.so: block-quantized matrix x
+ * vector and skinny GEMM (M = 1..8 activation rows) for LLM decode and
+ * speculative verification on AMD Instinct MI355X (gfx950).
+ *
+ * Sources.  "Machine Learning on NVIDIA CMP" (sections "TL;DR", "llama.cpp
+ * results", "The DP2A patch") describes decode as a quantized mat x vec
+ * (MMVQ) over Q4_0 weights whose inner loop is a 4-way int8 dot with int32
+ * accumulation, and requires any rewrite of that dot to stay bit-exact
+ * integer arithmetic.  "v100-skinny README" (sections "Result", "How QPN
+ * works", "Native mixed-precision checkpoint path") describes W4A16 NVFP4
+ * and W8A16 FP8 skinny GEMMs at verification width M <= 8: packed weights
+ * stay compressed in memory and are decoded only where consumed, the NVFP4
+ * global scale is folded into the group-16 scales, and every 16-element
+ * group is flushed into an FP32 accumulator so that binary16 cannot
+ * overflow.  The pages leave the activation format, nibble order and FP8
+ * scale granularity open; the readings taken are stated per function.
+ *
+ * Conventions shared by every entry point.
+ *   - Every pointer is a device pointer on the current HIP device; `stream`
+ *     is a hipStream_t passed as void* (NULL = the default stream).
+ *   - The caller allocates and owns every buffer.  The library allocates
+ *     nothing, keeps no state between calls, and is safe to call from
+ *     several host threads.  Outputs must not overlap inputs.
+ *   - A call validates its arguments on the host before any HIP call, then
+ *     enqueues one kernel on `stream` and returns without synchronizing.
+ *     Faults during execution surface at the caller's next synchronization.
+ *   - binary16 values are passed as their 16-bit patterns (uint16_t).
+ *   - A call with M == 0 or N == 0 has nothing to compute: it returns
+ *     SKINNY_OK without touching memory (pointers may then be NULL).
+ *   - There is exactly one code path per entry point; nothing falls back.
+ *
+ * Status codes (return values):
+ */
+#ifndef SKINNY_GEMM_H
+#define SKINNY_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SKINNY_OK               0
+#define SKINNY_ERR_NULL        -1  /* a required pointer is NULL                    */
+#define SKINNY_ERR_SHAPE       -2  /* K or N out of range, or K not a multiple of   */
+                                   /* the format's block (see each function)        */
+#define SKINNY_ERR_ALIGN       -3  /* a pointer is not aligned as required          */
+#define SKINNY_ERR_M           -4  /* M outside 0..8 (GEMV entry points)            */
+#define SKINNY_ERR_LAUNCH      -5  /* the HIP launch reported an error              */
+
+/* Limits: 1 <= K <= SKINNY_MAX_K, 0 <= N <= SKINNY_MAX_N. */
+#define SKINNY_MAX_K  (1 << 20)
+#define SKINNY_MAX_N  (1 << 28)
+#define SKINNY_MAX_M_GEMV   8
+#define SKINNY_MAX_M_QUANT  65536
+
+/* Static, human-readable text for a status code. */
+const char *skinny_status_string(int status);
+
+/*
+ * quantize_act_q8_1 -- quantize activation rows to Q8_1.
+ *
+ * The activation side of the quantized mat x vec kernel ("Machine Learning
+ * on NVIDIA CMP", "TL;DR" and "The DP2A patch": the dot consumes int8 codes).
+ * For each row m and each block b of 32 consecutive elements:
+ *   amax = max |x|;  if amax == 0 all outputs of the block are 0;
+ *   d32  = amax / 127                         (binary32, correctly rounded)
+ *   q_i  = round_half_away_from_zero(x_i / d32), clamped to [-127, 127]
+ *   d    = binary16(d32),  s = binary16(d32 * sum_i q_i)   (round to nearest even)
+ *
+ *   x   float32 [M][K] row-major, 16-byte aligned.
+ *   qs  int8    [M][K] row-major, 16-byte aligned.
+ *   d   binary16 [M][K/32], 2-byte aligned.
+ *   s   binary16 [M][K/32], 2-byte aligned.
+ *   0 <= M <= SKINNY_MAX_M_QUANT; K % 32 == 0.
+ * Results are bit-exact (one correct answer per input).  NaN or infinite
+ * inputs give unspecified codes.
+ */
+int quantize_act_q8_1(const float *x, int M, int K,
+                      int8_t *qs, uint16_t *d, uint16_t *s, void *stream);
+
+/*
+ * mmvq_q4_0 -- y = A * W^T for Q4_0 weights and Q8_1 activations.
+ *
+ * "Machine Learning on NVIDIA CMP", "llama.cpp results" and "The DP2A
+ * patch": MMVQ with a 4-way int8 dot per 32-element block.
+ * Weights, planar Q4_0: w_qs [N][K/2] bytes (byte j of block b holds code
+ * 32b+j in its low nibble and code 32b+16+j in its high nibble), w_d
+ * binary16 [N][K/32]; weight = (code - 8) * d.  Activations from
+ * quantize_act_q8_1.  For each m, n:
+ *   y[m][n] = sum_b d4[n][b] * (d8[m][b] * isum - 8 * s8[m][b]),
+ *   isum    = sum_{i<32} code[n][32b+i] * q8[m][32b+i]   (exact int32),
+ * i.e. the -8 of every weight is applied once per block through the Q8_1
+ * sum term.  Accumulated in float32, output float32.
+ *
+ *   w_qs 16-byte aligned; w_d, a_d, a_s 2-byte aligned; a_qs 16-byte
+ *   aligned; y float32 [M][N] row-major, 4-byte aligned.
+ *   0 <= M <= 8; K % 32 == 0.
+ * Block sums are exact integers; the float result matches the definition
+ * to float32 summation-order rounding.
+ */
+int mmvq_q4_0(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
+              const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
+              int M, float *y, void *stream);
+
+/*
+ * gemv_nvfp4_w4a16 -- y = x * W^T for NVFP4 weights and binary16 activations.
+ *
+ * "v100-skinny README", "How QPN works": E2M1 codes with an E4M3 scale per
+ * 16 elements and a per-tensor scale folded into the group scales; FP32
+ * accumulation per 16-element group.
+ *   w_codes  [N][K/2] bytes: element 2j of a row in the low nibble of byte
+ *            j, element 2j+1 in the high nibble.  16-byte aligned.
+ *   w_scales [N][K/16] OCP E4M3 ("FN") bytes, one per 16 elements.
+ *            2-byte aligned.
+ *   global_scale  per-tensor float32 multiplier.
+ *   x        binary16 [M][K] row-major, 16-byte aligned.
+ *   y        binary16 [M][N] row-major, 2-byte aligned:
+ *            y = binary16( sum_j (sum_{i<16} e2m1 * x) * (e4m3(scale_j) * g) ),
+ *            accumulated in float32, rounded to nearest even once.
+ *   0 <= M <= 8; K % 32 == 0.
+ */
+int gemv_nvfp4_w4a16(const uint8_t *w_codes, const uint8_t *w_scales,
+                     float global_scale, int N, int K,
+                     const uint16_t *x, int M, uint16_t *y, void *stream);
+
+/*
+ * gemv_fp8_w8a16 -- y = x * W^T for FP8 E4M3 weights and binary16 activations.
+ *
+ * "v100-skinny README", "How QPN works": one contiguous E4M3 byte stream
+ * per weight matrix.  The pages do not give the scale granularity; here it
+ * is one float32 scale per output channel, applied after the dot.
+ *   w   [N][K] OCP E4M3 ("FN") bytes, 16-byte aligned.
+ *   channel_scale float32 [N], 4-byte aligned.
+ *   x   binary16 [M][K] row-major, 16-byte aligned.
+ *   y   binary16 [M][N] row-major, 2-byte aligned:
+ *       y = binary16( channel_scale[n] * sum_k e4m3(w[n][k]) * x[m][k] ),
+ *       accumulated in float32.
+ *   0 <= M <= 8; K % 16 == 0.  NaN weight codes (0x7F, 0xFF) give
+ *   unspecified results.
+ */
+int gemv_fp8_w8a16(const uint8_t *w, const float *channel_scale, int N, int K,
+                   const uint16_t *x, int M, uint16_t *y, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKINNY_GEMM_H */

@@ -1,0 +1,19 @@
+"""skinny_gemm_amd -- block-quantized matrix x vector and skinny GEMM
+(M = 1..8) for AMD Instinct MI355X (gfx950).
+
+The computation lives in libskinny_gemm.so (hand-written HIP kernels behind
+the C ABI declared in include/skinny_gemm.h).  This package is its thin
+Python binding (same names as the C entry points) plus the build script and
+the seeded synthetic input generators.
+"""
+from ._lib import (  # noqa: F401
+    EXPORTS,
+    SkinnyError,
+    gemv_fp8_w8a16,
+    gemv_nvfp4_w4a16,
+    lib,
+    library_path,
+    mmvq_q4_0,
+    quantize_act_q8_1,
+    status_string,
+)

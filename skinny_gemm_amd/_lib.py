@@ -1,0 +1,188 @@
+"""ctypes binding of libskinny_gemm.so.
+
+Argument marshalling only: each function checks tensor dtypes, shapes,
+device and contiguity, allocates outputs that were not supplied (torch is
+used for device memory and streams, nothing else), and calls the C entry of
+the same name on the current stream.  Every step of the computation runs in
+the library's HIP kernels.  A missing library raises immediately; there is
+no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libskinny_gemm.so")
+
+OK = 0
+ERR_NULL = -1
+ERR_SHAPE = -2
+ERR_ALIGN = -3
+ERR_M = -4
+ERR_LAUNCH = -5
+
+EXPORTS = ("skinny_status_string", "quantize_act_q8_1", "mmvq_q4_0",
+           "gemv_nvfp4_w4a16", "gemv_fp8_w8a16")
+
+_lib = None
+
+
+class SkinnyError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__("%s failed with status %d (%s)" % (fn, status, text))
+        self.status = status
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def lib():
+    """Load libskinny_gemm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libskinny_gemm.so is not built (%s); run "
+                           "`python -m skinny_gemm_amd.build`" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    L.skinny_status_string.argtypes = [I]
+    L.skinny_status_string.restype = ctypes.c_char_p
+    L.quantize_act_q8_1.argtypes = [P, I, I, P, P, P, P]
+    L.quantize_act_q8_1.restype = I
+    L.mmvq_q4_0.argtypes = [P, P, I, I, P, P, P, I, P, P]
+    L.mmvq_q4_0.restype = I
+    L.gemv_nvfp4_w4a16.argtypes = [P, P, ctypes.c_float, I, I, P, I, P, P]
+    L.gemv_nvfp4_w4a16.restype = I
+    L.gemv_fp8_w8a16.argtypes = [P, P, I, I, P, I, P, P]
+    L.gemv_fp8_w8a16.restype = I
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().skinny_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != OK:
+        raise SkinnyError(fn, status, status_string(status))
+
+
+# ------------------------------------------------------------- marshalling
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _req(t, name, dtypes, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype not in dtypes:
+        raise TypeError("%s: dtype %s not in %s" % (name, t.dtype, dtypes))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU device" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s: shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    return t
+
+
+def _f16_bits_dtypes():
+    torch = _torch()
+    return (torch.float16, torch.int16, torch.uint16)
+
+
+def quantize_act_q8_1(x, qs=None, d=None, s=None, stream=None):
+    """x float32 [M][K] -> (qs int8 [M][K], d, s binary16 [M][K/32])."""
+    torch = _torch()
+    _req(x, "x", (torch.float32,))
+    M, K = x.shape
+    if qs is None:
+        qs = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if d is None:
+        d = torch.empty((M, K // 32), dtype=torch.float16, device=x.device)
+    if s is None:
+        s = torch.empty((M, K // 32), dtype=torch.float16, device=x.device)
+    _req(qs, "qs", (torch.int8,), (M, K))
+    _req(d, "d", _f16_bits_dtypes(), (M, K // 32))
+    _req(s, "s", _f16_bits_dtypes(), (M, K // 32))
+    _check("quantize_act_q8_1",
+           lib().quantize_act_q8_1(_ptr(x), M, K, _ptr(qs), _ptr(d), _ptr(s), _stream(stream)))
+    return qs, d, s
+
+
+def mmvq_q4_0(w_qs, w_d, a_qs, a_d, a_s, y=None, stream=None):
+    """Q4_0 weights [N][K/2] + [N][K/32], Q8_1 activations -> y float32 [M][N]."""
+    torch = _torch()
+    _req(w_qs, "w_qs", (torch.uint8,))
+    N, K2 = w_qs.shape
+    K = 2 * K2
+    _req(w_d, "w_d", _f16_bits_dtypes(), (N, K // 32))
+    _req(a_qs, "a_qs", (torch.int8,))
+    M = a_qs.shape[0]
+    _req(a_qs, "a_qs", (torch.int8,), (M, K))
+    _req(a_d, "a_d", _f16_bits_dtypes(), (M, K // 32))
+    _req(a_s, "a_s", _f16_bits_dtypes(), (M, K // 32))
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=w_qs.device)
+    _req(y, "y", (torch.float32,), (M, N))
+    _check("mmvq_q4_0", lib().mmvq_q4_0(_ptr(w_qs), _ptr(w_d), N, K, _ptr(a_qs), _ptr(a_d),
+                                         _ptr(a_s), M, _ptr(y), _stream(stream)))
+    return y
+
+
+def gemv_nvfp4_w4a16(w_codes, w_scales, global_scale, x, y=None, stream=None):
+    """NVFP4 weights [N][K/2] codes + [N][K/16] E4M3 scales, binary16 x [M][K]
+    -> binary16 y [M][N]."""
+    torch = _torch()
+    _req(w_codes, "w_codes", (torch.uint8,))
+    N, K2 = w_codes.shape
+    K = 2 * K2
+    _req(w_scales, "w_scales", (torch.uint8, torch.float8_e4m3fn), (N, K // 16))
+    _req(x, "x", _f16_bits_dtypes())
+    M = x.shape[0]
+    _req(x, "x", _f16_bits_dtypes(), (M, K))
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    _req(y, "y", _f16_bits_dtypes(), (M, N))
+    _check("gemv_nvfp4_w4a16",
+           lib().gemv_nvfp4_w4a16(_ptr(w_codes), _ptr(w_scales), float(global_scale), N, K,
+                                  _ptr(x), M, _ptr(y), _stream(stream)))
+    return y
+
+
+def gemv_fp8_w8a16(w, channel_scale, x, y=None, stream=None):
+    """FP8 E4M3 weights [N][K], float32 channel scales [N], binary16 x [M][K]
+    -> binary16 y [M][N]."""
+    torch = _torch()
+    _req(w, "w", (torch.uint8, torch.float8_e4m3fn))
+    N, K = w.shape
+    _req(channel_scale, "channel_scale", (torch.float32,), (N,))
+    _req(x, "x", _f16_bits_dtypes())
+    M = x.shape[0]
+    _req(x, "x", _f16_bits_dtypes(), (M, K))
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    _req(y, "y", _f16_bits_dtypes(), (M, N))
+    _check("gemv_fp8_w8a16", lib().gemv_fp8_w8a16(_ptr(w), _ptr(channel_scale), N, K, _ptr(x), M,
+                                                   _ptr(y), _stream(stream)))
+    return y

@@ -1,0 +1,94 @@
+// abi.hip -- the exported C entry points: host-side argument validation,
+// then one kernel launch on the caller's stream.  Validation makes no HIP
+// call, so it runs (and is tested) on machines without a GPU.  An invalid
+// call returns its status code and enqueues nothing; a valid call never
+// switches to another kernel.
+#include <stdint.h>
+
+#include "launch.h"
+#include "skinny_gemm.h"
+
+namespace {
+
+inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+inline int shape_status(int N, int K, int kmult) {
+  if (K <= 0 || K > SKINNY_MAX_K || (K % kmult) != 0) return SKINNY_ERR_SHAPE;
+  if (N < 0 || N > SKINNY_MAX_N) return SKINNY_ERR_SHAPE;
+  return SKINNY_OK;
+}
+
+inline int gemv_m_status(int M) {
+  if (M < 0 || M > SKINNY_MAX_M_GEMV) return SKINNY_ERR_M;
+  return SKINNY_OK;
+}
+
+inline int launched(hipError_t e) { return e == hipSuccess ? SKINNY_OK : SKINNY_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char *skinny_status_string(int status) {
+  switch (status) {
+    case SKINNY_OK: return "ok";
+    case SKINNY_ERR_NULL: return "null pointer argument";
+    case SKINNY_ERR_SHAPE: return "unsupported shape (K or N out of range, or K not a multiple of the block)";
+    case SKINNY_ERR_ALIGN: return "misaligned pointer argument";
+    case SKINNY_ERR_M: return "unsupported number of activation rows M";
+    case SKINNY_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int quantize_act_q8_1(const float *x, int M, int K, int8_t *qs, uint16_t *d, uint16_t *s,
+                      void *stream) {
+  if (M < 0 || M > SKINNY_MAX_M_QUANT) return SKINNY_ERR_M;
+  if (K <= 0 || K > SKINNY_MAX_K || (K % 32) != 0) return SKINNY_ERR_SHAPE;
+  if (M == 0) return SKINNY_OK;
+  if (!x || !qs || !d || !s) return SKINNY_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(qs, 16) || !aligned(d, 2) || !aligned(s, 2))
+    return SKINNY_ERR_ALIGN;
+  return launched(skinny::launch_quantize_q8_1(x, M, K, qs, d, s, (hipStream_t)stream));
+}
+
+int mmvq_q4_0(const uint8_t *w_qs, const uint16_t *w_d, int N, int K, const int8_t *a_qs,
+              const uint16_t *a_d, const uint16_t *a_s, int M, float *y, void *stream) {
+  int st = gemv_m_status(M);
+  if (st) return st;
+  if ((st = shape_status(N, K, 32))) return st;
+  if (M == 0 || N == 0) return SKINNY_OK;
+  if (!w_qs || !w_d || !a_qs || !a_d || !a_s || !y) return SKINNY_ERR_NULL;
+  if (!aligned(w_qs, 16) || !aligned(a_qs, 16) || !aligned(w_d, 2) || !aligned(a_d, 2) ||
+      !aligned(a_s, 2) || !aligned(y, 4))
+    return SKINNY_ERR_ALIGN;
+  return launched(skinny::launch_mmvq_q4_0(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y,
+                                           (hipStream_t)stream));
+}
+
+int gemv_nvfp4_w4a16(const uint8_t *w_codes, const uint8_t *w_scales, float global_scale,
+                     int N, int K, const uint16_t *x, int M, uint16_t *y, void *stream) {
+  int st = gemv_m_status(M);
+  if (st) return st;
+  if ((st = shape_status(N, K, 32))) return st;
+  if (M == 0 || N == 0) return SKINNY_OK;
+  if (!w_codes || !w_scales || !x || !y) return SKINNY_ERR_NULL;
+  if (!aligned(w_codes, 16) || !aligned(w_scales, 2) || !aligned(x, 16) || !aligned(y, 2))
+    return SKINNY_ERR_ALIGN;
+  return launched(skinny::launch_gemv_nvfp4(w_codes, w_scales, global_scale, N, K, x, M, y,
+                                            (hipStream_t)stream));
+}
+
+int gemv_fp8_w8a16(const uint8_t *w, const float *channel_scale, int N, int K,
+                   const uint16_t *x, int M, uint16_t *y, void *stream) {
+  int st = gemv_m_status(M);
+  if (st) return st;
+  if ((st = shape_status(N, K, 16))) return st;
+  if (M == 0 || N == 0) return SKINNY_OK;
+  if (!w || !channel_scale || !x || !y) return SKINNY_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(channel_scale, 4) || !aligned(x, 16) || !aligned(y, 2))
+    return SKINNY_ERR_ALIGN;
+  return launched(skinny::launch_gemv_fp8(w, channel_scale, N, K, x, M, y, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,165 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/skinny_gemm.h declares, and rejects bad arguments on the host with
+the documented status codes before making any HIP call.
+
+Only invalid calls (and the M == 0 / N == 0 no-ops, which return before any
+HIP call) are made here; nothing is launched.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "skinny_gemm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import skinny_gemm_amd
+
+    return skinny_gemm_amd.lib()
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(["skinny_status_string", "quantize_act_q8_1",
+                                           "mmvq_q4_0", "gemv_nvfp4_w4a16", "gemv_fp8_w8a16"])
+
+
+def test_library_exports_every_declared_symbol(L):
+    import skinny_gemm_amd
+
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", skinny_gemm_amd.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for name in declared_functions():
+        assert name in exported, name
+
+
+def test_status_strings(L):
+    import skinny_gemm_amd
+
+    for code in (0, -1, -2, -3, -4, -5):
+        assert skinny_gemm_amd.status_string(code) != "unknown status"
+    assert skinny_gemm_amd.status_string(7) == "unknown status"
+
+
+A = 0x10000          # a 16-byte aligned stand-in address (never dereferenced)
+V = ctypes.c_void_p
+
+
+def q4(L, w=A, wd=A, N=64, K=256, aq=A, ad=A, as_=A, M=1, y=A):
+    return L.mmvq_q4_0(V(w), V(wd), N, K, V(aq), V(ad), V(as_), M, V(y), None)
+
+
+def nv(L, c=A, s=A, N=64, K=256, x=A, M=1, y=A):
+    return L.gemv_nvfp4_w4a16(V(c), V(s), 1.0, N, K, V(x), M, V(y), None)
+
+
+def f8(L, w=A, cs=A, N=64, K=256, x=A, M=1, y=A):
+    return L.gemv_fp8_w8a16(V(w), V(cs), N, K, V(x), M, V(y), None)
+
+
+def qa(L, x=A, M=1, K=256, qs=A, d=A, s=A):
+    return L.quantize_act_q8_1(V(x), M, K, V(qs), V(d), V(s), None)
+
+
+@pytest.mark.parametrize("fn", [q4, nv, f8])
+def test_gemv_rejects_m_out_of_range(L, fn):
+    assert fn(L, M=9) == -4
+    assert fn(L, M=-1) == -4
+    assert fn(L, M=1000) == -4
+
+
+@pytest.mark.parametrize("fn,kmult", [(q4, 32), (nv, 32), (f8, 16)])
+def test_gemv_rejects_bad_shapes(L, fn, kmult):
+    assert fn(L, K=0) == -2
+    assert fn(L, K=-32) == -2
+    assert fn(L, K=kmult + kmult // 2) == -2
+    assert fn(L, K=(1 << 20) + kmult) == -2
+    assert fn(L, N=-1) == -2
+    assert fn(L, N=(1 << 28) + 1) == -2
+    # the largest K passes shape validation (stopped here by a NULL pointer)
+    assert fn(L, K=1 << 20, y=0) == -1
+
+
+def test_fp8_accepts_k_multiple_of_16(L):
+    assert f8(L, K=48, y=0) == -1
+    assert q4(L, K=48, y=0) == -2
+    assert nv(L, K=48, y=0) == -2
+
+
+def test_gemv_null_pointers(L):
+    for kw in ("w", "wd", "aq", "ad", "as_", "y"):
+        assert q4(L, **{kw: 0}) == -1, kw
+    for kw in ("c", "s", "x", "y"):
+        assert nv(L, **{kw: 0}) == -1, kw
+    for kw in ("w", "cs", "x", "y"):
+        assert f8(L, **{kw: 0}) == -1, kw
+
+
+def test_gemv_misaligned(L):
+    for kw, off in (("w", 8), ("aq", 4), ("wd", 1), ("ad", 1), ("as_", 1), ("y", 2)):
+        assert q4(L, **{kw: A + off}) == -3, kw
+    for kw, off in (("c", 8), ("s", 1), ("x", 8), ("y", 1)):
+        assert nv(L, **{kw: A + off}) == -3, kw
+    for kw, off in (("w", 8), ("cs", 2), ("x", 8), ("y", 1)):
+        assert f8(L, **{kw: A + off}) == -3, kw
+    # the weaker requirements really are weaker
+    assert q4(L, wd=A + 2, y=0) == -1
+    assert nv(L, s=A + 2, y=0) == -1
+
+
+def test_empty_calls_are_noops(L):
+    # M == 0 or N == 0: nothing to compute, pointers may be NULL, no HIP call
+    assert q4(L, w=0, wd=0, aq=0, ad=0, as_=0, y=0, M=0) == 0
+    assert q4(L, w=0, wd=0, aq=0, ad=0, as_=0, y=0, N=0) == 0
+    assert nv(L, c=0, s=0, x=0, y=0, M=0) == 0
+    assert nv(L, c=0, s=0, x=0, y=0, N=0) == 0
+    assert f8(L, w=0, cs=0, x=0, y=0, M=0) == 0
+    assert f8(L, w=0, cs=0, x=0, y=0, N=0) == 0
+    assert qa(L, x=0, qs=0, d=0, s=0, M=0) == 0
+
+
+def test_quantize_validation(L):
+    assert qa(L, K=48) == -2
+    assert qa(L, K=0) == -2
+    assert qa(L, M=-1) == -4
+    assert qa(L, M=65537) == -4
+    assert qa(L, x=0) == -1
+    assert qa(L, s=0) == -1
+    assert qa(L, x=A + 4) == -3
+    assert qa(L, qs=A + 8) == -3
+    assert qa(L, d=A + 1) == -3
+
+
+def test_binding_raises_without_gpu_tensors():
+    import torch
+
+    import skinny_gemm_amd
+
+    with pytest.raises(ValueError):
+        skinny_gemm_amd.gemv_fp8_w8a16(torch.zeros((4, 16), dtype=torch.uint8),
+                                       torch.ones(4), torch.zeros((1, 16), dtype=torch.float16))
+    with pytest.raises(TypeError):
+        skinny_gemm_amd.quantize_act_q8_1(torch.zeros((1, 32), dtype=torch.float64))
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    from skinny_gemm_amd import _lib
+
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.lib()

@@ -1,0 +1,414 @@
+"""GPU parity: every entry point against the CPU oracle, element by element,
+through the C ABI (via the thin binding), on seeded synthetic inputs.
+
+Bars:
+  * Q8_1 bytes (codes, d, s): bit-exact.
+  * Q4_0 integer gate (unit scales, integer activations): bit-exact.
+  * Q4_0 float32 output: normwise max|y - y_ref| / max|y_ref| <= 1e-3, and
+    per element |y - y_ref| <= (K/32 + 8) * 2^-24 * mag, the float32
+    summation bound (mag = sum over blocks of |d4| (|d8 isum| + 8 |s8|)).
+  * binary16 outputs: normwise <= 2e-2, and per element
+    |y - y_acc| <= 2^-10 |y_acc| + (K + 64) * 2^-24 * mag + 2^-24
+    (one binary16 rounding plus float32 summation; mag = sum |w x|).
+  * Exhaustive decode cases (every E4M3 code, every E2M1 x E4M3 pair):
+    bit-exact, the products being exact in binary16.
+The oracle is the reference throughout; nothing here derives an expected
+value from the GPU.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from conftest import gpu_available
+from skinny_gemm_amd import inputs
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+# ------------------------------------------------------------------ helpers
+
+def dev(a):
+    import torch
+
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+def host(t, dtype=None):
+    import torch
+
+    torch.cuda.synchronize()
+    a = t.cpu().numpy()
+    if dtype is not None:
+        a = a.view(dtype)
+    return a
+
+
+def f16(bits):
+    return np.asarray(bits, np.uint16).view(np.float16).astype(np.float64)
+
+
+def e4m3_table():
+    return np.array([oracle.e4m3_to_double(b) for b in range(256)])
+
+
+def e2m1_table():
+    return np.array([oracle.e2m1_to_double(c) for c in range(16)])
+
+
+def unpack_q4_0(w_qs):
+    N, K2 = w_qs.shape
+    b = w_qs.reshape(N, K2 // 16, 16)
+    return np.concatenate([b & 15, b >> 4], axis=2).reshape(N, 2 * K2).astype(np.int64)
+
+
+def unpack_nvfp4(codes):
+    out = np.empty((codes.shape[0], 2 * codes.shape[1]), np.int64)
+    out[:, 0::2] = codes & 15
+    out[:, 1::2] = codes >> 4
+    return out
+
+
+def check_f32(y, ref, mag, K, what):
+    err = np.abs(y.astype(np.float64) - ref)
+    norm = err.max() / max(np.abs(ref).max(), 1e-300)
+    assert norm <= 1e-3, "%s: normwise %.3g" % (what, norm)
+    bound = (K / 32 + 8) * 2.0 ** -24 * mag
+    bad = err > bound
+    assert not bad.any(), "%s: %d elements over the float32 bound, worst %s" % (
+        what, bad.sum(), np.unravel_index(np.argmax(err - bound), err.shape))
+
+
+def check_f16(y_bits, y_acc, mag, K, what):
+    y = f16(y_bits)
+    both_inf = np.isinf(y) & np.isinf(y_acc) & (np.sign(y) == np.sign(y_acc))
+    assert np.all(np.isfinite(y) | both_inf), what + ": non-finite output"
+    yf = np.where(both_inf, 0.0, y)
+    ra = np.where(both_inf, 0.0, y_acc)
+    err = np.abs(yf - ra)
+    norm = err.max() / max(np.abs(ra).max(), 1e-300)
+    assert norm <= 2e-2, "%s: normwise %.3g" % (what, norm)
+    bound = 2.0 ** -10 * np.abs(ra) + (K + 64) * 2.0 ** -24 * mag + 2.0 ** -24
+    bad = err > bound
+    assert not bad.any(), "%s: %d elements over the bound, worst %s" % (
+        what, bad.sum(), np.unravel_index(np.argmax(err - bound), err.shape))
+
+
+def q4_mag(w_qs, w_d, a_qs, a_d, a_s):
+    isum = oracle.q4_0_blocksums(w_qs, a_qs).astype(np.float64)          # [M][N][nb]
+    d4 = np.abs(f16(w_d))                                                 # [N][nb]
+    d8 = np.abs(f16(a_d))[:, None, :]
+    s8 = np.abs(f16(a_s))[:, None, :]
+    return (d4[None, :, :] * (d8 * np.abs(isum) + 8 * s8)).sum(axis=2)
+
+
+def nvfp4_mag(codes, scales, g, x):
+    W = np.abs(e2m1_table()[unpack_nvfp4(codes)] * np.repeat(e4m3_table()[scales], 16, axis=1) * g)
+    return np.abs(f16(x)) @ W.T
+
+
+def fp8_mag(w, cs, x):
+    return (np.abs(f16(x)) @ np.abs(e4m3_table()[w]).T) * np.abs(cs)[None, :]
+
+
+# ------------------------------------------------------------------ Q8_1
+
+def run_quantize(x):
+    import skinny_gemm_amd as sk
+
+    qs, d, s = sk.quantize_act_q8_1(dev(x))
+    return host(qs), host(d, np.uint16), host(s, np.uint16)
+
+
+@pytest.mark.parametrize("M,K", [(1, 32), (1, 4096), (3, 96), (8, 11008), (5, 5120), (8, 17408),
+                                 (37, 1024)])
+def test_quantize_q8_1_bit_exact(M, K):
+    x = inputs.normal_f32(M, K, 10 * M + K)
+    got = run_quantize(x)
+    want = oracle.quantize_q8_1(x)
+    for g, w, name in zip(got, want, ("qs", "d", "s")):
+        assert np.array_equal(g, w), name
+
+
+def test_quantize_q8_1_adversarial_bit_exact():
+    x = inputs.q8_1_unit_scale_source(4, 1024, 3)
+    x[0, 1:64:2] += 0.5                       # exact halfway quotients
+    x[1, :32] = 0.0                           # all-zero block
+    x[1, 32:64] *= 1e-9                       # binary16 scale subnormal / zero
+    x[2, :32] = 3.0e4                         # scaled sum overflows to +inf
+    x[2, 32:64] = -3.0e4
+    x[3] *= np.float32(1.0 / 3.0)             # inexact scales everywhere
+    x[3, 64:96] = np.float32(1e-30)           # tiny amax
+    got = run_quantize(x)
+    want = oracle.quantize_q8_1(x)
+    for g, w, name in zip(got, want, ("qs", "d", "s")):
+        assert np.array_equal(g, w), name
+    assert want[2][2, 0] == 0x7C00 and want[2][2, 1] == 0xFC00
+
+
+# ------------------------------------------------------------------ Q4_0
+
+def run_q4(w_qs, w_d, a_qs, a_d, a_s):
+    import skinny_gemm_amd as sk
+
+    return host(sk.mmvq_q4_0(dev(w_qs), dev(w_d), dev(a_qs), dev(a_d), dev(a_s)))
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("N,K", [(1, 32), (4096 + 37, 256), (4099, 1376), (257, 11008)])
+def test_mmvq_q4_0_vs_oracle(M, N, K):
+    w_qs, w_d = inputs.q4_0_weights(N, K, 7 * N + K)
+    x = inputs.normal_f32(M, K, 3 * M + K)
+    a_qs, a_d, a_s = oracle.quantize_q8_1(x)
+    y = run_q4(w_qs, w_d, a_qs, a_d, a_s)
+    ref = oracle.mmvq_q4_0(w_qs, w_d, a_qs, a_d, a_s)
+    check_f32(y, ref, q4_mag(w_qs, w_d, a_qs, a_d, a_s), K, "q4_0 M=%d N=%d K=%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_mmvq_q4_0_integer_gate_bit_exact(M):
+    # unit Q8_1 scales and unit weight scales: every term is an integer below
+    # 2^24, so the result is exact in any summation order
+    N, K = 1031, 4096
+    x = inputs.q8_1_unit_scale_source(M, K, 90 + M)
+    import skinny_gemm_amd as sk
+
+    qs, d, s = sk.quantize_act_q8_1(dev(x))            # quantized on the device
+    w_qs, _ = inputs.q4_0_weights(N, K, 91)
+    w_d = np.full((N, K // 32), 0x3C00, np.uint16)
+    y = host(sk.mmvq_q4_0(dev(w_qs), dev(w_d), qs, d, s))
+    a_qs, a_d, a_s = oracle.quantize_q8_1(x)
+    exact = oracle.mmvq_q4_0(w_qs, w_d, a_qs, a_d, a_s)
+    assert np.array_equal(exact, np.rint(exact))
+    assert np.array_equal(y.astype(np.float64), exact)
+    # every code 8: all weights zero
+    w8 = np.full((N, K // 2), 0x88, np.uint8)
+    y8 = host(sk.mmvq_q4_0(dev(w8), dev(w_d), qs, d, s))
+    assert np.all(y8 == 0.0)
+
+
+def test_q4_0_pipeline_device_quantize():
+    # quantize on the device, then the GEMV, against the oracle chain
+    M, N, K = 8, 2048 + 5, 4096
+    import skinny_gemm_amd as sk
+
+    x = inputs.normal_f32(M, K, 55)
+    w_qs, w_d = inputs.q4_0_weights(N, K, 56)
+    qs, d, s = sk.quantize_act_q8_1(dev(x))
+    y = host(sk.mmvq_q4_0(dev(w_qs), dev(w_d), qs, d, s))
+    a_qs, a_d, a_s = oracle.quantize_q8_1(x)
+    ref = oracle.mmvq_q4_0(w_qs, w_d, a_qs, a_d, a_s)
+    check_f32(y, ref, q4_mag(w_qs, w_d, a_qs, a_d, a_s), K, "q4_0 pipeline")
+
+
+# ------------------------------------------------------------------ NVFP4
+
+def run_nvfp4(codes, scales, g, x):
+    import skinny_gemm_amd as sk
+
+    return host(sk.gemv_nvfp4_w4a16(dev(codes), dev(scales), g, dev(x)), np.uint16)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("N,K,g", [(1, 32, 1.0), (4096 + 19, 320, 1.0), (1030, 5120, 0.5),
+                                   (129, 17408, 2.0 ** -3)])
+def test_gemv_nvfp4_vs_oracle(M, N, K, g):
+    codes, scales, _ = inputs.nvfp4_weights(N, K, 5 * N + K)
+    x = inputs.normal_f16_bits(M, K, 2 * M + K)
+    y = run_nvfp4(codes, scales, g, x)
+    y_acc, _ = oracle.gemv_nvfp4_w4a16(codes, scales, g, x)
+    check_f16(y, y_acc, nvfp4_mag(codes, scales, g, x), K, "nvfp4 M=%d N=%d K=%d" % (M, N, K))
+
+
+def test_gemv_nvfp4_every_code_and_scale_bit_exact():
+    # row n: the 16 E2M1 codes at elements 0..15 under group scale n (NaN
+    # scale codes replaced by 1.0); x row m is one-hot at element e, so
+    # y[m][n] = e2m1(e) * e4m3(n): exact in binary16
+    N, K = 256, 32
+    codes = np.zeros((N, K // 2), np.uint8)
+    codes[:, :8] = np.array([c0 | (c1 << 4) for c0, c1 in zip(range(0, 16, 2), range(1, 16, 2))],
+                            np.uint8)
+    codes[:, 8:] = np.array([0x12, 0x34, 0x56, 0x70, 0x89, 0xAB, 0xCD, 0xEF], np.uint8)
+    scales = np.zeros((N, 2), np.uint8)
+    scales[:, 0] = np.arange(256)
+    scales[:, 1] = np.arange(256)[::-1]
+    scales[scales == 0x7F] = 0x38
+    scales[scales == 0xFF] = 0x38
+    for base in (0, 8, 16, 24):
+        x = np.zeros((8, K), np.float16)
+        for m in range(8):
+            x[m, base + m] = 1.0
+        xb = x.view(np.uint16)
+        y = run_nvfp4(codes, scales, 1.0, xb)
+        _, want = oracle.gemv_nvfp4_w4a16(codes, scales, 1.0, xb)
+        assert np.array_equal(y, want), base
+
+
+def test_gemv_nvfp4_outliers():
+    # activation outliers of +-2e4: any binary16 partial sum would overflow
+    M, N, K = 4, 512, 5120
+    codes, scales, _ = inputs.nvfp4_weights(N, K, 61)
+    x = inputs.normal_f16_bits(M, K, 62).view(np.float16).copy()
+    rng = np.random.Generator(np.random.PCG64(63))
+    idx = rng.integers(0, K, size=(M, 24))
+    for m in range(M):
+        x[m, idx[m]] = np.float16(2.0e4) * np.where(rng.integers(0, 2, 24) == 0, -1, 1)
+    xb = x.view(np.uint16)
+    y = run_nvfp4(codes, scales, 1.0, xb)
+    y_acc, _ = oracle.gemv_nvfp4_w4a16(codes, scales, 1.0, xb)
+    assert np.all(np.isfinite(y_acc))
+    check_f16(y, y_acc, nvfp4_mag(codes, scales, 1.0, xb), K, "nvfp4 outliers")
+
+
+# ------------------------------------------------------------------ FP8
+
+def run_fp8(w, cs, x):
+    import skinny_gemm_amd as sk
+
+    return host(sk.gemv_fp8_w8a16(dev(w), dev(cs), dev(x)), np.uint16)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("N,K", [(1, 16), (4096 + 3, 272), (1030, 5120), (129, 17408)])
+def test_gemv_fp8_vs_oracle(M, N, K):
+    w, cs = inputs.fp8_weights(N, K, 3 * N + K)
+    x = inputs.normal_f16_bits(M, K, 4 * M + K)
+    y = run_fp8(w, cs, x)
+    y_acc, _ = oracle.gemv_fp8_w8a16(w, cs, x)
+    check_f16(y, y_acc, fp8_mag(w, cs, x), K, "fp8 M=%d N=%d K=%d" % (M, N, K))
+
+
+def test_gemv_fp8_every_code_bit_exact():
+    # row n holds code n at element n % 16; x row m is one-hot at m and m+8
+    N, K = 256, 16
+    w = np.zeros((N, K), np.uint8)
+    codes = np.arange(256)
+    codes[[0x7F, 0xFF]] = 0x38                # NaN codes are unspecified
+    w[np.arange(N), np.arange(N) % 16] = codes
+    cs = np.ones(N, np.float32)
+    x = np.zeros((8, K), np.float16)
+    for m in range(8):
+        x[m, m] = 1.0
+        x[m, m + 8] = 1.0
+    xb = x.view(np.uint16)
+    y = run_fp8(w, cs, xb)
+    _, want = oracle.gemv_fp8_w8a16(w, cs, xb)
+    assert np.array_equal(y, want)
+
+
+# ------------------------------------------------------------------ full sizes (sampled rows)
+
+LLAMA_Q4 = [(12288, 4096), (4096, 4096), (22016, 4096), (4096, 11008), (32000, 4096)]
+QWEN_FP = [(10240, 5120), (5120, 5120), (34816, 5120), (5120, 17408)]
+
+
+def sample_rows(N, k=48, seed=0):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return np.unique(np.concatenate([[0, 1, N - 2, N - 1], rng.integers(0, N, k)]))
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
+def test_q4_0_full_sizes_sampled(M):
+    import skinny_gemm_amd as sk
+
+    for si, (N, K) in enumerate(LLAMA_Q4):
+        w_qs, w_d = inputs.q4_0_weights(N, K, inputs.seed(1, si, 0))
+        x = inputs.normal_f32(M, K, inputs.seed(2, si, 2) + M)
+        qs, d, s = sk.quantize_act_q8_1(dev(x))
+        y = host(sk.mmvq_q4_0(dev(w_qs), dev(w_d), qs, d, s))
+        a_qs, a_d, a_s = oracle.quantize_q8_1(x)
+        assert np.array_equal(host(qs), a_qs) and np.array_equal(host(d, np.uint16), a_d)
+        rows = sample_rows(N, seed=si)
+        ref = oracle.mmvq_q4_0(w_qs[rows], w_d[rows], a_qs, a_d, a_s)
+        mag = q4_mag(w_qs[rows], w_d[rows], a_qs, a_d, a_s)
+        check_f32(y[:, rows], ref, mag, K, "q4_0 full M=%d %dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_nvfp4_full_sizes_sampled(M):
+    for si, (N, K) in enumerate(QWEN_FP):
+        codes, scales, g = inputs.nvfp4_weights(N, K, inputs.seed(3, si, 0))
+        x = inputs.normal_f16_bits(M, K, inputs.seed(3, si, 2) + M)
+        y = run_nvfp4(codes, scales, g, x)
+        rows = sample_rows(N, seed=si)
+        y_acc, _ = oracle.gemv_nvfp4_w4a16(codes[rows], scales[rows], g, x)
+        check_f16(y[:, rows], y_acc, nvfp4_mag(codes[rows], scales[rows], g, x), K,
+                  "nvfp4 full M=%d %dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_fp8_full_sizes_sampled(M):
+    for si, (N, K) in enumerate(QWEN_FP):
+        w, cs = inputs.fp8_weights(N, K, inputs.seed(4, si, 0))
+        x = inputs.normal_f16_bits(M, K, inputs.seed(4, si, 2) + M)
+        y = run_fp8(w, cs, x)
+        rows = sample_rows(N, seed=si)
+        y_acc, _ = oracle.gemv_fp8_w8a16(w[rows], cs[rows], x)
+        check_f16(y[:, rows], y_acc, fp8_mag(w[rows], cs[rows], x), K,
+                  "fp8 full M=%d %dx%d" % (M, N, K))
+
+
+# ------------------------------------------------------------------ determinism, streams, limits
+
+def test_repeat_runs_bit_identical_and_side_stream():
+    import torch
+
+    import skinny_gemm_amd as sk
+
+    M, N, K = 8, 3000, 5120
+    w_qs, w_d = inputs.q4_0_weights(N, K, 1)
+    codes, scales, g = inputs.nvfp4_weights(N, K, 2)
+    w8, cs = inputs.fp8_weights(N, K, 3)
+    xf = inputs.normal_f32(M, K, 4)
+    xh = inputs.normal_f16_bits(M, K, 5)
+    args = [dev(a) for a in (w_qs, w_d, codes, scales, w8, cs, xf, xh)]
+
+    def once(stream):
+        qs, d, s = sk.quantize_act_q8_1(args[6], stream=stream)
+        return (sk.mmvq_q4_0(args[0], args[1], qs, d, s, stream=stream),
+                sk.gemv_nvfp4_w4a16(args[2], args[3], g, args[7], stream=stream),
+                sk.gemv_fp8_w8a16(args[4], args[5], args[7], stream=stream))
+
+    a = [host(t) for t in once(None)]
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        b = once(side)
+    side.synchronize()
+    b = [host(t) for t in b]
+    for u, v in zip(a, b):
+        assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
+
+
+def test_largest_k_small_n():
+    # K at the documented maximum, a handful of rows, ragged N
+    M, N, K = 2, 5, 1 << 20
+    w8, cs = inputs.fp8_weights(N, K, 8)
+    x = inputs.normal_f16_bits(M, K, 9, std=0.1)
+    y = run_fp8(w8, cs, x)
+    y_acc, _ = oracle.gemv_fp8_w8a16(w8, cs, x)
+    check_f16(y, y_acc, fp8_mag(w8, cs, x), K, "fp8 max K")
+    w_qs, w_d = inputs.q4_0_weights(N, K, 10)
+    xf = inputs.normal_f32(M, K, 11)
+    a_qs, a_d, a_s = oracle.quantize_q8_1(xf)
+    y = run_q4(w_qs, w_d, a_qs, a_d, a_s)
+    ref = oracle.mmvq_q4_0(w_qs, w_d, a_qs, a_d, a_s)
+    check_f32(y, ref, q4_mag(w_qs, w_d, a_qs, a_d, a_s), K, "q4_0 max K")
+
+
+def test_empty_and_invalid_calls_on_device():
+    import torch
+
+    import skinny_gemm_amd as sk
+
+    z = torch.empty((0, 4096), dtype=torch.float16, device="cuda")
+    w = torch.zeros((64, 4096), dtype=torch.uint8, device="cuda")
+    cs = torch.ones(64, device="cuda")
+    y = sk.gemv_fp8_w8a16(w, cs, z)
+    assert tuple(y.shape) == (0, 64)
+    x9 = torch.zeros((9, 4096), dtype=torch.float16, device="cuda")
+    with pytest.raises(sk.SkinnyError) as e:
+        sk.gemv_fp8_w8a16(w, cs, x9)
+    assert e.value.status == -4
