@@ -122,3 +122,37 @@ def normal_f32_torch(M: int, K: int, s: int, device):
     g = torch.Generator(device=device)
     g.manual_seed(int(s))
     return torch.randn((M, K), dtype=torch.float32, device=device, generator=g)
+
+
+def nvfp4_weights_torch(N: int, K: int, base_seed: int, device):
+    """Device-side draw with the distributions of ``nvfp4_weights``.
+    -> (codes uint8 [N][K/2], scales uint8 E4M3 [N][K/16])."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(base_seed))
+    codes = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device=device, generator=g)
+    u = 0.01 + 0.09 * torch.rand((N, K // 16), dtype=torch.float32, device=device, generator=g)
+    scales = (u / 6.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, scales
+
+
+def fp8_weights_torch(N: int, K: int, base_seed: int, device):
+    """Device-side draw with the distributions of ``fp8_weights``.
+    -> (w uint8 E4M3 [N][K], cs float32 [N])."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(base_seed))
+    w = torch.randn((N, K), dtype=torch.float32, device=device, generator=g) * 0.05
+    w = w.clamp_(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn).view(torch.uint8)
+    cs = 0.5 + 1.5 * torch.rand((N,), dtype=torch.float32, device=device, generator=g)
+    return w, cs
+
+
+def normal_f16_torch(M: int, K: int, s: int, device):
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(s))
+    return torch.randn((M, K), dtype=torch.float32, device=device, generator=g).to(torch.float16)
