@@ -12,6 +12,7 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t uint2_t __attribute__((ext_vector_type(2)));
 typedef int32_t int4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
@@ -34,6 +35,27 @@ __device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast
 template <typename T>
 __device__ __forceinline__ uint4_t load16(const T *p) {
   return *reinterpret_cast<const uint4_t *>(p);
+}
+
+// 128-bit non-temporal load, for the weight stream: every weight byte is
+// read exactly once per call, so it should not displace reusable lines.
+template <typename T>
+__device__ __forceinline__ uint4_t load16_nt(const T *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint4_t *>(p));
+}
+
+template <typename T>
+__device__ __forceinline__ uint2_t load8_nt(const T *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint2_t *>(p));
+}
+
+template <typename T>
+__device__ __forceinline__ uint2_t load8(const T *p) {
+  return *reinterpret_cast<const uint2_t *>(p);
+}
+
+__device__ __forceinline__ uint16_t load_u16_nt(const uint16_t *p) {
+  return __builtin_nontemporal_load(p);
 }
 
 // Value held by lane (lane ^ D), D in {1, 2, 4, 8}.
@@ -148,6 +170,34 @@ __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
 
 __device__ __forceinline__ int32_t dot4_i8(uint32_t a, uint32_t b, int32_t c) {
   return __builtin_amdgcn_sdot4(a, b, c, false);
+}
+
+// 16x16 matrix-core products.  Operand layout (wave64): lane l supplies
+// row (l % 16) of A and column (l % 16) of B for k-slot (l / 16); both
+// operands use the same slot and element positions, so any consistent
+// assignment of K indices to (slot, position) gives
+//   C[i][j] = sum over lanes l = i + 16g, j + 16g and positions p of
+//             A_l[p] * B_l[p].
+// Lane l receives C[4 * (l / 16) + r][l % 16] in element r of the result.
+__device__ __forceinline__ float4_t mfma_16x16x32_f16(const half8_t &a, const half8_t &b,
+                                                      const float4_t &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int4_t mfma_16x16x64_i8(const int4_t &a, const int4_t &b,
+                                                   const int4_t &c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// x + (value of x in lane l ^ 32): one v_permlane32_swap and one add.
+__device__ __forceinline__ float add_swap32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(x), false, false);
+  return as_f32(r[0]) + as_f32(r[1]);
+}
+
+__device__ __forceinline__ half2_t h2_bcast(float f) {
+  const _Float16 h = (_Float16)f;
+  return half2_t{h, h};
 }
 
 }  // namespace skinny
