@@ -58,8 +58,8 @@ __global__ __launch_bounds__(256) void gemv_nvfp4_kernel(
     uint32_t sc2[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      wq[r] = load16(crow[r] + 16 * c);
-      sc2[r] = *reinterpret_cast<const uint16_t *>(srow[r] + 2 * c);
+      wq[r] = load16_nt(crow[r] + 16 * c);
+      sc2[r] = load_u16_nt(reinterpret_cast<const uint16_t *>(srow[r]) + c);
     }
     // activations of the chunk: 32 binary16 = 16 pairs per row m
     uint4_t xv[M][4];
@@ -110,27 +110,9 @@ __global__ __launch_bounds__(256) void gemv_nvfp4_kernel(
   }
 }
 
-// Matrix-core variant (any M <= 8).
-//
-// A workgroup of W waves owns T tiles of 16 weight rows; each wave takes a
-// contiguous range of K.  The weight stream is read row-contiguously -- one
-// 128-bit load per lane, 64 lanes covering 1 KB of a single row per
-// instruction, which the memory system serves at close to streaming rate --
-// into registers, then written to a wave-private LDS buffer (rows padded
-// against bank conflicts) and read back in the matrix-core operand layout:
-// lane l = (i = l % 16, g = l / 16) takes 16 code bytes of row 16t + i
-// (elements k0 .. k0+31, k0 = 128 s + 32 g) and the two group scales, and
-// decodes them two at a time to binary16 times the binary16 group scale --
-// exact, as an E2M1 value times an E4M3 value has at most 5 significant
-// bits and lies in [2^-10, 2688] -- giving the A operands of four
-// v_mfma_f32_16x16x32_f16.  The B operands are the activations
-// x[i][k0 + 8t .. +8], loaded four steps ahead into a register ring by the
-// lanes with i < M (the other lanes' columns are never stored).  The matrix core accumulates in
-// float32 across all of K, so no binary16 partial sum exists anywhere; the
-// per-tensor scale is applied to the finished float32 sum.  The next chunk
-// of weights is in flight while the current one is consumed.  Steps past
-// the last whole chunk are read directly in the operand layout.  The W
-// partial tiles are summed through LDS.
+// One 128-K step of a 16-row tile: decode the lane's 16 code bytes with its
+// two group scales into four A operands and accumulate against the four B
+// operands xv.
 __device__ __forceinline__ void nvfp4_step(const uint4_t &wq, uint32_t sc, const uint4_t (&xv)[4],
                                            float4_t &acc) {
   const half2_t s0 = h2_bcast(e4m3_to_f32<0>(sc));
@@ -147,181 +129,225 @@ __device__ __forceinline__ void nvfp4_step(const uint4_t &wq, uint32_t sc, const
   }
 }
 
+// Matrix-core variant (3 <= M <= 8, K % 256 == 0).
+//
+// Tile: 16 weight rows.  Lane l = (i = l % 16, g = l / 16) of a wave feeds
+// row 16t + i of the A operand of four v_mfma_f32_16x16x32_f16 per 128-K
+// step: its 16 code bytes (elements k0 .. k0+31, k0 = 128 s + 32 g) decode
+// two at a time to binary16 times the binary16 group scale -- exact, as an
+// E2M1 value times an E4M3 value has at most 5 significant bits and lies in
+// [2^-10, 2688].  The B operands are the activations x[i][k0 + 8t .. +8]
+// (columns i >= M are computed and dropped).  The matrix core accumulates
+// in float32 across all of K, so no binary16 partial sum exists anywhere;
+// the per-tensor scale multiplies the finished sum.
+//
+// Data movement.  Each wave streams its own T tiles over its own slice of
+// K, independently of the other waves (no barrier until the final sum), in
+// chunks of S steps.  A chunk -- codes, group scales and the matching MP
+// activation rows (rows past M repeat row M - 1) -- is read with 128-bit
+// loads in row-contiguous order (each 1 KB load instruction covers whole
+// 128-byte lines) into registers one chunk ahead of its use; registers, not
+// LDS, hold the bytes in flight.  When its turn comes the chunk is written
+// to a wave-private LDS buffer and read back in the operand layout, its
+// registers immediately refilled with the next chunk.  Loads are issued
+// in the order they are consumed, so each wait covers exactly one chunk.
+// LDS layout: 1 KB blocks as written by one store instruction (lane l ->
+// bytes 16 l); the 16-byte columns of each block are XOR-swizzled so the
+// operand-layout reads (16 rows at one column) hit distinct banks.  The
+// workgroup's KS waves split K; their partial tiles are summed in LDS.
 namespace nv {
-constexpr int kCh = 8;                 // 128-element steps per staged chunk
-constexpr int kRowB = kCh * 64;        // code bytes per row per chunk (512)
-constexpr int kSclB = kCh * 8;         // scale bytes per row per chunk (64)
-constexpr int kRowP = kRowB + 16;      // padded LDS pitches
-constexpr int kSclP = kSclB + 16;
-constexpr int kXr = 4;                 // activation steps kept in flight
-template <int T>
-constexpr int wave_lds() { return 16 * T * (kRowP + kSclP); }
+template <int T, int S, int MP>
+struct Cfg {
+  static constexpr int kRows = 16 * T;              // weight rows per wave
+  static constexpr int kRpi = 16 / S;               // code rows per 1 KB block
+  static constexpr int kCi = T * S;                 // code loads per chunk
+  static constexpr int kSclB = kRows * 8 * S;       // scale bytes per chunk
+  static constexpr int kRpa = 4 / S;                // activation rows per 1 KB block
+  static constexpr int kAi = MP / kRpa;             // activation loads per chunk
+  static constexpr int kSclOff = kCi * 1024;
+  static constexpr int kActOff = kSclOff + kSclB;
+  static constexpr int kSt = kActOff + kAi * 1024;  // LDS bytes per wave
+  static_assert(S == 2 || S == 4, "chunk steps");
+  static_assert(MP == 4 || MP == 8, "padded activation rows");
+  static_assert(kSclB <= 1024, "one scale load per chunk");
+};
 }  // namespace nv
 
-template <int W, int T>
-__global__ __launch_bounds__(64 * W) void gemv_nvfp4_mfma_kernel(
-    const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales, float g,
-    int N, int K, const uint16_t *__restrict__ x, int M, uint16_t *__restrict__ y) {
-  using namespace nv;
-  constexpr int ROWS = 16 * T;
-  constexpr int CLD = ROWS / 2;        // 1 KB code loads per chunk (2 rows each)
-  constexpr int SLD = T;               // 1 KB scale loads per chunk (16 rows each)
+template <int T, int S>
+struct NvChunk {
+  uint4_t c[T * S];
+  uint4_t s;
+  uint4_t a[8];
+};
+
+// (No __restrict__ on the inputs: the issue fences below must be able to
+// order their loads.)
+template <int T, int KS, int S, int MP>
+__global__ __launch_bounds__(64 * KS) void gemv_nvfp4_mfma_kernel(
+    const uint8_t *codes, const uint8_t *scales, float g,
+    int N, int K, const uint16_t *x, int M, uint16_t *y) {
+  using C = nv::Cfg<T, S, MP>;
+  using R = NvChunk<T, S>;
   extern __shared__ uint4_t smem4[];
   uint8_t *smem = reinterpret_cast<uint8_t *>(smem4);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int ks = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int i = lane & 15, grp = lane >> 4;
-  const int n0 = blockIdx.x * ROWS;
-  uint8_t *cl = smem + wave * wave_lds<T>();
-  uint8_t *sl = cl + ROWS * kRowP;
-  float4_t *red = reinterpret_cast<float4_t *>(smem + W * wave_lds<T>());
+  const int n0 = blockIdx.x * C::kRows;
+  uint8_t *ws = smem + ks * C::kSt;
 
   const size_t rowc = (size_t)(K >> 1), rows_ = (size_t)(K >> 4);
-  // row-contiguous load mapping: codes, lane -> (row 2q + lane/32, bytes 16 (lane%32));
-  // scales, lane -> (row 16q + lane/4, bytes 16 (lane%4))
-  const uint8_t *cg[CLD];
-  const uint8_t *sg[SLD];
-#pragma unroll
-  for (int q = 0; q < CLD; ++q)
-    cg[q] = codes + (size_t)min(n0 + 2 * q + (lane >> 5), N - 1) * rowc + 16 * (lane & 31);
-#pragma unroll
-  for (int q = 0; q < SLD; ++q)
-    sg[q] = scales + (size_t)min(n0 + 16 * q + (lane >> 2), N - 1) * rows_ + 16 * (lane & 3);
+  const int nct = K / (128 * S);
+  const int cps = (nct + KS - 1) / KS;
+  const int cb = ks * cps, ce = min(nct, cb + cps);
 
-  const bool xact = i < M;
-  const uint16_t *xrow = x + (size_t)(xact ? i : 0) * (size_t)K + 32 * grp;
-  const int nsteps = (K + 127) >> 7;
-  // staged chunks need 16-byte aligned scale rows (K % 256 == 0)
-  const int nchunks = (K % 256 == 0) ? K / (128 * kCh) : 0;
-  const int per = (nchunks + W - 1) / W;
-  const int c0 = min(nchunks, wave * per), c1 = min(nchunks, c0 + per);
+  // per-lane sources (chunk 0)
+  const uint8_t *csrc[C::kCi];
+#pragma unroll
+  for (int q = 0; q < C::kCi; ++q) {
+    const int r = q * C::kRpi + (lane % C::kRpi);
+    const int j = (lane / C::kRpi) ^ (q & (S - 1));
+    csrc[q] = codes + (size_t)min(n0 + r, N - 1) * rowc + 16 * j;
+  }
+  const bool sact = lane < C::kSclB / 16;
+  const int sl = lane % (C::kSclB / 16);       // lanes past the scale bytes repeat one
+  const uint8_t *ssrc = scales + (size_t)min(n0 + sl % C::kRows, N - 1) * rows_ +
+                        16 * (sl / C::kRows);
+  const uint16_t *asrc[C::kAi];
+#pragma unroll
+  for (int a = 0; a < C::kAi; ++a) {
+    const int r = min(a * C::kRpa + (lane % C::kRpa), M - 1);
+    const int j = (lane / C::kRpa) ^ a;
+    asrc[a] = x + (size_t)r * K + 8 * j;
+  }
+  auto load = [&](int c, R &rg) {
+#pragma unroll
+    for (int q = 0; q < C::kCi; ++q) rg.c[q] = load16_nt(csrc[q] + (size_t)c * (64 * S));
+    rg.s = load16_nt(ssrc + (size_t)c * (8 * S));
+#pragma unroll
+    for (int a = 0; a < C::kAi; ++a) rg.a[a] = load16(asrc[a] + (size_t)c * (128 * S));
+    issue_fence();   // keep each chunk's loads together and ahead of later work
+  };
+  auto store = [&](const R &rg) {
+#pragma unroll
+    for (int q = 0; q < C::kCi; ++q) *reinterpret_cast<uint4_t *>(ws + 1024 * q + 16 * lane) = rg.c[q];
+    if (sact) *reinterpret_cast<uint4_t *>(ws + C::kSclOff + 16 * lane) = rg.s;
+#pragma unroll
+    for (int a = 0; a < C::kAi; ++a)
+      *reinterpret_cast<uint4_t *>(ws + C::kActOff + 1024 * a + 16 * lane) = rg.a[a];
+  };
 
   float4_t acc[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  // activations for the next kXr steps, kept in a ring of registers
-  uint4_t xr[kXr][4];
+  const int ar = i & (MP - 1), aa = ar / C::kRpa;   // activation row (columns >= MP wrap)
+  const int aoff = C::kActOff + 1024 * aa + 16 * (ar % C::kRpa);
+  auto consume = [&]() {
 #pragma unroll
-  for (int d = 0; d < kXr; ++d) {
+    for (int st = 0; st < S; ++st) {
+      uint4_t xv[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) xr[d][q] = uint4_t{0u, 0u, 0u, 0u};
-    if (xact && c0 * kCh + d < c1 * kCh) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) xr[d][q] = load16(xrow + 128 * (c0 * kCh + d) + 8 * q);
-    }
-  }
-  uint4_t cr[CLD], sr[SLD];
-  if (c0 < c1) {
-#pragma unroll
-    for (int q = 0; q < CLD; ++q) cr[q] = load16_nt(cg[q] + (size_t)c0 * kRowB);
-#pragma unroll
-    for (int q = 0; q < SLD; ++q) sr[q] = load16_nt(sg[q] + (size_t)c0 * kSclB);
-  }
-  for (int c = c0; c < c1; ++c) {
-#pragma unroll
-    for (int q = 0; q < CLD; ++q)
-      *reinterpret_cast<uint4_t *>(cl + (2 * q + (lane >> 5)) * kRowP + 16 * (lane & 31)) = cr[q];
-#pragma unroll
-    for (int q = 0; q < SLD; ++q)
-      *reinterpret_cast<uint4_t *>(sl + (16 * q + (lane >> 2)) * kSclP + 16 * (lane & 3)) = sr[q];
-    if (c + 1 < c1) {
-#pragma unroll
-      for (int q = 0; q < CLD; ++q) cr[q] = load16_nt(cg[q] + (size_t)(c + 1) * kRowB);
-#pragma unroll
-      for (int q = 0; q < SLD; ++q) sr[q] = load16_nt(sg[q] + (size_t)(c + 1) * kSclB);
-    }
-#pragma unroll
-    for (int st = 0; st < kCh; ++st) {
-      const int slot = st % kXr;
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const uint4_t wq = *reinterpret_cast<const uint4_t *>(cl + (16 * t + i) * kRowP + 64 * st + 16 * grp);
-        const uint32_t sc = *reinterpret_cast<const uint16_t *>(sl + (16 * t + i) * kSclP + 8 * st + 2 * grp);
-        nvfp4_step(wq, sc, xr[slot], acc[t]);
-      }
-      // refill this slot with the activations kXr steps ahead
-      const int ahead = c * kCh + st + kXr;
-      if (xact && ahead < c1 * kCh) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) xr[slot][q] = load16(xrow + 128 * ahead + 8 * q);
-      }
-    }
-  }
-  // steps past the last whole chunk, read in the operand layout (last wave)
-  if (wave == W - 1) {
-    for (int s = nchunks * kCh; s < nsteps; ++s) {
-      const bool kact = 128 * s + 32 * grp < K;
-      uint4_t xv[4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-      if (kact && xact) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) xv[q] = load16(xrow + 128 * s + 8 * q);
+      for (int u = 0; u < 4; ++u) {
+        const int j = 16 * st + 4 * grp + u;
+        xv[u] = *reinterpret_cast<const uint4_t *>(ws + aoff + 16 * C::kRpa * (j ^ aa));
       }
 #pragma unroll
       for (int t = 0; t < T; ++t) {
-        const int nrow = min(n0 + 16 * t + i, N - 1);
-        uint4_t wq = {0u, 0u, 0u, 0u};
-        uint32_t sc = 0;
-        if (kact) {
-          wq = load16_nt(codes + (size_t)nrow * rowc + 64 * s + 16 * grp);
-          sc = load_u16_nt(reinterpret_cast<const uint16_t *>(scales + (size_t)nrow * rows_) +
-                           4 * s + grp);
-        }
+        const int r = 16 * t + i, q = r / C::kRpi;
+        const int j = 4 * st + grp;
+        const uint4_t wq = *reinterpret_cast<const uint4_t *>(
+            ws + 1024 * q + 16 * (C::kRpi * (j ^ (q & (S - 1))) + r % C::kRpi));
+        const uint32_t sc = *reinterpret_cast<const uint16_t *>(
+            ws + C::kSclOff + 16 * ((st >> 1) * C::kRows + r) + 8 * (st & 1) + 2 * grp);
         nvfp4_step(wq, sc, xv, acc[t]);
       }
     }
+  };
+
+  if (cb < ce) {
+    // The load past the slice re-reads its last chunk into registers that
+    // are never stored, so every path issues the same loads.
+    R r0;
+    load(cb, r0);
+    for (int c = cb; c < ce; ++c) {
+      store(r0);
+      load(min(c + 1, ce - 1), r0);
+      consume();
+    }
   }
 
+  if constexpr (KS > 1) {
+    wg_barrier();
+    float4_t *red = reinterpret_cast<float4_t *>(smem);
 #pragma unroll
-  for (int t = 0; t < T; ++t) red[(wave * T + t) * kWave + lane] = acc[t];
-  __syncthreads();
-  if (wave == 0 && xact) {
+    for (int t = 0; t < T; ++t) red[(ks * T + t) * kWave + lane] = acc[t];
+    wg_barrier();
+    if (ks == 0) {
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int v = 1; v < KS; ++v) acc[t] += red[(v * T + t) * kWave + lane];
+    }
+  }
+  if (ks == 0 && i < M) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      float4_t tot = red[t * kWave + lane];
-#pragma unroll
-      for (int v = 1; v < W; ++v) tot += red[(v * T + t) * kWave + lane];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int n = n0 + 16 * t + 4 * grp + r;
-        if (n < N) y[(size_t)i * N + n] = f32_to_f16_bits(tot[r] * g);
+        if (n < N) y[(size_t)i * N + n] = f32_to_f16_bits(acc[t][r] * g);
       }
     }
   }
 }
 
-template <int W, int T>
-static hipError_t launch_mfma_wt(const uint8_t *codes, const uint8_t *scales, float g, int N,
-                                 int K, const uint16_t *x, int M, uint16_t *y,
-                                 hipStream_t stream) {
-  const int blocks = (N + 16 * T - 1) / (16 * T);
-  const size_t shmem = (size_t)W * nv::wave_lds<T>() + sizeof(float4_t) * W * T * kWave;
-  hipLaunchKernelGGL((gemv_nvfp4_mfma_kernel<W, T>), dim3(blocks), dim3(64 * W), shmem, stream,
-                     codes, scales, g, N, K, x, M, y);
+template <int T, int KS, int S, int MP>
+static hipError_t launch_mfma_cfg(const uint8_t *codes, const uint8_t *scales, float g, int N,
+                                  int K, const uint16_t *x, int M, uint16_t *y,
+                                  hipStream_t stream) {
+  using C = nv::Cfg<T, S, MP>;
+  constexpr int kLds = KS * C::kSt;
+  static_assert(T * kWave * 16 <= C::kSt, "reduction buffer");
+  static_assert(kLds <= 160 * 1024, "LDS per workgroup");
+  if (K % (128 * S) != 0) return hipErrorInvalidValue;   // chunks must tile K
+  // workgroups above 64 KB of LDS must be allowed once per kernel
+  static const hipError_t lds_ok = allow_lds((const void *)gemv_nvfp4_mfma_kernel<T, KS, S, MP>, kLds);
+  if (lds_ok != hipSuccess) return lds_ok;
+  const int blocks = (N + C::kRows - 1) / C::kRows;
+  hipLaunchKernelGGL((gemv_nvfp4_mfma_kernel<T, KS, S, MP>), dim3(blocks), dim3(64 * KS), kLds,
+                     stream, codes, scales, g, N, K, x, M, y);
   return hipGetLastError();
 }
 
-// Tiles per wave T (weight rows sharing one activation operand) and waves
-// per workgroup W (K split), W * T <= 4 so the staging buffers fit in 64 KB
-// of LDS.  Measured on MI355X at M = 4 and 8: wide matrices prefer two
-// tiles and few K splits, narrow ones four K splits.
-static void pick_tw(int N, int K, int &T, int &W) {
-  (void)K;
+// Tiles per wave, K split and chunk length, measured on MI355X at M = 4 and
+// 8 over K 5120..17408, N 5120..34816: wide matrices want two tiles per
+// wave and no split; mid-width ones one tile; narrow ones (few tiles, long
+// K) a four-way split to keep enough waves streaming.
+template <int MP>
+static hipError_t launch_mfma_mp(const uint8_t *codes, const uint8_t *scales, float g, int N,
+                                 int K, const uint16_t *x, int M, uint16_t *y,
+                                 hipStream_t stream) {
   const int tiles = (N + 15) / 16;
-  if (tiles >= 2000) { T = 2; W = 1; }
-  else if (tiles >= 1024) { T = 2; W = 2; }
-  else { T = 1; W = 4; }
+  const bool s4 = K % 512 == 0;
+#define SKINNY_NV(T, KS, S) return launch_mfma_cfg<T, KS, S, MP>(codes, scales, g, N, K, x, M, y, stream)
+  if (tiles >= 1536) {
+    if (s4) SKINNY_NV(2, 1, 4);
+    SKINNY_NV(2, 1, 2);
+  }
+  if (tiles >= 512) {
+    if (s4) { if (M <= 4) SKINNY_NV(1, 2, 4); SKINNY_NV(1, 1, 4); }
+    SKINNY_NV(1, 1, 2);
+  }
+  if (s4 && K >= 8192) SKINNY_NV(2, 4, 4);
+  SKINNY_NV(2, 4, 2);
+#undef SKINNY_NV
 }
 
 static hipError_t launch_mfma(const uint8_t *codes, const uint8_t *scales, float g, int N,
                               int K, const uint16_t *x, int M, uint16_t *y, hipStream_t stream) {
-  int T, W;
-  pick_tw(N, K, T, W);
-#define SKINNY_NV_CASE(TT, WW) \
-  if (T == TT && W == WW) return launch_mfma_wt<WW, TT>(codes, scales, g, N, K, x, M, y, stream);
-  SKINNY_NV_CASE(1, 1) SKINNY_NV_CASE(1, 2) SKINNY_NV_CASE(1, 4)
-  SKINNY_NV_CASE(2, 1) SKINNY_NV_CASE(2, 2)
-#undef SKINNY_NV_CASE
-  return hipErrorInvalidValue;
+  if (M <= 4) return launch_mfma_mp<4>(codes, scales, g, N, K, x, M, y, stream);
+  return launch_mfma_mp<8>(codes, scales, g, N, K, x, M, y, stream);
 }
 
 template <int M, int R>
@@ -334,16 +360,18 @@ static hipError_t launch_mr(const uint8_t *codes, const uint8_t *scales, float g
   return hipGetLastError();
 }
 
-static int rows_per_wave(int N) {
-  int r = 2;
-  while (r < 8 && N / (2 * r) >= 2048) r *= 2;
-  return r;
+// Two rows per wave measured best on MI355X at M <= 2 for every shape
+// tried (K 4096 to 17408, N 4096 to 34816): few weight loads in flight per
+// lane and many waves.  Wider M runs on the matrix-core kernel.
+static int rows_per_wave(int N, int M) {
+  (void)N;
+  return M <= 2 ? 2 : 4;
 }
 
 template <int M>
 static hipError_t launch_m(const uint8_t *codes, const uint8_t *scales, float g, int N, int K,
                            const uint16_t *x, uint16_t *y, hipStream_t stream) {
-  switch (rows_per_wave(N)) {
+  switch (rows_per_wave(N, M)) {
     case 2: return launch_mr<M, 2>(codes, scales, g, N, K, x, y, stream);
     case 4: return launch_mr<M, 4>(codes, scales, g, N, K, x, y, stream);
     default: return launch_mr<M, 8>(codes, scales, g, N, K, x, y, stream);
@@ -352,7 +380,8 @@ static hipError_t launch_m(const uint8_t *codes, const uint8_t *scales, float g,
 
 hipError_t launch_gemv_nvfp4(const uint8_t *codes, const uint8_t *scales, float g, int N, int K,
                              const uint16_t *x, int M, uint16_t *y, hipStream_t stream) {
-  if (M >= kNvfp4MfmaMinM) return launch_mfma(codes, scales, g, N, K, x, M, y, stream);
+  if (M >= kNvfp4MfmaMinM && K % 256 == 0)
+    return launch_mfma(codes, scales, g, N, K, x, M, y, stream);
   switch (M) {
     case 1: return launch_m<1>(codes, scales, g, N, K, x, y, stream);
     case 2: return launch_m<2>(codes, scales, g, N, K, x, y, stream);

@@ -21,4 +21,11 @@ hipError_t launch_gemv_nvfp4(const uint8_t *w_codes, const uint8_t *w_scales,
 hipError_t launch_gemv_fp8(const uint8_t *w, const float *cs, int N, int K,
                            const uint16_t *x, int M, uint16_t *y, hipStream_t stream);
 
+// Let a kernel use more than 64 KB of LDS per workgroup (gfx950 has 160 KB
+// per compute unit); a no-op at or below 64 KB.
+inline hipError_t allow_lds(const void *kernel, int bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
 }  // namespace skinny

@@ -214,7 +214,11 @@ def run_nvfp4(codes, scales, g, x):
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("N,K,g", [(1, 32, 1.0), (4096 + 19, 320, 1.0), (1030, 5120, 0.5),
-                                   (129, 17408, 2.0 ** -3)])
+                                   (129, 17408, 2.0 ** -3),
+                                   # matrix-core paths: wide / mid / narrow, chunk of 2
+                                   # steps (K % 512 == 256), ragged tiles, K slices
+                                   # of unequal length and one empty slice
+                                   (25000, 768, 1.0), (9000, 1280, 1.0), (40, 768, 1.0)])
 def test_gemv_nvfp4_vs_oracle(M, N, K, g):
     codes, scales, _ = inputs.nvfp4_weights(N, K, 5 * N + K)
     x = inputs.normal_f16_bits(M, K, 2 * M + K)
