@@ -195,29 +195,11 @@ __device__ __forceinline__ float add_swap32(float x) {
   return as_f32(r[0]) + as_f32(r[1]);
 }
 
-// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
-// lane l's 16 bytes land at ldst + 16 l, where ldst is the same for the
-// whole wave.  Completion is counted by vmcnt like any vector-memory load;
-// the compiler does not track it, so the caller waits with dma_wait.
-typedef __attribute__((address_space(3))) void lds_void_t;
-template <bool NT>
-__device__ __forceinline__ void dma16(const void *gsrc, void *ldst) {
-  __builtin_amdgcn_global_load_lds(gsrc, (lds_void_t *)ldst, 16, 0, NT ? 2 : 0);
-}
-
-// Wait until at most N vector-memory operations of this wave are in flight.
-// The memory clobber keeps the compiler from moving LDS reads above it.
-template <int N>
-__device__ __forceinline__ void dma_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 // Compiler-only fence: memory operations are not moved across it, so the
-// hardware sees loads and copies in program order (what vmcnt counts).
+// hardware sees loads in program order (what vmcnt counts).
 __device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
 
-// Workgroup barrier with no implied memory wait (in-flight copies stay in
+// Workgroup barrier with no implied memory wait (in-flight loads stay in
 // flight); LDS accesses are not moved across it.
 __device__ __forceinline__ void wg_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");

@@ -90,21 +90,26 @@ __global__ __launch_bounds__(256) void gemv_fp8_kernel(
   }
 }
 
-// Matrix-core variant (any M <= 8).
+// Matrix-core variant (3 <= M <= 8, K % 256 == 0).
 //
-// A workgroup of W waves owns T tiles of 16 weight rows; each wave takes a
-// contiguous range of K.  The weights are read row-contiguously (64 lanes x
-// 16 bytes covering 512 bytes of each of two rows per instruction) into
-// registers, written to a wave-private LDS buffer and read back in the
-// matrix-core operand layout: lane l = (i = l % 16, g = l / 16) takes 32
-// bytes of row 16t + i (elements k0 .. k0+31, k0 = 128 s + 32 g), decodes
-// them exactly to binary16 and feeds four v_mfma_f32_16x16x32_f16 whose B
-// operands are x[i][k0 + 8t .. +8], kept four steps ahead in a register
-// ring by the lanes with i < M.  Float32 accumulation across K; the channel
-// scale multiplies the finished sum.  The next chunk of weights is in
-// flight while the current one is consumed; steps past the last whole chunk
-// (the final one possibly partial, K being a multiple of 16 only) are read
-// directly in the operand layout.  The W partial tiles are summed in LDS.
+// Tile: 16 weight rows.  Lane l = (i = l % 16, g = l / 16) of a wave feeds
+// row 16t + i of the A operand of four v_mfma_f32_16x16x32_f16 per 128-K
+// step: its 32 weight bytes (elements k0 .. k0+31, k0 = 128 s + 32 g)
+// decode exactly to binary16 (every E4M3 value is a binary16 value).  The B
+// operands are the activations x[i][k0 + 8t .. +8] (columns i >= M are
+// computed and dropped).  Float32 accumulation across all of K; the channel
+// scale multiplies the finished sum.
+//
+// Data movement, as for the NVFP4 kernel: each wave streams its own T tiles
+// over its own slice of K with no barrier until the final sum, in chunks of
+// S steps.  A chunk -- weight bytes and the matching MP activation rows
+// (rows past M repeat row M - 1) -- is read with 128-bit loads in
+// row-contiguous order into registers one chunk ahead of its use, then
+// written to a wave-private LDS buffer (1 KB blocks, 16-byte columns
+// XOR-swizzled per block so the operand-layout reads hit distinct banks)
+// and read back in the operand layout.  Loads are issued in the order they
+// are consumed, so each wait covers exactly one chunk.  The workgroup's KS
+// waves split K; their partial tiles are summed in LDS.
 __device__ __forceinline__ void fp8_step(const uint4_t (&wq)[2], const uint4_t (&xv)[4],
                                          float4_t &acc) {
 #pragma unroll
@@ -121,159 +126,183 @@ __device__ __forceinline__ void fp8_step(const uint4_t (&wq)[2], const uint4_t (
 }
 
 namespace f8 {
-constexpr int kCh = 4;                 // 128-element steps per staged chunk
-constexpr int kRowB = kCh * 128;       // weight bytes per row per chunk (512)
-constexpr int kRowP = kRowB + 16;      // padded LDS pitch
-constexpr int kXr = 4;                 // activation steps kept in flight
-template <int T>
-constexpr int wave_lds() { return 16 * T * kRowP; }
+template <int T, int S, int MP>
+struct Cfg {
+  static constexpr int kRows = 16 * T;              // weight rows per wave
+  static constexpr int kRpi = 8 / S;                // weight rows per 1 KB block
+  static constexpr int kSwz = 2 * S - 1;            // column swizzle mask
+  static constexpr int kCi = 2 * T * S;             // weight loads per chunk
+  static constexpr int kRpa = 4 / S;                // activation rows per 1 KB block
+  static constexpr int kAi = MP / kRpa;             // activation loads per chunk
+  static constexpr int kActOff = kCi * 1024;
+  static constexpr int kSt = kActOff + kAi * 1024;  // LDS bytes per wave
+  static_assert(S == 2 || S == 4, "chunk steps");
+  static_assert(MP == 4 || MP == 8, "padded activation rows");
+};
+template <int T, int S>
+struct Chunk {
+  uint4_t c[2 * T * S];
+  uint4_t a[8];
+};
 }  // namespace f8
 
-template <int W, int T>
-__global__ __launch_bounds__(64 * W) void gemv_fp8_mfma_kernel(
-    const uint8_t *__restrict__ w, const float *__restrict__ cs, int N, int K,
-    const uint16_t *__restrict__ x, int M, uint16_t *__restrict__ y) {
-  using namespace f8;
-  constexpr int ROWS = 16 * T;
-  constexpr int CLD = ROWS / 2;        // 1 KB loads per chunk (2 rows each)
+// (No __restrict__ on the inputs: the issue fence below must be able to
+// order their loads.)
+template <int T, int KS, int S, int MP>
+__global__ __launch_bounds__(64 * KS) void gemv_fp8_mfma_kernel(
+    const uint8_t *w, const float *cs, int N, int K, const uint16_t *x, int M, uint16_t *y) {
+  using C = f8::Cfg<T, S, MP>;
+  using R = f8::Chunk<T, S>;
   extern __shared__ uint4_t smem4[];
   uint8_t *smem = reinterpret_cast<uint8_t *>(smem4);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int ks = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int i = lane & 15, grp = lane >> 4;
-  const int n0 = blockIdx.x * ROWS;
-  uint8_t *wl = smem + wave * wave_lds<T>();
-  float4_t *red = reinterpret_cast<float4_t *>(smem + W * wave_lds<T>());
+  const int n0 = blockIdx.x * C::kRows;
+  uint8_t *ws = smem + ks * C::kSt;
 
-  const uint8_t *wg[CLD];
+  const int nct = K / (128 * S);
+  const int cps = (nct + KS - 1) / KS;
+  const int cb = ks * cps, ce = min(nct, cb + cps);
+
+  const uint8_t *wsrc[C::kCi];
 #pragma unroll
-  for (int q = 0; q < CLD; ++q)
-    wg[q] = w + (size_t)min(n0 + 2 * q + (lane >> 5), N - 1) * (size_t)K + 16 * (lane & 31);
-
-  const bool xact = i < M;
-  const uint16_t *xrow = x + (size_t)(xact ? i : 0) * (size_t)K + 32 * grp;
-  const int nsteps = (K + 127) >> 7;
-  const int nchunks = K / kRowB;
-  const int per = (nchunks + W - 1) / W;
-  const int c0 = min(nchunks, wave * per), c1 = min(nchunks, c0 + per);
+  for (int q = 0; q < C::kCi; ++q) {
+    const int r = q * C::kRpi + (lane % C::kRpi);
+    const int j = (lane / C::kRpi) ^ (q & C::kSwz);
+    wsrc[q] = w + (size_t)min(n0 + r, N - 1) * (size_t)K + 16 * j;
+  }
+  const uint16_t *asrc[C::kAi];
+#pragma unroll
+  for (int a = 0; a < C::kAi; ++a) {
+    const int r = min(a * C::kRpa + (lane % C::kRpa), M - 1);
+    const int j = (lane / C::kRpa) ^ a;
+    asrc[a] = x + (size_t)r * K + 8 * j;
+  }
+  auto load = [&](int c, R &rg) {
+#pragma unroll
+    for (int q = 0; q < C::kCi; ++q) rg.c[q] = load16_nt(wsrc[q] + (size_t)c * (128 * S));
+#pragma unroll
+    for (int a = 0; a < C::kAi; ++a) rg.a[a] = load16(asrc[a] + (size_t)c * (128 * S));
+    issue_fence();   // keep each chunk's loads together and ahead of later work
+  };
+  auto store = [&](const R &rg) {
+#pragma unroll
+    for (int q = 0; q < C::kCi; ++q) *reinterpret_cast<uint4_t *>(ws + 1024 * q + 16 * lane) = rg.c[q];
+#pragma unroll
+    for (int a = 0; a < C::kAi; ++a)
+      *reinterpret_cast<uint4_t *>(ws + C::kActOff + 1024 * a + 16 * lane) = rg.a[a];
+  };
 
   float4_t acc[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint4_t xr[kXr][4];
+  const int ar = i & (MP - 1), aa = ar / C::kRpa;   // activation row (columns >= MP wrap)
+  const int aoff = C::kActOff + 1024 * aa + 16 * (ar % C::kRpa);
+  auto consume = [&]() {
 #pragma unroll
-  for (int d = 0; d < kXr; ++d) {
+    for (int st = 0; st < S; ++st) {
+      uint4_t xv[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) xr[d][q] = uint4_t{0u, 0u, 0u, 0u};
-    if (xact && c0 * kCh + d < c1 * kCh) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) xr[d][q] = load16(xrow + 128 * (c0 * kCh + d) + 8 * q);
-    }
-  }
-  uint4_t cr[CLD];
-  if (c0 < c1) {
-#pragma unroll
-    for (int q = 0; q < CLD; ++q) cr[q] = load16_nt(wg[q] + (size_t)c0 * kRowB);
-  }
-  for (int c = c0; c < c1; ++c) {
-#pragma unroll
-    for (int q = 0; q < CLD; ++q)
-      *reinterpret_cast<uint4_t *>(wl + (2 * q + (lane >> 5)) * kRowP + 16 * (lane & 31)) = cr[q];
-    if (c + 1 < c1) {
-#pragma unroll
-      for (int q = 0; q < CLD; ++q) cr[q] = load16_nt(wg[q] + (size_t)(c + 1) * kRowB);
-    }
-#pragma unroll
-    for (int st = 0; st < kCh; ++st) {
-      const int slot = st % kXr;
+      for (int u = 0; u < 4; ++u) {
+        const int j = 16 * st + 4 * grp + u;
+        xv[u] = *reinterpret_cast<const uint4_t *>(ws + aoff + 16 * C::kRpa * (j ^ aa));
+      }
 #pragma unroll
       for (int t = 0; t < T; ++t) {
-        const uint8_t *src = wl + (16 * t + i) * kRowP + 128 * st + 32 * grp;
-        const uint4_t wq[2] = {*reinterpret_cast<const uint4_t *>(src),
-                               *reinterpret_cast<const uint4_t *>(src + 16)};
-        fp8_step(wq, xr[slot], acc[t]);
-      }
-      const int ahead = c * kCh + st + kXr;
-      if (xact && ahead < c1 * kCh) {
+        const int r = 16 * t + i, q = r / C::kRpi;
+        uint4_t wq[2];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) xr[slot][q] = load16(xrow + 128 * ahead + 8 * q);
-      }
-    }
-  }
-  // steps past the last whole chunk, read in the operand layout (last wave)
-  if (wave == W - 1) {
-    for (int s = nchunks * kCh; s < nsteps; ++s) {
-      uint4_t xv[4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-      bool hact[2];
-#pragma unroll
-      for (int hlf = 0; hlf < 2; ++hlf) {
-        hact[hlf] = 128 * s + 32 * grp + 16 * hlf < K;
-        if (hact[hlf] && xact) {
-          xv[2 * hlf] = load16(xrow + 128 * s + 16 * hlf);
-          xv[2 * hlf + 1] = load16(xrow + 128 * s + 16 * hlf + 8);
+        for (int h = 0; h < 2; ++h) {
+          const int j = 8 * st + 2 * grp + h;
+          wq[h] = *reinterpret_cast<const uint4_t *>(
+              ws + 1024 * q + 16 * (C::kRpi * (j ^ (q & C::kSwz)) + r % C::kRpi));
         }
-      }
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const uint8_t *row = w + (size_t)min(n0 + 16 * t + i, N - 1) * (size_t)K + 32 * grp;
-        uint4_t wq[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-#pragma unroll
-        for (int hlf = 0; hlf < 2; ++hlf)
-          if (hact[hlf]) wq[hlf] = load16_nt(row + 128 * s + 16 * hlf);
         fp8_step(wq, xv, acc[t]);
       }
     }
+  };
+
+  if (cb < ce) {
+    // The load past the slice re-reads its last chunk into registers that
+    // are never stored, so every path issues the same loads.
+    R r0;
+    load(cb, r0);
+    for (int c = cb; c < ce; ++c) {
+      store(r0);
+      load(min(c + 1, ce - 1), r0);
+      consume();
+    }
   }
 
+  if constexpr (KS > 1) {
+    wg_barrier();
+    float4_t *red = reinterpret_cast<float4_t *>(smem);
 #pragma unroll
-  for (int t = 0; t < T; ++t) red[(wave * T + t) * kWave + lane] = acc[t];
-  __syncthreads();
-  if (wave == 0 && xact) {
+    for (int t = 0; t < T; ++t) red[(ks * T + t) * kWave + lane] = acc[t];
+    wg_barrier();
+    if (ks == 0) {
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int v = 1; v < KS; ++v) acc[t] += red[(v * T + t) * kWave + lane];
+    }
+  }
+  if (ks == 0 && i < M) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      float4_t tot = red[t * kWave + lane];
-#pragma unroll
-      for (int v = 1; v < W; ++v) tot += red[(v * T + t) * kWave + lane];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int n = n0 + 16 * t + 4 * grp + r;
-        if (n < N) y[(size_t)i * N + n] = f32_to_f16_bits(tot[r] * cs[n]);
+        if (n < N) y[(size_t)i * N + n] = f32_to_f16_bits(acc[t][r] * cs[n]);
       }
     }
   }
 }
 
-template <int W, int T>
-static hipError_t launch_mfma_wt(const uint8_t *w, const float *cs, int N, int K,
-                                 const uint16_t *x, int M, uint16_t *y, hipStream_t stream) {
-  const int blocks = (N + 16 * T - 1) / (16 * T);
-  const size_t shmem = (size_t)W * f8::wave_lds<T>() + sizeof(float4_t) * W * T * kWave;
-  hipLaunchKernelGGL((gemv_fp8_mfma_kernel<W, T>), dim3(blocks), dim3(64 * W), shmem, stream,
-                     w, cs, N, K, x, M, y);
+template <int T, int KS, int S, int MP>
+static hipError_t launch_mfma_cfg(const uint8_t *w, const float *cs, int N, int K,
+                                  const uint16_t *x, int M, uint16_t *y, hipStream_t stream) {
+  using C = f8::Cfg<T, S, MP>;
+  constexpr int kLds = KS * C::kSt;
+  static_assert(T * kWave * 16 <= C::kSt, "reduction buffer");
+  static_assert(kLds <= 160 * 1024, "LDS per workgroup");
+  if (K % (128 * S) != 0) return hipErrorInvalidValue;   // chunks must tile K
+  static const hipError_t lds_ok = allow_lds((const void *)gemv_fp8_mfma_kernel<T, KS, S, MP>, kLds);
+  if (lds_ok != hipSuccess) return lds_ok;
+  const int blocks = (N + C::kRows - 1) / C::kRows;
+  hipLaunchKernelGGL((gemv_fp8_mfma_kernel<T, KS, S, MP>), dim3(blocks), dim3(64 * KS), kLds,
+                     stream, w, cs, N, K, x, M, y);
   return hipGetLastError();
 }
 
-// Tiles per wave T (weight rows sharing one activation operand) and waves
-// per workgroup W (K split), W * T <= 4 so the staging buffers fit in 64 KB
-// of LDS.  Measured on MI355X at M = 4 and 8: two tiles without K split for
-// wide matrices, one tile and two K splits otherwise.
-static void pick_tw(int N, int K, int &T, int &W) {
-  (void)K;
+// Tiles per wave, K split and chunk length, measured on MI355X at M = 3, 4
+// and 8 over K 5120..17408, N 5120..34816.
+template <int MP>
+static hipError_t launch_mfma_mp(const uint8_t *w, const float *cs, int N, int K,
+                                 const uint16_t *x, int M, uint16_t *y, hipStream_t stream) {
   const int tiles = (N + 15) / 16;
-  if (tiles >= 2000) { T = 2; W = 1; }
-  else { T = 1; W = 2; }
+  const bool s4 = K % 512 == 0;
+#define SKINNY_F8(T, KS, S) return launch_mfma_cfg<T, KS, S, MP>(w, cs, N, K, x, M, y, stream)
+  if (tiles >= 1536) {
+    if (M <= 4) SKINNY_F8(1, 1, 2);
+    SKINNY_F8(2, 1, 2);
+  }
+  if (tiles >= 512) {
+    if (s4) SKINNY_F8(1, 1, 4);
+    SKINNY_F8(1, 1, 2);
+  }
+  if (s4 && K >= 8192 && M > 4) SKINNY_F8(2, 4, 4);
+  if (s4) SKINNY_F8(1, 2, 4);
+  SKINNY_F8(1, 2, 2);
+#undef SKINNY_F8
 }
 
 static hipError_t launch_mfma(const uint8_t *w, const float *cs, int N, int K, const uint16_t *x,
                               int M, uint16_t *y, hipStream_t stream) {
-  int T, W;
-  pick_tw(N, K, T, W);
-#define SKINNY_F8_CASE(TT, WW) \
-  if (T == TT && W == WW) return launch_mfma_wt<WW, TT>(w, cs, N, K, x, M, y, stream);
-  SKINNY_F8_CASE(1, 1) SKINNY_F8_CASE(1, 2) SKINNY_F8_CASE(1, 4)
-  SKINNY_F8_CASE(2, 1) SKINNY_F8_CASE(2, 2)
-#undef SKINNY_F8_CASE
-  return hipErrorInvalidValue;
+  if (M <= 4) return launch_mfma_mp<4>(w, cs, N, K, x, M, y, stream);
+  return launch_mfma_mp<8>(w, cs, N, K, x, M, y, stream);
 }
 
 template <int M, int R>
@@ -308,7 +337,7 @@ static hipError_t launch_m(const uint8_t *w, const float *cs, int N, int K, cons
 
 hipError_t launch_gemv_fp8(const uint8_t *w, const float *cs, int N, int K, const uint16_t *x,
                            int M, uint16_t *y, hipStream_t stream) {
-  if (M >= kFp8MfmaMinM) return launch_mfma(w, cs, N, K, x, M, y, stream);
+  if (M >= kFp8MfmaMinM && K % 256 == 0) return launch_mfma(w, cs, N, K, x, M, y, stream);
   switch (M) {
     case 1: return launch_m<1>(w, cs, N, K, x, y, stream);
     case 2: return launch_m<2>(w, cs, N, K, x, y, stream);

@@ -25,8 +25,11 @@
 
 namespace skinny {
 
-// Activation rows from which the matrix-core kernel is used.
-constexpr int kQ4MfmaMinM = 5;
+// Activation rows from which the matrix-core kernel is used, and below
+// which the vector kernel keeps small, short matrices (measured on MI355X:
+// at M <= 4 it wins only for N <= 8191 with K < 8192).
+constexpr int kQ4MfmaMinM = 3;
+constexpr int kQ4VectorMaxM = 4;
 
 constexpr int next_pow2(int v) { return v <= 1 ? 1 : 2 * next_pow2((v + 1) / 2); }
 
@@ -112,43 +115,65 @@ __global__ __launch_bounds__(256) void mmvq_q4_0_kernel(
 }
 
 // Matrix-core variant for wider M.  One v_mfma_i32_16x16x64_i8 computes the
-// exact int32 block sums of 16 weight rows x 2 blocks x 8 activation rows.
-// K slot g (lane group l / 16) of a step covers block b + g/2, bytes
-// 8(g%2) .. 8(g%2)+7 of its 16 code bytes, i.e. elements 8(g%2) + 0..7
-// (low nibbles) and 16 + 8(g%2) + 0..7 (high nibbles):
+// exact int32 block sums of 16 weight rows x 2 blocks x 8 activation rows
+// (one 64-element step).  K slot g (lane group l / 16) of a step covers
+// block 2s + g/2, bytes 8(g%2) .. 8(g%2)+7 of its 16 code bytes, i.e.
+// elements 8(g%2) + 0..7 (low nibbles) and 16 + 8(g%2) + 0..7 (high
+// nibbles):
 //   * B operand (columns = weight rows): lane (j = l % 16, g) takes those 8
-//     bytes of row n0 + j and splits them into 16 codes with two ANDs and
+//     bytes of row 16t + j and splits them into 16 codes with two ANDs and
 //     two shift+ANDs;
 //   * A operand (rows a = 8h + m): block-diagonal, so a row only meets the
 //     K slots of its own block h -- lane (j, g) holds the matching 16 Q8_1
-//     codes of row m = j % 8 when j / 8 == g / 2 and m < M, else zeros; it
-//     is shared by the T weight tiles and kept four steps ahead in a ring;
-//   * lane l then owns isum for weight row n0 + l%16, block b + g/2 and
+//     codes of row m = j % 8 when j / 8 == g / 2, else zeros (read from a
+//     zero area of LDS); rows m >= M repeat row M - 1 and are dropped;
+//   * lane l then owns isum for weight row 16t + l%16, block 2s + g/2 and
 //     activation rows 4(g%2) .. 4(g%2)+3, and applies the float32 block
 //     epilogue acc += d4 * (d8 * isum - 8 * s8).
-// Each wave takes a contiguous range of K and stages it in chunks of 32
-// blocks in wave-private LDS: weight codes and scales are read
-// row-contiguously (a 128-bit load per lane covering 512 bytes of each of
-// two rows per instruction), the chunk's activation scales as (d8, 8 s8)
-// pairs; the next chunk is in flight while the current one is consumed,
-// and the last chunk may be partial.  Lanes l and l^32 (even and odd
-// blocks) and then the waves are summed at the end.
+// Data movement as for the NVFP4 and FP8 kernels: each wave streams its own
+// T tiles over its own slice of K with no barrier until the final sum, in
+// chunks of S steps.  A chunk -- weight codes and scales, the MP activation
+// code rows and their Q8_1 scales -- is read with 128-bit loads in
+// row-contiguous order into registers one chunk ahead of its use, then
+// written to a wave-private LDS buffer (1 KB blocks, 16-byte columns
+// XOR-swizzled per block so that the operand-layout reads hit distinct
+// banks; activation scales converted once to float pairs (d8, 8 s8)) and
+// read back in the operand layout.  Loads are issued in the order they are
+// consumed, so each wait covers exactly one chunk.  The workgroup's KS waves
+// split K; their partial tiles are summed in LDS.
 namespace q4 {
-constexpr int kCh = 16;                // block pairs per staged chunk
-constexpr int kBlk = 2 * kCh;          // blocks per chunk (32)
-constexpr int kRowB = kBlk * 16;       // code bytes per row per chunk (512)
-constexpr int kSclB = kBlk * 2;        // weight-scale bytes per row per chunk (64)
-constexpr int kRowP = kRowB + 16;      // padded LDS pitches
-constexpr int kSclP = kSclB + 16;
-constexpr int kActB = kBlk * 8 * 8;    // (d8, 8 s8) for 8 rows m per block (2 KB)
-constexpr int kXr = 4;                 // activation steps kept in flight
-template <int T>
-constexpr int wave_lds() { return 16 * T * (kRowP + kSclP) + kActB; }
+template <int T, int S, int MP>
+struct Cfg {
+  static constexpr int kRows = 16 * T;              // weight rows per wave
+  static constexpr int kCB = 32 * S;                // code bytes per row per chunk
+  static constexpr int kRpi = 1024 / kCB;           // code rows per 1 KB block
+  static constexpr int kSwz = S / 2 - 1;            // code column swizzle mask
+  static constexpr int kCi = kRows / kRpi;          // code loads per chunk
+  static constexpr int kWsB = kRows * 4 * S;        // weight-scale bytes per chunk
+  static constexpr int kRpa = 16 / S;               // activation rows per 1 KB block
+  static constexpr int kAi = MP / kRpa;             // activation code loads per chunk
+  static constexpr int kNd = S * MP / 4;            // lanes loading d8 (and as many s8)
+  static constexpr int kWsOff = kCi * 1024;
+  static constexpr int kActOff = kWsOff + kWsB;
+  static constexpr int kAsOff = kActOff + kAi * 1024;       // float (d8, 8 s8)[2S][8]
+  static constexpr int kZeroOff = kAsOff + 2 * S * 8 * 8;   // 1 KB of zeros
+  static constexpr int kSt = kZeroOff + 1024;               // LDS bytes per wave
+  static_assert(S == 4 || S == 8, "chunk steps");
+  static_assert(MP == 4 || MP == 8, "padded activation rows");
+  static_assert(kWsB <= 1024 && 2 * kNd <= 64, "one load per chunk for each kind of scale");
+};
+template <int T, int S>
+struct Chunk {
+  uint4_t c[T * S / 2];
+  uint4_t ws;
+  uint4_t a[4];
+  uint4_t as;
+};
 }  // namespace q4
 
 __device__ __forceinline__ void q4_mfma_step(const uint2_t &wq, const int4_t &aop, float d4,
                                              const float4_t &sa, const float4_t &sb,
-                                             float (&acc)[4]) {
+                                             float4_t &acc) {
   int4_t bop;
   bop[0] = (int)(wq.x & 0x0F0F0F0Fu);
   bop[1] = (int)(wq.y & 0x0F0F0F0Fu);
@@ -162,230 +187,207 @@ __device__ __forceinline__ void q4_mfma_step(const uint2_t &wq, const int4_t &ao
   acc[3] = fmaf(d4, fmaf(sb[2], (float)isum[3], -sb[3]), acc[3]);
 }
 
-// The 16 activation codes a lane contributes to the A operand of block
-// pair p (the caller zeroes them off the diagonal or past K).
-__device__ __forceinline__ int4_t q4_aop(const int8_t *arow, int p) {
-  const uint2_t lo = load8(arow + 64 * p);
-  const uint2_t hi = load8(arow + 64 * p + 16);
-  return int4_t{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
-}
-
-__device__ __forceinline__ int4_t keep_if(bool keep, const int4_t &v) {
-  return int4_t{keep ? v[0] : 0, keep ? v[1] : 0, keep ? v[2] : 0, keep ? v[3] : 0};
-}
-
-__device__ __forceinline__ uint4_t keep_if(bool keep, const uint4_t &v) {
-  return uint4_t{keep ? v[0] : 0u, keep ? v[1] : 0u, keep ? v[2] : 0u, keep ? v[3] : 0u};
-}
-
-template <int W, int T>
-__global__ __launch_bounds__(64 * W) void mmvq_q4_0_mfma_kernel(
-    const uint8_t *__restrict__ w_qs, const uint16_t *__restrict__ w_d, int N, int K,
-    const int8_t *__restrict__ a_qs, const uint16_t *__restrict__ a_d,
-    const uint16_t *__restrict__ a_s, int M, float *__restrict__ y) {
-  using namespace q4;
-  constexpr int ROWS = 16 * T;
-  constexpr int CLD = ROWS / 2;        // code loads per chunk (2 rows of 512 B each)
+// (No __restrict__ on the inputs: the issue fence below must be able to
+// order their loads.)
+template <int T, int KS, int S, int MP>
+__global__ __launch_bounds__(64 * KS) void mmvq_q4_0_mfma_kernel(
+    const uint8_t *w_qs, const uint16_t *w_d, int N, int K, const int8_t *a_qs,
+    const uint16_t *a_d, const uint16_t *a_s, int M, float *y) {
+  using C = q4::Cfg<T, S, MP>;
+  using R = q4::Chunk<T, S>;
   extern __shared__ uint4_t smem4[];
   uint8_t *smem = reinterpret_cast<uint8_t *>(smem4);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int ks = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int j = lane & 15, grp = lane >> 4;
-  const int hb = grp >> 1, bh = grp & 1, q0 = 2 * bh;
-  const int n0 = blockIdx.x * ROWS;
+  const int hb = grp >> 1, bh = grp & 1;
+  const int n0 = blockIdx.x * C::kRows;
   const int nb = K >> 5;
-  uint8_t *cl = smem + wave * wave_lds<T>();
-  uint8_t *sl = cl + ROWS * kRowP;
-  float4_t *al = reinterpret_cast<float4_t *>(sl + ROWS * kSclP);   // [32 blocks][4]
-  float4_t *red = reinterpret_cast<float4_t *>(smem + W * wave_lds<T>());
+  uint8_t *ws = smem + ks * C::kSt;
 
-  const size_t rowc = (size_t)(K >> 1);
-  const uint8_t *cg[CLD];
-  const uint8_t *sg[T];
-#pragma unroll
-  for (int q = 0; q < CLD; ++q)
-    cg[q] = w_qs + (size_t)min(n0 + 2 * q + (lane >> 5), N - 1) * rowc + 16 * (lane & 31);
-#pragma unroll
-  for (int q = 0; q < T; ++q)
-    sg[q] = reinterpret_cast<const uint8_t *>(w_d + (size_t)min(n0 + 16 * q + (lane >> 2), N - 1) * nb) +
-            16 * (lane & 3);
-  // activation-scale staging: lane -> block (lane & 31), rows m = 4 (lane >> 5) .. +3
-  const int ab = lane & 31, am0 = 4 * (lane >> 5);
+  const int nct = K / (64 * S);
+  const int cps = (nct + KS - 1) / KS;
+  const int cb = ks * cps, ce = min(nct, cb + cps);
 
-  const bool aact = ((j >> 3) == hb) && (j & 7) < M;
-  const int8_t *arow = a_qs + (size_t)(aact ? (j & 7) : 0) * (size_t)K + 32 * hb + 8 * bh;
-  // Staged chunks of 32 blocks need 16-byte aligned weight-scale rows
-  // (K % 256 == 0, so nb % 8 == 0); the last chunk may be partial, its
-  // missing pieces staged as zeros (zero codes and zero scales add nothing).
-  const bool staged = (K % 256) == 0;
-  const int nchunks = staged ? (nb + kBlk - 1) / kBlk : 0;
-  const int per = (nchunks + W - 1) / W;
-  const int c0 = min(nchunks, wave * per), c1 = min(nchunks, c0 + per);
+  // per-lane sources (chunk 0)
+  const uint8_t *csrc[C::kCi];
+#pragma unroll
+  for (int q = 0; q < C::kCi; ++q) {
+    const int r = q * C::kRpi + (lane % C::kRpi);
+    const int col = (lane / C::kRpi) ^ (q & C::kSwz);
+    csrc[q] = w_qs + (size_t)min(n0 + r, N - 1) * (size_t)(K >> 1) + 16 * col;
+  }
+  const bool wsact = lane < C::kWsB / 16;
+  const int wl = lane % (C::kWsB / 16);     // lanes past the scale bytes repeat one
+  const uint8_t *wssrc = reinterpret_cast<const uint8_t *>(
+      w_d + (size_t)min(n0 + wl % C::kRows, N - 1) * nb) + 16 * (wl / C::kRows);
+  const int8_t *asrc[C::kAi];
+#pragma unroll
+  for (int a = 0; a < C::kAi; ++a) {
+    const int r = min(a * C::kRpa + (lane % C::kRpa), M - 1);
+    const int col = (lane / C::kRpa) ^ a;
+    asrc[a] = a_qs + (size_t)r * K + 16 * col;
+  }
+  // activation scales: lanes [0, kNd) take d8, [kNd, 2 kNd) s8, as 16-byte
+  // pieces (8 blocks) of row m; the other lanes repeat lane 0
+  const int al = lane < 2 * C::kNd ? lane : 0;
+  const bool asd = al < C::kNd;
+  const int apc = (al % C::kNd) % (S / 4), am = (al % C::kNd) / (S / 4);
+  const uint16_t *assrc = (asd ? a_d : a_s) + (size_t)min(am, M - 1) * nb + 8 * apc;
 
-  float acc[T][4];
+  auto load = [&](int c, R &rg) {
 #pragma unroll
-  for (int t = 0; t < T; ++t)
+    for (int q = 0; q < C::kCi; ++q) rg.c[q] = load16_nt(csrc[q] + (size_t)c * C::kCB);
+    rg.ws = load16_nt(wssrc + (size_t)c * (4 * S));
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[t][r] = 0.f;
-
-  // Every prefetch below is unconditional, from an address clamped into the
-  // arrays, so that no branch separates a load from its use; what lies past
-  // K (or off the diagonal) is zeroed by a select when it is consumed.
-  // Staged chunks imply nb >= 8, so the clamps below stay in range.
-  const int pmax = (nb - 1 - hb) >> 1;             // last pair with this lane's block < nb
-  int4_t ar[kXr];
+    for (int a = 0; a < C::kAi; ++a) rg.a[a] = load16(asrc[a] + (size_t)c * (64 * S));
+    rg.as = load16(assrc + (size_t)c * (2 * S));
+    issue_fence();   // keep each chunk's loads together and ahead of later work
+  };
+  auto store = [&](const R &rg) {
 #pragma unroll
-  for (int d = 0; d < kXr; ++d) ar[d] = q4_aop(arow, min(c0 * kCh + d, pmax));
-
-  uint4_t cr[CLD], sr[T];
-  uint32_t avr[8];                     // raw binary16 bits of d8, s8 for 4 rows m
-  auto fetch = [&](int c) {
-    const int cb = min(c * kBlk + (lane & 31), nb - 1);
+    for (int q = 0; q < C::kCi; ++q) *reinterpret_cast<uint4_t *>(ws + 1024 * q + 16 * lane) = rg.c[q];
+    if (wsact) *reinterpret_cast<uint4_t *>(ws + C::kWsOff + 16 * lane) = rg.ws;
 #pragma unroll
-    for (int q = 0; q < CLD; ++q) cr[q] = load16_nt(cg[q] + (size_t)(cb - (lane & 31)) * 16);
-    const int sb = min(c * kBlk + 8 * (lane & 3), nb - 8);
+    for (int a = 0; a < C::kAi; ++a)
+      *reinterpret_cast<uint4_t *>(ws + C::kActOff + 1024 * a + 16 * lane) = rg.a[a];
+    if (lane < 2 * C::kNd) {
+      // 8 blocks of row am: float d8 at slot 0, 8 * s8 at slot 1
+      float *as = reinterpret_cast<float *>(ws + C::kAsOff) + 2 * am + (asd ? 0 : 1);
 #pragma unroll
-    for (int q = 0; q < T; ++q) sr[q] = load16_nt(sg[q] + (size_t)(sb - 8 * (lane & 3)) * 2);
-    const int abk = min(c * kBlk + ab, nb - 1);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = min(am0 + r, M - 1);
-      avr[2 * r] = a_d[(size_t)m * nb + abk];
-      avr[2 * r + 1] = a_s[(size_t)m * nb + abk];
+      for (int e = 0; e < 8; ++e) {
+        const uint16_t h = (uint16_t)(rg.as[e >> 1] >> (16 * (e & 1)));
+        const float v = f16_bits_to_f32(h);
+        as[16 * (8 * apc + e)] = asd ? v : 8.0f * v;
+      }
     }
   };
-  if (c0 < c1) fetch(c0);
-  for (int c = c0; c < c1; ++c) {
-    {
-      const bool cv = c * kBlk + (lane & 31) < nb;
-      const bool sv = c * kBlk + 8 * (lane & 3) < nb;
-      const bool av = c * kBlk + ab < nb;
+
+  float4_t acc[T];
 #pragma unroll
-      for (int q = 0; q < CLD; ++q)
-        *reinterpret_cast<uint4_t *>(cl + (2 * q + (lane >> 5)) * kRowP + 16 * (lane & 31)) =
-            keep_if(cv, cr[q]);
+  for (int t = 0; t < T; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  // A operand sources: row m = j % 8 of block h = j / 8, live when h == g / 2;
+  // both 8-byte pieces advance by a fixed stride per step
+  const int m = j & (MP - 1) & 7, ablk = m / C::kRpa;
+  const bool live = (j >> 3) == hb;
+  const int abase = C::kActOff + 1024 * ablk + 8 * bh + 16 * (m % C::kRpa);
+  const int alo = live ? abase + 16 * C::kRpa * ((2 * hb) ^ ablk) : C::kZeroOff;
+  const int ahi = live ? abase + 16 * C::kRpa * ((2 * hb + 1) ^ ablk) : C::kZeroOff + 8;
+  constexpr int kAStride = 64 * C::kRpa;                   // bytes per step (4 columns)
+  auto consume = [&]() {
 #pragma unroll
-      for (int q = 0; q < T; ++q)
-        *reinterpret_cast<uint4_t *>(sl + (16 * q + (lane >> 2)) * kSclP + 16 * (lane & 3)) =
-            keep_if(sv, sr[q]);
-      float v[8];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        v[2 * r] = av ? f16_bits_to_f32((uint16_t)avr[2 * r]) : 0.f;
-        v[2 * r + 1] = av ? 8.0f * f16_bits_to_f32((uint16_t)avr[2 * r + 1]) : 0.f;
-      }
-      al[4 * ab + 2 * (lane >> 5)] = float4_t{v[0], v[1], v[2], v[3]};
-      al[4 * ab + 2 * (lane >> 5) + 1] = float4_t{v[4], v[5], v[6], v[7]};
-    }
-    if (c + 1 < c1) fetch(c + 1);
-#pragma unroll
-    for (int st = 0; st < kCh; ++st) {
-      const int slot = st % kXr;
-      const int bl = 2 * st + hb;                  // this lane's block within the chunk
-      const bool live = aact && c * kBlk + bl < nb;
-      const int4_t aop = keep_if(live, ar[slot]);
-      const float4_t sa = al[4 * bl + q0], sb = al[4 * bl + q0 + 1];
+    for (int st = 0; st < S; ++st) {
+      const int bl = 2 * st + hb;                          // this lane's block in the chunk
+      const uint2_t lo = *reinterpret_cast<const uint2_t *>(ws + alo + (live ? kAStride * st : 0));
+      const uint2_t hi = *reinterpret_cast<const uint2_t *>(ws + ahi + (live ? kAStride * st : 0));
+      const int4_t aop = {(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+      const float4_t *asf = reinterpret_cast<const float4_t *>(ws + C::kAsOff + 64 * bl + 32 * bh);
+      const float4_t sa = asf[0], sb = asf[1];
 #pragma unroll
       for (int t = 0; t < T; ++t) {
-        const uint2_t wq = *reinterpret_cast<const uint2_t *>(cl + (16 * t + j) * kRowP + 16 * bl + 8 * bh);
-        const float d4 = f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(sl + (16 * t + j) * kSclP + 2 * bl));
-        q4_mfma_step(wq, aop, d4, sa, sb, acc[t]);
-      }
-      ar[slot] = q4_aop(arow, min(c * kCh + st + kXr, pmax));
-    }
-  }
-  // without staging (K % 256 != 0) the last wave reads every block directly
-  if (!staged && wave == W - 1) {
-    for (int p = 0; 2 * p < nb; ++p) {
-      const int b = 2 * p + hb;                    // this lane's block
-      const bool bact = b < nb;
-      int4_t aop = {0, 0, 0, 0};
-      float4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-      if (bact) {
-        aop = keep_if(aact, q4_aop(arow, p));
-        float v[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = min(4 * bh + r, M - 1);
-          v[2 * r] = f16_bits_to_f32(a_d[(size_t)m * nb + b]);
-          v[2 * r + 1] = 8.0f * f16_bits_to_f32(a_s[(size_t)m * nb + b]);
-        }
-        sa = float4_t{v[0], v[1], v[2], v[3]};
-        sb = float4_t{v[4], v[5], v[6], v[7]};
-      }
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const int nrow = min(n0 + 16 * t + j, N - 1);
-        uint2_t wq = {0u, 0u};
-        float d4 = 0.f;
-        if (bact) {
-          wq = load8_nt(w_qs + (size_t)nrow * rowc + 16 * b + 8 * bh);
-          d4 = f16_bits_to_f32(load_u16_nt(w_d + (size_t)nrow * nb + b));
-        }
+        const int r = 16 * t + j, q = r / C::kRpi;
+        const int col = (2 * st + hb) ^ (q & C::kSwz);
+        const uint2_t wq = *reinterpret_cast<const uint2_t *>(
+            ws + 1024 * q + 16 * (C::kRpi * col + r % C::kRpi) + 8 * bh);
+        const float d4 = f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(
+            ws + C::kWsOff + 16 * ((bl >> 3) * C::kRows + r) + 2 * (bl & 7)));
         q4_mfma_step(wq, aop, d4, sa, sb, acc[t]);
       }
     }
+  };
+
+  if (cb < ce) {
+    *reinterpret_cast<uint4_t *>(ws + C::kZeroOff + 16 * lane) = uint4_t{0u, 0u, 0u, 0u};
+    // The load past the slice re-reads its last chunk into registers that
+    // are never stored, so every path issues the same loads.
+    R r0;
+    load(cb, r0);
+    for (int c = cb; c < ce; ++c) {
+      store(r0);
+      load(min(c + 1, ce - 1), r0);
+      consume();
+    }
   }
+
+  if constexpr (KS > 1) {
+    wg_barrier();
+    float4_t *red = reinterpret_cast<float4_t *>(smem);
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
+    for (int t = 0; t < T; ++t) red[(ks * T + t) * kWave + lane] = acc[t];
+    wg_barrier();
+    if (ks == 0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[t][r] = add_swap32(acc[t][r]);
-    if (lane < 32)
-      red[(wave * T + t) * 32 + lane] = float4_t{acc[t][0], acc[t][1], acc[t][2], acc[t][3]};
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int v = 1; v < KS; ++v) acc[t] += red[(v * T + t) * kWave + lane];
+    }
   }
-  __syncthreads();
-  if (wave == 0 && lane < 32) {
+  // lanes l and l ^ 32 hold the two blocks of each step: add them
+  if (ks == 0) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      float4_t tot = red[t * 32 + lane];
+      float4_t v;
 #pragma unroll
-      for (int v = 1; v < W; ++v) tot += red[(v * T + t) * 32 + lane];
+      for (int r = 0; r < 4; ++r) v[r] = add_swap32(acc[t][r]);
       const int n = n0 + 16 * t + j;
-      if (n < N) {
+      if (lane < 32 && n < N) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int m = 4 * bh + r;
-          if (m < M) y[(size_t)m * N + n] = tot[r];
+          const int mm = 4 * bh + r;
+          if (mm < M) y[(size_t)mm * N + n] = v[r];
         }
       }
     }
   }
 }
 
-template <int W, int T>
-static hipError_t launch_mfma_wt(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
-                                 const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
-                                 int M, float *y, hipStream_t stream) {
-  const int blocks = (N + 16 * T - 1) / (16 * T);
-  const size_t shmem = (size_t)W * q4::wave_lds<T>() + sizeof(float4_t) * 32 * W * T;
-  hipLaunchKernelGGL((mmvq_q4_0_mfma_kernel<W, T>), dim3(blocks), dim3(64 * W), shmem,
+template <int T, int KS, int S, int MP>
+static hipError_t launch_mfma_cfg(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
+                                  const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
+                                  int M, float *y, hipStream_t stream) {
+  using C = q4::Cfg<T, S, MP>;
+  constexpr int kLds = KS * C::kSt;
+  static_assert(T * kWave * 16 <= C::kSt, "reduction buffer");
+  static_assert(kLds <= 160 * 1024, "LDS per workgroup");
+  if (K % (64 * S) != 0) return hipErrorInvalidValue;   // chunks must tile K
+  static const hipError_t lds_ok = allow_lds((const void *)mmvq_q4_0_mfma_kernel<T, KS, S, MP>, kLds);
+  if (lds_ok != hipSuccess) return lds_ok;
+  const int blocks = (N + C::kRows - 1) / C::kRows;
+  hipLaunchKernelGGL((mmvq_q4_0_mfma_kernel<T, KS, S, MP>), dim3(blocks), dim3(64 * KS), kLds,
                      stream, w_qs, w_d, N, K, a_qs, a_d, a_s, M, y);
   return hipGetLastError();
 }
 
-// Tiles per wave T (weight rows sharing one activation operand) and waves
-// per workgroup W (K split), W * T <= 4 so the staging buffers fit in 64 KB
-// of LDS.  Measured on MI355X at M = 8: wide matrices prefer two tiles and
-// few K splits, narrow ones four K splits to fill the machine.
-static void pick_tw(int N, int K, int &T, int &W) {
-  (void)K;
+// One tile per wave throughout; the K split grows as the tile count falls
+// so that enough waves stream (measured on MI355X at M = 3..8 over the
+// Llama-2-7B shapes: 1376..2000 tiles no split, 768 tiles two, 256 tiles
+// eight).
+template <int MP>
+static hipError_t launch_mfma_mp(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
+                                 const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
+                                 int M, float *y, hipStream_t stream) {
   const int tiles = (N + 15) / 16;
-  if (tiles >= 1024) { T = 2; W = tiles >= 2000 ? 1 : 2; }
-  else if (tiles >= 512) { T = 1; W = 2; }
-  else { T = 1; W = 4; }
+  const bool s8 = K % 512 == 0;
+#define SKINNY_Q4(T, KS, S) \
+  return launch_mfma_cfg<T, KS, S, MP>(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream)
+  if (tiles >= 1024) {
+    if (s8) SKINNY_Q4(1, 1, 8);
+    SKINNY_Q4(1, 1, 4);
+  }
+  if (tiles >= 512) {
+    if (s8) SKINNY_Q4(1, 2, 8);
+    SKINNY_Q4(1, 2, 4);
+  }
+  SKINNY_Q4(1, 8, 4);
+#undef SKINNY_Q4
 }
 
 static hipError_t launch_mfma(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                               const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
                               int M, float *y, hipStream_t stream) {
-  int T, W;
-  pick_tw(N, K, T, W);
-#define SKINNY_Q4_CASE(TT, WW)                                                              \
-  if (T == TT && W == WW)                                                                  \
-    return launch_mfma_wt<WW, TT>(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream);
-  SKINNY_Q4_CASE(1, 1) SKINNY_Q4_CASE(1, 2) SKINNY_Q4_CASE(1, 4)
-  SKINNY_Q4_CASE(2, 1) SKINNY_Q4_CASE(2, 2)
-#undef SKINNY_Q4_CASE
-  return hipErrorInvalidValue;
+  if (M <= 4) return launch_mfma_mp<4>(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream);
+  return launch_mfma_mp<8>(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream);
 }
 
 template <int M, int R, bool NT = true>
@@ -422,7 +424,9 @@ static hipError_t launch_m(const uint8_t *w_qs, const uint16_t *w_d, int N, int 
 hipError_t launch_mmvq_q4_0(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                             const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
                             int M, float *y, hipStream_t stream) {
-  if (M >= kQ4MfmaMinM) return launch_mfma(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream);
+  const bool small = M <= kQ4VectorMaxM && N < 8192 && K < 8192;
+  if (M >= kQ4MfmaMinM && K % 256 == 0 && !small)
+    return launch_mfma(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream);
   switch (M) {
     case 1: return launch_m<1>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
     case 2: return launch_m<2>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);

@@ -158,7 +158,11 @@ def run_q4(w_qs, w_d, a_qs, a_d, a_s):
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
-@pytest.mark.parametrize("N,K", [(1, 32), (4096 + 37, 256), (4099, 1376), (257, 11008)])
+@pytest.mark.parametrize("N,K", [(1, 32), (4096 + 37, 256), (4099, 1376), (257, 11008),
+                                 # matrix-core paths: wide / mid / narrow, chunks of 4
+                                 # and 8 steps, ragged tiles, unequal K slices and
+                                 # one empty slice
+                                 (25000, 768), (9000, 1280), (40, 768), (700, 8192)])
 def test_mmvq_q4_0_vs_oracle(M, N, K):
     w_qs, w_d = inputs.q4_0_weights(N, K, 7 * N + K)
     x = inputs.normal_f32(M, K, 3 * M + K)
@@ -276,7 +280,9 @@ def run_fp8(w, cs, x):
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
-@pytest.mark.parametrize("N,K", [(1, 16), (4096 + 3, 272), (1030, 5120), (129, 17408)])
+@pytest.mark.parametrize("N,K", [(1, 16), (4096 + 3, 272), (1030, 5120), (129, 17408),
+                                 # matrix-core paths, as for NVFP4
+                                 (25000, 768), (9000, 1280), (40, 768)])
 def test_gemv_fp8_vs_oracle(M, N, K):
     w, cs = inputs.fp8_weights(N, K, 3 * N + K)
     x = inputs.normal_f16_bits(M, K, 4 * M + K)
