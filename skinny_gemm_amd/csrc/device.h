@@ -199,6 +199,14 @@ __device__ __forceinline__ float add_swap32(float x) {
 // hardware sees loads in program order (what vmcnt counts).
 __device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
 
+// Fence plus scheduling barrier: no instruction (arithmetic included) is
+// moved across it, so all loads above it are in flight before any of their
+// results is waited for.
+__device__ __forceinline__ void issue_all() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Workgroup barrier with no implied memory wait (in-flight loads stay in
 // flight); LDS accesses are not moved across it.
 __device__ __forceinline__ void wg_barrier() {

@@ -23,10 +23,11 @@ constexpr int kFp8MfmaMinM = 3;
 
 constexpr int next_pow2_f(int v) { return v <= 1 ? 1 : 2 * next_pow2_f((v + 1) / 2); }
 
-template <int M, int R>
+// (No __restrict__ on the inputs: the issue barrier below must be able to
+// keep a round's loads ahead of its arithmetic.)
+template <int M, int R, int U>
 __global__ __launch_bounds__(256) void gemv_fp8_kernel(
-    const uint8_t *__restrict__ w, const float *__restrict__ cs, int N, int K,
-    const uint16_t *__restrict__ x, uint16_t *__restrict__ y) {
+    const uint8_t *w, const float *cs, int N, int K, const uint16_t *x, uint16_t *y) {
   const int lane = threadIdx.x & 63;
   const int n0 = (blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6)) * R;
   if (n0 >= N) return;
@@ -45,33 +46,49 @@ __global__ __launch_bounds__(256) void gemv_fp8_kernel(
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
 
-#pragma unroll 2
-  for (int c = lane; c < nc; c += kWave) {
-    uint4_t wq[R];
+  // U chunks per lane per round, all loaded before any is used (one memory
+  // round trip per round); chunks past the row end load chunk nc - 1 again
+  // and are not accumulated.
+  // U == 0: one chunk per iteration, unrolled twice, the compiler free to
+  // pipeline loads of later iterations under the arithmetic.
+  constexpr int UU = U > 0 ? U : 1;
+  constexpr int kUnroll = U > 0 ? 1 : 2;
+#pragma unroll kUnroll
+  for (int c0 = lane; c0 < nc; c0 += UU * kWave) {
+    uint4_t wq[UU][R];
+    uint4_t xv[UU][M][2];
 #pragma unroll
-    for (int r = 0; r < R; ++r) wq[r] = load16_nt(wrow[r] + 16 * c);
-    uint4_t xv[M][2];
+    for (int u = 0; u < UU; ++u) {
+      const int c = min(c0 + u * kWave, nc - 1);
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const uint16_t *xp = x + (size_t)m * K + 16 * c;
-      xv[m][0] = load16(xp);
-      xv[m][1] = load16(xp + 8);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      // word i holds elements 4i..4i+3: pair (4i, 4i+1) and (4i+2, 4i+3)
-      uint32_t wh[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        wh[2 * i + 0] = __builtin_bit_cast(uint32_t, e4m3x2_to_h2<false>(wq[r][i]));
-        wh[2 * i + 1] = __builtin_bit_cast(uint32_t, e4m3x2_to_h2<true>(wq[r][i]));
-      }
+      for (int r = 0; r < R; ++r) wq[u][r] = load16_nt(wrow[r] + 16 * c);
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        float a = acc[r][m];
+        const uint16_t *xp = x + (size_t)m * K + 16 * c;
+        xv[u][m][0] = load16(xp);
+        xv[u][m][1] = load16(xp + 8);
+      }
+    }
+    if constexpr (U > 0) issue_all();
 #pragma unroll
-        for (int p = 0; p < 8; ++p) a = dot2_f16(wh[p], xv[m][p >> 2][p & 3], a);
-        acc[r][m] = a;
+    for (int u = 0; u < UU; ++u) {
+      const bool live = c0 + u * kWave < nc;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        // word i holds elements 4i..4i+3: pair (4i, 4i+1) and (4i+2, 4i+3)
+        uint32_t wh[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          wh[2 * i + 0] = __builtin_bit_cast(uint32_t, e4m3x2_to_h2<false>(wq[u][r][i]));
+          wh[2 * i + 1] = __builtin_bit_cast(uint32_t, e4m3x2_to_h2<true>(wq[u][r][i]));
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          float a = acc[r][m];
+#pragma unroll
+          for (int p = 0; p < 8; ++p) a = dot2_f16(wh[p], xv[u][m][p >> 2][p & 3], a);
+          acc[r][m] = live ? a : acc[r][m];
+        }
       }
     }
   }
@@ -305,33 +322,32 @@ static hipError_t launch_mfma(const uint8_t *w, const float *cs, int N, int K, c
   return launch_mfma_mp<8>(w, cs, N, K, x, M, y, stream);
 }
 
-template <int M, int R>
-static hipError_t launch_mr(const uint8_t *w, const float *cs, int N, int K, const uint16_t *x,
-                            uint16_t *y, hipStream_t stream) {
+template <int M, int R, int U>
+static hipError_t launch_mru(const uint8_t *w, const float *cs, int N, int K, const uint16_t *x,
+                             uint16_t *y, hipStream_t stream) {
   const int waves = (N + R - 1) / R;
   const int blocks = (waves + 3) / 4;
-  hipLaunchKernelGGL((gemv_fp8_kernel<M, R>), dim3(blocks), dim3(256), 0, stream,
+  hipLaunchKernelGGL((gemv_fp8_kernel<M, R, U>), dim3(blocks), dim3(256), 0, stream,
                      w, cs, N, K, x, y);
   return hipGetLastError();
 }
 
-// Two rows per wave: few 128-bit weight loads in flight per lane and many
-// waves measured best on MI355X at M <= 2 for every shape tried (K 4096 to
-// 17408, N 4096 to 34816); four or eight rows only pay once the activation
-// block is reused across more rows, which is where the matrix-core kernel
-// takes over.
-static int rows_per_wave(int N, int M) {
-  (void)N;
-  return M <= 2 ? 2 : 4;
-}
-
+// Vector kernel shape: two rows per wave measured best on MI355X at M <= 2
+// for every shape tried (K 4096 to 17408, N 4096 to 34816).  Each lane
+// loads up to U = 6 chunks of a row per round (one memory round trip per
+// round: 5.9 -> 6.2 TB/s on a 5120 x 34816 matrix), U fitted to the chunks
+// per lane.  Wider M (only for K % 256 != 0) takes four rows per wave.
 template <int M>
 static hipError_t launch_m(const uint8_t *w, const float *cs, int N, int K, const uint16_t *x,
                            uint16_t *y, hipStream_t stream) {
-  switch (rows_per_wave(N, M)) {
-    case 2: return launch_mr<M, 2>(w, cs, N, K, x, y, stream);
-    case 4: return launch_mr<M, 4>(w, cs, N, K, x, y, stream);
-    default: return launch_mr<M, 8>(w, cs, N, K, x, y, stream);
+  if constexpr (M <= 2) {
+    const int per_lane = ((K >> 4) + kWave - 1) / kWave;
+    if (per_lane <= 2) return launch_mru<M, 2, 2>(w, cs, N, K, x, y, stream);
+    if (per_lane <= 3) return launch_mru<M, 2, 3>(w, cs, N, K, x, y, stream);
+    if (per_lane <= 4) return launch_mru<M, 2, 4>(w, cs, N, K, x, y, stream);
+    return launch_mru<M, 2, 6>(w, cs, N, K, x, y, stream);
+  } else {
+    return launch_mru<M, 4, 1>(w, cs, N, K, x, y, stream);
   }
 }
 

@@ -28,22 +28,24 @@ constexpr int kNvfp4MfmaMinM = 3;
 
 constexpr int next_pow2_n(int v) { return v <= 1 ? 1 : 2 * next_pow2_n((v + 1) / 2); }
 
-template <int M, int R>
+// (No __restrict__ on the inputs: the issue barrier below must be able to
+// keep a round's loads ahead of its arithmetic.)
+template <int M, int R, int U>
 __global__ __launch_bounds__(256) void gemv_nvfp4_kernel(
-    const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales, float g,
-    int N, int K, const uint16_t *__restrict__ x, uint16_t *__restrict__ y) {
+    const uint8_t *codes, const uint8_t *scales, float g, int N, int K, const uint16_t *x,
+    uint16_t *y) {
   const int lane = threadIdx.x & 63;
   const int n0 = (blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6)) * R;
   if (n0 >= N) return;
   const int nc = K >> 5;                    // 32-element chunks per row
 
   const uint8_t *crow[R];
-  const uint8_t *srow[R];
+  const uint16_t *srow[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int n = min(n0 + r, N - 1);
     crow[r] = codes + (size_t)n * (size_t)(K >> 1);
-    srow[r] = scales + (size_t)n * (size_t)(K >> 4);
+    srow[r] = reinterpret_cast<const uint16_t *>(scales + (size_t)n * (size_t)(K >> 4));
   }
 
   float acc[R][M];
@@ -52,46 +54,63 @@ __global__ __launch_bounds__(256) void gemv_nvfp4_kernel(
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
 
-#pragma unroll 2
-  for (int c = lane; c < nc; c += kWave) {
-    uint4_t wq[R];
-    uint32_t sc2[R];
+  // U chunks per lane per round, all loaded before any is used (one memory
+  // round trip per round); chunks past the row end load chunk nc - 1 again
+  // and are not accumulated.
+  // U == 0: one chunk per iteration, unrolled twice, the compiler free to
+  // pipeline loads of later iterations under the arithmetic.
+  constexpr int UU = U > 0 ? U : 1;
+  constexpr int kUnroll = U > 0 ? 1 : 2;
+#pragma unroll kUnroll
+  for (int c0 = lane; c0 < nc; c0 += UU * kWave) {
+    uint4_t wq[UU][R];
+    uint32_t sc2[UU][R];
+    uint4_t xv[UU][M][4];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      wq[r] = load16_nt(crow[r] + 16 * c);
-      sc2[r] = load_u16_nt(reinterpret_cast<const uint16_t *>(srow[r]) + c);
-    }
-    // activations of the chunk: 32 binary16 = 16 pairs per row m
-    uint4_t xv[M][4];
+    for (int u = 0; u < UU; ++u) {
+      const int c = min(c0 + u * kWave, nc - 1);
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const uint16_t *xp = x + (size_t)m * K + 32 * c;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) xv[m][q] = load16(xp + 8 * q);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      // decode: word i, byte j -> elements 8i+2j (low nibble), 8i+2j+1
-      uint32_t wh[16];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        wh[4 * i + 0] = __builtin_bit_cast(uint32_t, e2m1x2_to_h2<0>(wq[r][i]));
-        wh[4 * i + 1] = __builtin_bit_cast(uint32_t, e2m1x2_to_h2<1>(wq[r][i]));
-        wh[4 * i + 2] = __builtin_bit_cast(uint32_t, e2m1x2_to_h2<2>(wq[r][i]));
-        wh[4 * i + 3] = __builtin_bit_cast(uint32_t, e2m1x2_to_h2<3>(wq[r][i]));
+      for (int r = 0; r < R; ++r) {
+        wq[u][r] = load16_nt(crow[r] + 16 * c);
+        sc2[u][r] = load_u16_nt(srow[r] + c);
       }
-      const float s0 = e4m3_to_f32<0>(sc2[r]) * g;
-      const float s1 = e4m3_to_f32<1>(sc2[r]) * g;
+      // activations of the chunk: 32 binary16 = 16 pairs per row m
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        // pair p (0..15) of the chunk is dword p%4 of xv[m][p/4]
-        float p0 = 0.0f, p1 = 0.0f;
+        const uint16_t *xp = x + (size_t)m * K + 32 * c;
 #pragma unroll
-        for (int p = 0; p < 8; ++p) p0 = dot2_f16(wh[p], xv[m][p >> 2][p & 3], p0);
+        for (int q = 0; q < 4; ++q) xv[u][m][q] = load16(xp + 8 * q);
+      }
+    }
+    if constexpr (U > 0) issue_all();
 #pragma unroll
-        for (int p = 8; p < 16; ++p) p1 = dot2_f16(wh[p], xv[m][p >> 2][p & 3], p1);
-        acc[r][m] = fmaf(p0, s0, acc[r][m]);
-        acc[r][m] = fmaf(p1, s1, acc[r][m]);
+    for (int u = 0; u < UU; ++u) {
+      const bool live = c0 + u * kWave < nc;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        // decode: word i, byte j -> elements 8i+2j (low nibble), 8i+2j+1
+        uint32_t wh[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          wh[4 * i + 0] = __builtin_bit_cast(uint32_t, e2m1x2_to_h2<0>(wq[u][r][i]));
+          wh[4 * i + 1] = __builtin_bit_cast(uint32_t, e2m1x2_to_h2<1>(wq[u][r][i]));
+          wh[4 * i + 2] = __builtin_bit_cast(uint32_t, e2m1x2_to_h2<2>(wq[u][r][i]));
+          wh[4 * i + 3] = __builtin_bit_cast(uint32_t, e2m1x2_to_h2<3>(wq[u][r][i]));
+        }
+        const float s0 = e4m3_to_f32<0>(sc2[u][r]) * g;
+        const float s1 = e4m3_to_f32<1>(sc2[u][r]) * g;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          // pair p (0..15) of the chunk is dword p%4 of xv[u][m][p/4]
+          float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+          for (int p = 0; p < 8; ++p) p0 = dot2_f16(wh[p], xv[u][m][p >> 2][p & 3], p0);
+#pragma unroll
+          for (int p = 8; p < 16; ++p) p1 = dot2_f16(wh[p], xv[u][m][p >> 2][p & 3], p1);
+          float a = fmaf(p0, s0, acc[r][m]);
+          a = fmaf(p1, s1, a);
+          acc[r][m] = live ? a : acc[r][m];
+        }
       }
     }
   }
@@ -350,31 +369,33 @@ static hipError_t launch_mfma(const uint8_t *codes, const uint8_t *scales, float
   return launch_mfma_mp<8>(codes, scales, g, N, K, x, M, y, stream);
 }
 
-template <int M, int R>
-static hipError_t launch_mr(const uint8_t *codes, const uint8_t *scales, float g, int N, int K,
-                            const uint16_t *x, uint16_t *y, hipStream_t stream) {
+template <int M, int R, int U>
+static hipError_t launch_mru(const uint8_t *codes, const uint8_t *scales, float g, int N,
+                             int K, const uint16_t *x, uint16_t *y, hipStream_t stream) {
   const int waves = (N + R - 1) / R;
   const int blocks = (waves + 3) / 4;
-  hipLaunchKernelGGL((gemv_nvfp4_kernel<M, R>), dim3(blocks), dim3(256), 0, stream,
+  hipLaunchKernelGGL((gemv_nvfp4_kernel<M, R, U>), dim3(blocks), dim3(256), 0, stream,
                      codes, scales, g, N, K, x, y);
   return hipGetLastError();
 }
 
-// Two rows per wave measured best on MI355X at M <= 2 for every shape
-// tried (K 4096 to 17408, N 4096 to 34816): few weight loads in flight per
-// lane and many waves.  Wider M runs on the matrix-core kernel.
-static int rows_per_wave(int N, int M) {
-  (void)N;
-  return M <= 2 ? 2 : 4;
-}
-
+// Vector kernel shape: two rows per wave measured best on MI355X at M <= 2
+// for every shape tried (K 4096 to 17408, N 4096 to 34816).  A row of up to
+// 4 chunks per lane is loaded in one round (one memory round trip: 3.9 ->
+// 4.7 TB/s on a 5120 x 34816 matrix); longer rows keep the pipelined loop,
+// faster there than several rounds.  Wider M (only for K % 256 != 0) takes
+// four rows per wave.
 template <int M>
 static hipError_t launch_m(const uint8_t *codes, const uint8_t *scales, float g, int N, int K,
                            const uint16_t *x, uint16_t *y, hipStream_t stream) {
-  switch (rows_per_wave(N, M)) {
-    case 2: return launch_mr<M, 2>(codes, scales, g, N, K, x, y, stream);
-    case 4: return launch_mr<M, 4>(codes, scales, g, N, K, x, y, stream);
-    default: return launch_mr<M, 8>(codes, scales, g, N, K, x, y, stream);
+  if constexpr (M <= 2) {
+    const int per_lane = ((K >> 5) + kWave - 1) / kWave;
+    if (per_lane <= 2) return launch_mru<M, 2, 2>(codes, scales, g, N, K, x, y, stream);
+    if (per_lane <= 3) return launch_mru<M, 2, 3>(codes, scales, g, N, K, x, y, stream);
+    if (per_lane <= 4) return launch_mru<M, 2, 4>(codes, scales, g, N, K, x, y, stream);
+    return launch_mru<M, 2, 0>(codes, scales, g, N, K, x, y, stream);
+  } else {
+    return launch_mru<M, 4, 1>(codes, scales, g, N, K, x, y, stream);
   }
 }
 

@@ -33,11 +33,12 @@ constexpr int kQ4VectorMaxM = 4;
 
 constexpr int next_pow2(int v) { return v <= 1 ? 1 : 2 * next_pow2((v + 1) / 2); }
 
-template <int M, int R, bool NT>
+// (No __restrict__ on the inputs: the issue fence below must be able to
+// keep a round's loads ahead of its arithmetic.)
+template <int M, int R, int U, bool NT>
 __global__ __launch_bounds__(256) void mmvq_q4_0_kernel(
-    const uint8_t *__restrict__ w_qs, const uint16_t *__restrict__ w_d, int N, int K,
-    const int8_t *__restrict__ a_qs, const uint16_t *__restrict__ a_d,
-    const uint16_t *__restrict__ a_s, float *__restrict__ y) {
+    const uint8_t *w_qs, const uint16_t *w_d, int N, int K, const int8_t *a_qs,
+    const uint16_t *a_d, const uint16_t *a_s, float *y) {
   const int lane = threadIdx.x & 63;
   const int n0 = (blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6)) * R;
   if (n0 >= N) return;
@@ -58,44 +59,58 @@ __global__ __launch_bounds__(256) void mmvq_q4_0_kernel(
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
 
-#pragma unroll 2
-  for (int b = lane; b < nb; b += kWave) {
-    uint4_t wq[R];
-    float d4[R];
+  // U blocks per lane per round, all loaded before any is used, so a row of
+  // up to 64 U blocks costs one memory round trip.  Blocks past the row end
+  // load block nb - 1 again and are not accumulated.
+  for (int b0 = lane; b0 < nb; b0 += U * kWave) {
+    uint4_t wq[U][R];
+    uint16_t d4h[U][R];
+    uint4_t aq0[U][M], aq1[U][M];
+    uint16_t d8h[U][M], s8h[U][M];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      wq[r] = NT ? load16_nt(wrow[r] + 16 * b) : load16(wrow[r] + 16 * b);
-      d4[r] = f16_bits_to_f32(NT ? load_u16_nt(drow[r] + b) : drow[r][b]);
-    }
-    uint4_t aq0[M], aq1[M];
-    float d8[M], s8x8[M];
+    for (int u = 0; u < U; ++u) {
+      const int b = min(b0 + u * kWave, nb - 1);
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const int8_t *ap = a_qs + (size_t)m * K + 32 * b;
-      aq0[m] = load16(ap);
-      aq1[m] = load16(ap + 16);
-      d8[m] = f16_bits_to_f32(a_d[(size_t)m * nb + b]);
-      s8x8[m] = 8.0f * f16_bits_to_f32(a_s[(size_t)m * nb + b]);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      // low nibbles = codes 0..15 of the block, high nibbles = codes 16..31
-      uint32_t lo[4], hi[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lo[i] = wq[r][i] & 0x0F0F0F0Fu;
-        hi[i] = (wq[r][i] >> 4) & 0x0F0F0F0Fu;
+      for (int r = 0; r < R; ++r) {
+        wq[u][r] = NT ? load16_nt(wrow[r] + 16 * b) : load16(wrow[r] + 16 * b);
+        d4h[u][r] = NT ? load_u16_nt(drow[r] + b) : drow[r][b];
       }
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        int32_t isum = 0;
+        const int8_t *ap = a_qs + (size_t)m * K + 32 * b;
+        aq0[u][m] = load16(ap);
+        aq1[u][m] = load16(ap + 16);
+        d8h[u][m] = a_d[(size_t)m * nb + b];
+        s8h[u][m] = a_s[(size_t)m * nb + b];
+      }
+    }
+    issue_all();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool live = b0 + u * kWave < nb;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        // low nibbles = codes 0..15 of the block, high nibbles = codes 16..31
+        uint32_t lo[4], hi[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          isum = dot4_i8(lo[i], aq0[m][i], isum);
-          isum = dot4_i8(hi[i], aq1[m][i], isum);
+          lo[i] = wq[u][r][i] & 0x0F0F0F0Fu;
+          hi[i] = (wq[u][r][i] >> 4) & 0x0F0F0F0Fu;
         }
-        const float t = fmaf(d8[m], (float)isum, -s8x8[m]);
-        acc[r][m] = fmaf(d4[r], t, acc[r][m]);
+        const float d4 = f16_bits_to_f32(d4h[u][r]);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          int32_t isum = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            isum = dot4_i8(lo[i], aq0[u][m][i], isum);
+            isum = dot4_i8(hi[i], aq1[u][m][i], isum);
+          }
+          const float t = fmaf(f16_bits_to_f32(d8h[u][m]), (float)isum,
+                               -8.0f * f16_bits_to_f32(s8h[u][m]));
+          const float a = fmaf(d4, t, acc[r][m]);
+          acc[r][m] = live ? a : acc[r][m];
+        }
       }
     }
   }
@@ -390,34 +405,37 @@ static hipError_t launch_mfma(const uint8_t *w_qs, const uint16_t *w_d, int N, i
   return launch_mfma_mp<8>(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream);
 }
 
-template <int M, int R, bool NT = true>
-static hipError_t launch_mr(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
-                            const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
-                            float *y, hipStream_t stream) {
+template <int M, int R, int U>
+static hipError_t launch_mru(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
+                             const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
+                             float *y, hipStream_t stream) {
   const int waves = (N + R - 1) / R;
   const int blocks = (waves + 3) / 4;
-  hipLaunchKernelGGL((mmvq_q4_0_kernel<M, R, NT>), dim3(blocks), dim3(256), 0, stream,
+  hipLaunchKernelGGL((mmvq_q4_0_kernel<M, R, U, true>), dim3(blocks), dim3(256), 0, stream,
                      w_qs, w_d, N, K, a_qs, a_d, a_s, y);
   return hipGetLastError();
 }
 
-// Rows per wave for the vector kernel: two rows (a handful of 128-bit
-// weight loads in flight per lane, many waves) measured best on MI355X at
-// M <= 4 on every Llama-2-7B shape; four at wider M, where the activation
-// block is reused across more rows.
-static int rows_per_wave(int N, int M) {
-  (void)N;
-  return M <= 4 ? 2 : 4;
-}
-
+// Vector kernel shape: two rows per wave (a handful of 128-bit weight loads
+// in flight per lane, many waves) measured best on MI355X at M <= 4 on
+// every Llama-2-7B shape.  At M <= 2 each lane loads all of its blocks of a
+// row in one round (U = blocks per lane, up to 6 = K 12288) -- long rows
+// are otherwise bound by successive memory round trips (7.8 -> 6.3 us for
+// an 11008 x 4096 matrix).
 template <int M>
 static hipError_t launch_m(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                            const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
                            float *y, hipStream_t stream) {
-  switch (rows_per_wave(N, M)) {
-    case 2: return launch_mr<M, 2>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
-    case 4: return launch_mr<M, 4>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
-    default: return launch_mr<M, 8>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+  if constexpr (M <= 2) {
+    const int per_lane = ((K >> 5) + kWave - 1) / kWave;
+    if (per_lane > 4) return launch_mru<M, 2, 6>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+    if (per_lane > 3) return launch_mru<M, 2, 4>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+    if (per_lane > 2) return launch_mru<M, 2, 3>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+    return launch_mru<M, 2, 2>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+  } else if constexpr (M <= 4) {
+    return launch_mru<M, 2, 2>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+  } else {
+    return launch_mru<M, 4, 2>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
   }
 }
 
