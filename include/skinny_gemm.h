@@ -54,6 +54,9 @@ extern "C" {
 #define SKINNY_MAX_N  (1 << 28)
 #define SKINNY_MAX_M_GEMV   8
 #define SKINNY_MAX_M_QUANT  65536
+/* mmvq_q4_0_f32act: decode widths only, one row of K in LDS per workgroup. */
+#define SKINNY_MAX_M_F32ACT 2
+#define SKINNY_MAX_K_F32ACT 12288
 
 /* Static, human-readable text for a status code. */
 const char *skinny_status_string(int status);
@@ -103,6 +106,26 @@ int quantize_act_q8_1(const float *x, int M, int K,
 int mmvq_q4_0(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
               const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
               int M, float *y, void *stream);
+
+/*
+ * mmvq_q4_0_f32act -- quantize_act_q8_1 and mmvq_q4_0 in one launch, for
+ * decode (M = 1 or 2).
+ *
+ * The same computation as quantize_act_q8_1(x) followed by mmvq_q4_0 on its
+ * output ("Machine Learning on NVIDIA CMP", "TL;DR" and "The DP2A patch":
+ * the activations are quantized to int8 blocks on the device before the
+ * int8 dot), with the same block arithmetic, so y is bit-identical to the
+ * two calls; the Q8_1 activations are kept in on-chip memory and never
+ * written out, which saves the second launch and its round trip.
+ *   w_qs, w_d  planar Q4_0 weights as for mmvq_q4_0.
+ *   x          float32 [M][K] row-major, 16-byte aligned.
+ *   y          float32 [M][N] row-major, 4-byte aligned.
+ *   0 <= M <= SKINNY_MAX_M_F32ACT (else SKINNY_ERR_M; wider M: call the two
+ *   entry points); K % 32 == 0 and K <= SKINNY_MAX_K_F32ACT (else
+ *   SKINNY_ERR_SHAPE).
+ */
+int mmvq_q4_0_f32act(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
+                     const float *x, int M, float *y, void *stream);
 
 /*
  * gemv_nvfp4_w4a16 -- y = x * W^T for NVFP4 weights and binary16 activations.

@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     lib,
     library_path,
     mmvq_q4_0,
+    mmvq_q4_0_f32act,
     quantize_act_q8_1,
     status_string,
 )

@@ -22,7 +22,7 @@ ERR_ALIGN = -3
 ERR_M = -4
 ERR_LAUNCH = -5
 
-EXPORTS = ("skinny_status_string", "quantize_act_q8_1", "mmvq_q4_0",
+EXPORTS = ("skinny_status_string", "quantize_act_q8_1", "mmvq_q4_0", "mmvq_q4_0_f32act",
            "gemv_nvfp4_w4a16", "gemv_fp8_w8a16")
 
 _lib = None
@@ -55,6 +55,8 @@ def lib():
     L.quantize_act_q8_1.restype = I
     L.mmvq_q4_0.argtypes = [P, P, I, I, P, P, P, I, P, P]
     L.mmvq_q4_0.restype = I
+    L.mmvq_q4_0_f32act.argtypes = [P, P, I, I, P, I, P, P]
+    L.mmvq_q4_0_f32act.restype = I
     L.gemv_nvfp4_w4a16.argtypes = [P, P, ctypes.c_float, I, I, P, I, P, P]
     L.gemv_nvfp4_w4a16.restype = I
     L.gemv_fp8_w8a16.argtypes = [P, P, I, I, P, I, P, P]
@@ -147,6 +149,25 @@ def mmvq_q4_0(w_qs, w_d, a_qs, a_d, a_s, y=None, stream=None):
     _req(y, "y", (torch.float32,), (M, N))
     _check("mmvq_q4_0", lib().mmvq_q4_0(_ptr(w_qs), _ptr(w_d), N, K, _ptr(a_qs), _ptr(a_d),
                                          _ptr(a_s), M, _ptr(y), _stream(stream)))
+    return y
+
+
+def mmvq_q4_0_f32act(w_qs, w_d, x, y=None, stream=None):
+    """Q4_0 weights [N][K/2] + [N][K/32], float32 activations x [M][K] (M <= 2)
+    quantized to Q8_1 inside the same launch -> y float32 [M][N]."""
+    torch = _torch()
+    _req(w_qs, "w_qs", (torch.uint8,))
+    N, K2 = w_qs.shape
+    K = 2 * K2
+    _req(w_d, "w_d", _f16_bits_dtypes(), (N, K // 32))
+    _req(x, "x", (torch.float32,))
+    M = x.shape[0]
+    _req(x, "x", (torch.float32,), (M, K))
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=w_qs.device)
+    _req(y, "y", (torch.float32,), (M, N))
+    _check("mmvq_q4_0_f32act", lib().mmvq_q4_0_f32act(_ptr(w_qs), _ptr(w_d), N, K, _ptr(x), M,
+                                                       _ptr(y), _stream(stream)))
     return y
 
 

@@ -66,6 +66,19 @@ int mmvq_q4_0(const uint8_t *w_qs, const uint16_t *w_d, int N, int K, const int8
                                            (hipStream_t)stream));
 }
 
+int mmvq_q4_0_f32act(const uint8_t *w_qs, const uint16_t *w_d, int N, int K, const float *x,
+                     int M, float *y, void *stream) {
+  if (M < 0 || M > SKINNY_MAX_M_F32ACT) return SKINNY_ERR_M;
+  int st = shape_status(N, K, 32);
+  if (st) return st;
+  if (K > SKINNY_MAX_K_F32ACT) return SKINNY_ERR_SHAPE;
+  if (M == 0 || N == 0) return SKINNY_OK;
+  if (!w_qs || !w_d || !x || !y) return SKINNY_ERR_NULL;
+  if (!aligned(w_qs, 16) || !aligned(w_d, 2) || !aligned(x, 16) || !aligned(y, 4))
+    return SKINNY_ERR_ALIGN;
+  return launched(skinny::launch_mmvq_q4_0_f32act(w_qs, w_d, N, K, x, M, y, (hipStream_t)stream));
+}
+
 int gemv_nvfp4_w4a16(const uint8_t *w_codes, const uint8_t *w_scales, float global_scale,
                      int N, int K, const uint16_t *x, int M, uint16_t *y, void *stream) {
   int st = gemv_m_status(M);

@@ -22,6 +22,8 @@
 // 4*M*N output.
 #include "device.h"
 #include "launch.h"
+#include "q8_1.h"
+#include "skinny_gemm.h"
 
 namespace skinny {
 
@@ -145,44 +147,52 @@ __global__ __launch_bounds__(256) void mmvq_q4_0_kernel(
 //   * lane l then owns isum for weight row 16t + l%16, block 2s + g/2 and
 //     activation rows 4(g%2) .. 4(g%2)+3, and applies the float32 block
 //     epilogue acc += d4 * (d8 * isum - 8 * s8).
-// Data movement as for the NVFP4 and FP8 kernels: each wave streams its own
-// T tiles over its own slice of K with no barrier until the final sum, in
-// chunks of S steps.  A chunk -- weight codes and scales, the MP activation
-// code rows and their Q8_1 scales -- is read with 128-bit loads in
-// row-contiguous order into registers one chunk ahead of its use, then
-// written to a wave-private LDS buffer (1 KB blocks, 16-byte columns
-// XOR-swizzled per block so that the operand-layout reads hit distinct
-// banks; activation scales converted once to float pairs (d8, 8 s8)) and
-// read back in the operand layout.  Loads are issued in the order they are
-// consumed, so each wait covers exactly one chunk.  The workgroup's KS waves
-// split K; their partial tiles are summed in LDS.
+// Data movement.  A workgroup is WR x KS waves: WR waves own different
+// tiles (T each) and share one K slice, KS slices split K.  K is walked in
+// chunks of S steps.  Every wave reads its own weight codes and scales, and
+// a 1/WR share of the slice's activation chunk (Q8_1 codes and scales),
+// with 128-bit loads in row-contiguous order into registers, D chunks ahead
+// of their use; registers, not LDS, hold the bytes in flight.  When a
+// chunk's turn comes its weights are written to a wave-private LDS buffer
+// and its activation share to a double-buffered buffer of the slice
+// (activation scales converted once to float pairs (d8, 8 s8)); one barrier
+// later every wave reads both back in the operand layout.  LDS blocks are
+// 1 KB as written by one store instruction, their 16-byte columns
+// XOR-swizzled so the operand-layout reads hit distinct banks.  Loads are
+// issued in the order they are consumed, so each wait covers one chunk.
+// The KS partial tiles are summed in LDS.
 namespace q4 {
-template <int T, int S, int MP>
+template <int T, int WR, int KS, int S, int MP>
 struct Cfg {
+  static constexpr int kWaves = WR * KS;
   static constexpr int kRows = 16 * T;              // weight rows per wave
   static constexpr int kCB = 32 * S;                // code bytes per row per chunk
   static constexpr int kRpi = 1024 / kCB;           // code rows per 1 KB block
   static constexpr int kSwz = S / 2 - 1;            // code column swizzle mask
   static constexpr int kCi = kRows / kRpi;          // code loads per chunk
   static constexpr int kWsB = kRows * 4 * S;        // weight-scale bytes per chunk
+  static constexpr int kWst = kCi * 1024 + kWsB;    // wave weight buffer
   static constexpr int kRpa = 16 / S;               // activation rows per 1 KB block
   static constexpr int kAi = MP / kRpa;             // activation code loads per chunk
+  static constexpr int kAp = kAi + 1;               // ... plus one scale load
+  static constexpr int kApw = (kAp + WR - 1) / WR;  // activation loads per wave
   static constexpr int kNd = S * MP / 4;            // lanes loading d8 (and as many s8)
-  static constexpr int kWsOff = kCi * 1024;
-  static constexpr int kActOff = kWsOff + kWsB;
-  static constexpr int kAsOff = kActOff + kAi * 1024;       // float (d8, 8 s8)[2S][8]
-  static constexpr int kZeroOff = kAsOff + 2 * S * 8 * 8;   // 1 KB of zeros
-  static constexpr int kSt = kZeroOff + 1024;               // LDS bytes per wave
+  static constexpr int kAsOff = kAi * 1024;         // float (d8, 8 s8)[2S][8]
+  static constexpr int kAst = kAsOff + 2 * S * 8 * 8;   // activation buffer
+  static constexpr int kActBase = kWaves * kWst;
+  static constexpr int kZeroOff = kActBase + KS * 2 * kAst;  // 1 KB of zeros
+  static constexpr int kLds = kZeroOff + 1024;
   static_assert(S == 4 || S == 8, "chunk steps");
   static_assert(MP == 4 || MP == 8, "padded activation rows");
   static_assert(kWsB <= 1024 && 2 * kNd <= 64, "one load per chunk for each kind of scale");
+  static_assert(kWaves * T * kWave * 16 <= kActBase, "reduction buffer");
+  static_assert(kLds <= 160 * 1024, "LDS per workgroup");
 };
-template <int T, int S>
+template <int T, int S, int APW>
 struct Chunk {
   uint4_t c[T * S / 2];
   uint4_t ws;
-  uint4_t a[4];
-  uint4_t as;
+  uint4_t a[APW];
 };
 }  // namespace q4
 
@@ -204,27 +214,30 @@ __device__ __forceinline__ void q4_mfma_step(const uint2_t &wq, const int4_t &ao
 
 // (No __restrict__ on the inputs: the issue fence below must be able to
 // order their loads.)
-template <int T, int KS, int S, int MP>
-__global__ __launch_bounds__(64 * KS) void mmvq_q4_0_mfma_kernel(
+template <int T, int WR, int KS, int S, int MP, int D>
+__global__ __launch_bounds__(64 * WR * KS) void mmvq_q4_0_mfma_kernel(
     const uint8_t *w_qs, const uint16_t *w_d, int N, int K, const int8_t *a_qs,
     const uint16_t *a_d, const uint16_t *a_s, int M, float *y) {
-  using C = q4::Cfg<T, S, MP>;
-  using R = q4::Chunk<T, S>;
+  using C = q4::Cfg<T, WR, KS, S, MP>;
+  using R = q4::Chunk<T, S, C::kApw>;
+  static_assert(D == 1 || D == 2, "chunks in flight");
   extern __shared__ uint4_t smem4[];
   uint8_t *smem = reinterpret_cast<uint8_t *>(smem4);
   const int lane = threadIdx.x & 63;
-  const int ks = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int wr = wave % WR, ks = wave / WR;
   const int j = lane & 15, grp = lane >> 4;
   const int hb = grp >> 1, bh = grp & 1;
-  const int n0 = blockIdx.x * C::kRows;
+  const int n0 = blockIdx.x * (C::kRows * WR) + C::kRows * wr;
   const int nb = K >> 5;
-  uint8_t *ws = smem + ks * C::kSt;
+  uint8_t *wbuf = smem + wave * C::kWst;
+  uint8_t *abuf = smem + C::kActBase + ks * 2 * C::kAst;
 
   const int nct = K / (64 * S);
   const int cps = (nct + KS - 1) / KS;
   const int cb = ks * cps, ce = min(nct, cb + cps);
 
-  // per-lane sources (chunk 0)
+  // weight sources (chunk 0)
   const uint8_t *csrc[C::kCi];
 #pragma unroll
   for (int q = 0; q < C::kCi; ++q) {
@@ -236,44 +249,53 @@ __global__ __launch_bounds__(64 * KS) void mmvq_q4_0_mfma_kernel(
   const int wl = lane % (C::kWsB / 16);     // lanes past the scale bytes repeat one
   const uint8_t *wssrc = reinterpret_cast<const uint8_t *>(
       w_d + (size_t)min(n0 + wl % C::kRows, N - 1) * nb) + 16 * (wl / C::kRows);
-  const int8_t *asrc[C::kAi];
-#pragma unroll
-  for (int a = 0; a < C::kAi; ++a) {
-    const int r = min(a * C::kRpa + (lane % C::kRpa), M - 1);
-    const int col = (lane / C::kRpa) ^ a;
-    asrc[a] = a_qs + (size_t)r * K + 16 * col;
-  }
-  // activation scales: lanes [0, kNd) take d8, [kNd, 2 kNd) s8, as 16-byte
-  // pieces (8 blocks) of row m; the other lanes repeat lane 0
+  // activation pieces of this wave: p = wr, wr + WR, ... (the last repeated);
+  // pieces 0 .. kAi-1 are code blocks, piece kAi the scales (lanes [0, kNd)
+  // d8, [kNd, 2 kNd) s8, 16-byte pieces of 8 blocks of row am)
   const int al = lane < 2 * C::kNd ? lane : 0;
   const bool asd = al < C::kNd;
   const int apc = (al % C::kNd) % (S / 4), am = (al % C::kNd) / (S / 4);
-  const uint16_t *assrc = (asd ? a_d : a_s) + (size_t)min(am, M - 1) * nb + 8 * apc;
+  const uint8_t *asrc[C::kApw];
+  int apiece[C::kApw];
+#pragma unroll
+  for (int u = 0; u < C::kApw; ++u) {
+    const int p = min(wr + WR * u, C::kAp - 1);
+    apiece[u] = p;
+    if (p < C::kAi) {
+      const int r = min(p * C::kRpa + (lane % C::kRpa), M - 1);
+      const int col = (lane / C::kRpa) ^ p;
+      asrc[u] = reinterpret_cast<const uint8_t *>(a_qs + (size_t)r * K + 16 * col);
+    } else {
+      asrc[u] = reinterpret_cast<const uint8_t *>((asd ? a_d : a_s) + (size_t)min(am, M - 1) * nb +
+                                                  8 * apc);
+    }
+  }
 
   auto load = [&](int c, R &rg) {
 #pragma unroll
     for (int q = 0; q < C::kCi; ++q) rg.c[q] = load16_nt(csrc[q] + (size_t)c * C::kCB);
     rg.ws = load16_nt(wssrc + (size_t)c * (4 * S));
 #pragma unroll
-    for (int a = 0; a < C::kAi; ++a) rg.a[a] = load16(asrc[a] + (size_t)c * (64 * S));
-    rg.as = load16(assrc + (size_t)c * (2 * S));
+    for (int u = 0; u < C::kApw; ++u)
+      rg.a[u] = load16(asrc[u] + (size_t)c * (apiece[u] < C::kAi ? 64 * S : 4 * S));
     issue_fence();   // keep each chunk's loads together and ahead of later work
   };
-  auto store = [&](const R &rg) {
+  auto store = [&](const R &rg, uint8_t *ab) {
 #pragma unroll
-    for (int q = 0; q < C::kCi; ++q) *reinterpret_cast<uint4_t *>(ws + 1024 * q + 16 * lane) = rg.c[q];
-    if (wsact) *reinterpret_cast<uint4_t *>(ws + C::kWsOff + 16 * lane) = rg.ws;
+    for (int q = 0; q < C::kCi; ++q) *reinterpret_cast<uint4_t *>(wbuf + 1024 * q + 16 * lane) = rg.c[q];
+    if (wsact) *reinterpret_cast<uint4_t *>(wbuf + C::kCi * 1024 + 16 * lane) = rg.ws;
 #pragma unroll
-    for (int a = 0; a < C::kAi; ++a)
-      *reinterpret_cast<uint4_t *>(ws + C::kActOff + 1024 * a + 16 * lane) = rg.a[a];
-    if (lane < 2 * C::kNd) {
-      // 8 blocks of row am: float d8 at slot 0, 8 * s8 at slot 1
-      float *as = reinterpret_cast<float *>(ws + C::kAsOff) + 2 * am + (asd ? 0 : 1);
+    for (int u = 0; u < C::kApw; ++u) {
+      if (apiece[u] < C::kAi) {
+        *reinterpret_cast<uint4_t *>(ab + 1024 * apiece[u] + 16 * lane) = rg.a[u];
+      } else if (lane < 2 * C::kNd) {
+        // 8 blocks of row am: float d8 at slot 0, 8 * s8 at slot 1
+        float *as = reinterpret_cast<float *>(ab + C::kAsOff) + 2 * am + (asd ? 0 : 1);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint16_t h = (uint16_t)(rg.as[e >> 1] >> (16 * (e & 1)));
-        const float v = f16_bits_to_f32(h);
-        as[16 * (8 * apc + e)] = asd ? v : 8.0f * v;
+        for (int e = 0; e < 8; ++e) {
+          const float v = f16_bits_to_f32((uint16_t)(rg.a[u][e >> 1] >> (16 * (e & 1))));
+          as[16 * (8 * apc + e)] = asd ? v : 8.0f * v;
+        }
       }
     }
   };
@@ -286,42 +308,61 @@ __global__ __launch_bounds__(64 * KS) void mmvq_q4_0_mfma_kernel(
   // both 8-byte pieces advance by a fixed stride per step
   const int m = j & (MP - 1) & 7, ablk = m / C::kRpa;
   const bool live = (j >> 3) == hb;
-  const int abase = C::kActOff + 1024 * ablk + 8 * bh + 16 * (m % C::kRpa);
-  const int alo = live ? abase + 16 * C::kRpa * ((2 * hb) ^ ablk) : C::kZeroOff;
-  const int ahi = live ? abase + 16 * C::kRpa * ((2 * hb + 1) ^ ablk) : C::kZeroOff + 8;
+  const int abase = 1024 * ablk + 8 * bh + 16 * (m % C::kRpa);
+  const int alo = abase + 16 * C::kRpa * ((2 * hb) ^ ablk);
+  const int ahi = abase + 16 * C::kRpa * ((2 * hb + 1) ^ ablk);
+  const uint8_t *zero = smem + C::kZeroOff;
   constexpr int kAStride = 64 * C::kRpa;                   // bytes per step (4 columns)
-  auto consume = [&]() {
+  auto consume = [&](const uint8_t *ab) {
 #pragma unroll
     for (int st = 0; st < S; ++st) {
       const int bl = 2 * st + hb;                          // this lane's block in the chunk
-      const uint2_t lo = *reinterpret_cast<const uint2_t *>(ws + alo + (live ? kAStride * st : 0));
-      const uint2_t hi = *reinterpret_cast<const uint2_t *>(ws + ahi + (live ? kAStride * st : 0));
+      const uint8_t *plo = live ? ab + alo + kAStride * st : zero;
+      const uint8_t *phi = live ? ab + ahi + kAStride * st : zero + 8;
+      const uint2_t lo = *reinterpret_cast<const uint2_t *>(plo);
+      const uint2_t hi = *reinterpret_cast<const uint2_t *>(phi);
       const int4_t aop = {(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
-      const float4_t *asf = reinterpret_cast<const float4_t *>(ws + C::kAsOff + 64 * bl + 32 * bh);
+      const float4_t *asf = reinterpret_cast<const float4_t *>(ab + C::kAsOff + 64 * bl + 32 * bh);
       const float4_t sa = asf[0], sb = asf[1];
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         const int r = 16 * t + j, q = r / C::kRpi;
         const int col = (2 * st + hb) ^ (q & C::kSwz);
         const uint2_t wq = *reinterpret_cast<const uint2_t *>(
-            ws + 1024 * q + 16 * (C::kRpi * col + r % C::kRpi) + 8 * bh);
+            wbuf + 1024 * q + 16 * (C::kRpi * col + r % C::kRpi) + 8 * bh);
         const float d4 = f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(
-            ws + C::kWsOff + 16 * ((bl >> 3) * C::kRows + r) + 2 * (bl & 7)));
+            wbuf + C::kCi * 1024 + 16 * ((bl >> 3) * C::kRows + r) + 2 * (bl & 7)));
         q4_mfma_step(wq, aop, d4, sa, sb, acc[t]);
       }
     }
   };
 
-  if (cb < ce) {
-    *reinterpret_cast<uint4_t *>(ws + C::kZeroOff + 16 * lane) = uint4_t{0u, 0u, 0u, 0u};
-    // The load past the slice re-reads its last chunk into registers that
-    // are never stored, so every path issues the same loads.
-    R r0;
-    load(cb, r0);
-    for (int c = cb; c < ce; ++c) {
-      store(r0);
-      load(min(c + 1, ce - 1), r0);
-      consume();
+  // Every wave runs cps steps in lockstep (the barrier); steps past its
+  // slice load the slice's last chunk again and compute nothing, so every
+  // path issues the same loads.
+  if (cb < ce || WR * KS > 1) {
+    *reinterpret_cast<uint4_t *>(smem + C::kZeroOff + 16 * lane) = uint4_t{0u, 0u, 0u, 0u};
+    const int cl = max(ce - 1, 0);                       // a valid chunk to re-read
+    auto step = [&](int k, R &rg) {
+      const int c = cb + k;
+      uint8_t *ab = abuf + (k & 1) * C::kAst;
+      store(rg, ab);
+      if constexpr (WR > 1) wg_barrier();
+      load(min(c + D, cl), rg);
+      if (c < ce) consume(ab);
+    };
+    if constexpr (D == 1) {
+      R r0;
+      load(min(cb, cl), r0);
+      for (int k = 0; k < cps; ++k) step(k, r0);
+    } else {
+      R r0, r1;
+      load(min(cb, cl), r0);
+      load(min(cb + 1, cl), r1);
+      for (int k = 0; k < cps; k += 2) {
+        step(k, r0);
+        step(k + 1, r1);
+      }
     }
   }
 
@@ -329,13 +370,13 @@ __global__ __launch_bounds__(64 * KS) void mmvq_q4_0_mfma_kernel(
     wg_barrier();
     float4_t *red = reinterpret_cast<float4_t *>(smem);
 #pragma unroll
-    for (int t = 0; t < T; ++t) red[(ks * T + t) * kWave + lane] = acc[t];
+    for (int t = 0; t < T; ++t) red[(wave * T + t) * kWave + lane] = acc[t];
     wg_barrier();
     if (ks == 0) {
 #pragma unroll
       for (int t = 0; t < T; ++t)
 #pragma unroll
-        for (int v = 1; v < KS; ++v) acc[t] += red[(v * T + t) * kWave + lane];
+        for (int v = 1; v < KS; ++v) acc[t] += red[((v * WR + wr) * T + t) * kWave + lane];
     }
   }
   // lanes l and l ^ 32 hold the two blocks of each step: add them
@@ -357,44 +398,49 @@ __global__ __launch_bounds__(64 * KS) void mmvq_q4_0_mfma_kernel(
   }
 }
 
-template <int T, int KS, int S, int MP>
+template <int T, int WR, int KS, int S, int MP, int D>
 static hipError_t launch_mfma_cfg(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                                   const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
                                   int M, float *y, hipStream_t stream) {
-  using C = q4::Cfg<T, S, MP>;
-  constexpr int kLds = KS * C::kSt;
-  static_assert(T * kWave * 16 <= C::kSt, "reduction buffer");
-  static_assert(kLds <= 160 * 1024, "LDS per workgroup");
+  using C = q4::Cfg<T, WR, KS, S, MP>;
   if (K % (64 * S) != 0) return hipErrorInvalidValue;   // chunks must tile K
-  static const hipError_t lds_ok = allow_lds((const void *)mmvq_q4_0_mfma_kernel<T, KS, S, MP>, kLds);
+  static const hipError_t lds_ok =
+      allow_lds((const void *)mmvq_q4_0_mfma_kernel<T, WR, KS, S, MP, D>, C::kLds);
   if (lds_ok != hipSuccess) return lds_ok;
-  const int blocks = (N + C::kRows - 1) / C::kRows;
-  hipLaunchKernelGGL((mmvq_q4_0_mfma_kernel<T, KS, S, MP>), dim3(blocks), dim3(64 * KS), kLds,
-                     stream, w_qs, w_d, N, K, a_qs, a_d, a_s, M, y);
+  const int rows = C::kRows * WR;
+  const int blocks = (N + rows - 1) / rows;
+  hipLaunchKernelGGL((mmvq_q4_0_mfma_kernel<T, WR, KS, S, MP, D>), dim3(blocks),
+                     dim3(64 * C::kWaves), C::kLds, stream, w_qs, w_d, N, K, a_qs, a_d, a_s,
+                     M, y);
   return hipGetLastError();
 }
 
-// One tile per wave throughout; the K split grows as the tile count falls
-// so that enough waves stream (measured on MI355X at M = 3..8 over the
-// Llama-2-7B shapes: 1376..2000 tiles no split, 768 tiles two, 256 tiles
-// eight).
+// One tile per wave throughout.  Wide matrices share each activation chunk
+// between two (>= 1024 tiles) or four (>= 1800 tiles) waves; narrower ones
+// split K instead so that enough waves stream (measured on MI355X at M = 4
+// and 8 over the Llama-2-7B shapes: 2000 tiles four-way sharing, 1376 tiles
+// two-way, 768 tiles a two-way K split, 256 tiles an eight-way split).
 template <int MP>
 static hipError_t launch_mfma_mp(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                                  const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
                                  int M, float *y, hipStream_t stream) {
   const int tiles = (N + 15) / 16;
   const bool s8 = K % 512 == 0;
-#define SKINNY_Q4(T, KS, S) \
-  return launch_mfma_cfg<T, KS, S, MP>(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream)
+#define SKINNY_Q4(T, WR, KS, S) \
+  return launch_mfma_cfg<T, WR, KS, S, MP, 1>(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream)
+  if (tiles >= 1800) {
+    if (s8) SKINNY_Q4(1, 4, 1, 8);
+    SKINNY_Q4(1, 4, 1, 4);
+  }
   if (tiles >= 1024) {
-    if (s8) SKINNY_Q4(1, 1, 8);
-    SKINNY_Q4(1, 1, 4);
+    if (s8) SKINNY_Q4(1, 2, 1, 8);
+    SKINNY_Q4(1, 2, 1, 4);
   }
   if (tiles >= 512) {
-    if (s8) SKINNY_Q4(1, 2, 8);
-    SKINNY_Q4(1, 2, 4);
+    if (s8) SKINNY_Q4(1, 1, 2, 8);
+    SKINNY_Q4(1, 1, 2, 4);
   }
-  SKINNY_Q4(1, 8, 4);
+  SKINNY_Q4(1, 1, 8, 4);
 #undef SKINNY_Q4
 }
 
@@ -403,6 +449,208 @@ static hipError_t launch_mfma(const uint8_t *w_qs, const uint16_t *w_d, int N, i
                               int M, float *y, hipStream_t stream) {
   if (M <= 4) return launch_mfma_mp<4>(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream);
   return launch_mfma_mp<8>(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream);
+}
+
+// Vector kernel with the activation rows staged in LDS (M <= 2, one round of
+// U blocks per lane, K <= 2048 U).  A workgroup of W waves (two weight rows
+// each) reads the Q8_1 activation rows once -- or, FUSED, reads the float32
+// rows and quantizes them into LDS itself with the same block arithmetic as
+// quantize_act_q8_1 -- so activation bytes per weight byte drop W-fold
+// (each wave of the plain kernel re-reads the whole row from L2, as many
+// bytes as its weights).  Activation loads are issued first, then the
+// wave's whole round of weight loads; the activations are stored (or
+// quantized) while the weights are in flight, one barrier, then the dot.
+// LDS: codes int8 [M][K] | d8 float [M][K/32] | 8 s8 float [M][K/32].
+// The dot is exactly the plain kernel's (same blocks per lane, same order,
+// same reduction), so the result equals mmvq_q4_0 on the same Q8_1 input.
+template <int M, int U, bool FUSED>
+struct LdsAct {
+  static constexpr int kW = 8;                                     // waves per workgroup
+  static constexpr int kMaxNb = kWave * U;                         // blocks per row (max)
+  // activation 16-byte loads per lane: plain = codes + d + s pieces;
+  // fused = two per 8-element group
+  static constexpr int kPieces = FUSED ? (M * kMaxNb * 4) : (M * kMaxNb * 2 + M * kMaxNb / 4);
+  static constexpr int kA = (kPieces + kW * kWave - 1) / (kW * kWave);
+};
+
+// (No __restrict__ on the inputs: the issue fence below must be able to
+// keep the activation loads ahead of the weight loads.)
+template <int M, int U, bool FUSED>
+__global__ __launch_bounds__(512) void mmvq_q4_0_lds_kernel(
+    const uint8_t *w_qs, const uint16_t *w_d, int N, int K, const int8_t *a_qs,
+    const uint16_t *a_d, const uint16_t *a_s, const float *x, float *y) {
+  using P = LdsAct<M, U, FUSED>;
+  static_assert(P::kW * kWave == 512, "launch bounds");
+  constexpr int R = 2;
+  extern __shared__ uint4_t smem4[];
+  int8_t *lq = reinterpret_cast<int8_t *>(smem4);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nb = K >> 5;
+  float *ld8 = reinterpret_cast<float *>(lq + M * K);
+  float *ls8 = ld8 + M * nb;
+  const int n0 = (blockIdx.x * P::kW + wave) * R;
+
+  // 1. activation loads (flat pieces over the workgroup, the last repeated)
+  uint4_t av[P::kA][FUSED ? 2 : 1];
+  int apiece[P::kA];
+  const int npieces = FUSED ? M * K / 8 : M * K / 16 + M * nb / 4;
+#pragma unroll
+  for (int a = 0; a < P::kA; ++a) {
+    const int p = min(tid + a * P::kW * kWave, npieces - 1);
+    apiece[a] = tid + a * P::kW * kWave;
+    if constexpr (FUSED) {
+      const float4_t *src = reinterpret_cast<const float4_t *>(x + (size_t)p * 8);
+      av[a][0] = __builtin_bit_cast(uint4_t, src[0]);
+      av[a][1] = __builtin_bit_cast(uint4_t, src[1]);
+    } else {
+      const int ncode = M * K / 16, nd = M * nb / 8;
+      const uint8_t *src =
+          p < ncode ? reinterpret_cast<const uint8_t *>(a_qs) + 16 * p
+          : p < ncode + nd ? reinterpret_cast<const uint8_t *>(a_d) + 16 * (p - ncode)
+                           : reinterpret_cast<const uint8_t *>(a_s) + 16 * (p - ncode - nd);
+      av[a][0] = load16(src);
+    }
+  }
+  issue_fence();
+
+  // 2. this wave's round of weight loads
+  const int nw = min(n0, N - 1);            // waves past N load row N - 1 and store nothing
+  const uint8_t *wrow[R];
+  const uint16_t *drow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int n = min(nw + r, N - 1);
+    wrow[r] = w_qs + (size_t)n * (size_t)(K >> 1);
+    drow[r] = w_d + (size_t)n * (size_t)nb;
+  }
+  uint4_t wq[U][R];
+  uint16_t d4h[U][R];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int b = min(lane + u * kWave, nb - 1);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      wq[u][r] = load16_nt(wrow[r] + 16 * b);
+      d4h[u][r] = load_u16_nt(drow[r] + b);
+    }
+  }
+  issue_fence();
+
+  // 3. activations into LDS (waits only for the activation loads)
+#pragma unroll
+  for (int a = 0; a < P::kA; ++a) {
+    const int p = apiece[a];
+    if constexpr (FUSED) {
+      // groups of a quad form one block; a quad is all in or all out
+      uint32_t lo, hi;
+      uint16_t db, sb;
+      quantize_q8_1_group(__builtin_bit_cast(float4_t, av[a][0]),
+                          __builtin_bit_cast(float4_t, av[a][1]), lo, hi, db, sb);
+      if (p < npieces) {
+        *reinterpret_cast<uint2_t *>(lq + 8 * p) = uint2_t{lo, hi};
+        if ((p & 3) == 0) {
+          const int blk = p >> 2;                     // flat block index m * nb + b
+          ld8[blk] = f16_bits_to_f32(db);
+          ls8[blk] = 8.0f * f16_bits_to_f32(sb);
+        }
+      }
+    } else if (p < npieces) {
+      const int ncode = M * K / 16, nd = M * nb / 8;
+      if (p < ncode) {
+        *reinterpret_cast<uint4_t *>(lq + 16 * p) = av[a][0];
+      } else {
+        const bool isd = p < ncode + nd;
+        float *dst = isd ? ld8 + 8 * (p - ncode) : ls8 + 8 * (p - ncode - nd);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = f16_bits_to_f32((uint16_t)(av[a][0][e >> 1] >> (16 * (e & 1))));
+          dst[e] = isd ? v : 8.0f * v;
+        }
+      }
+    }
+  }
+  wg_barrier();
+
+  // 4. the dot, exactly as in mmvq_q4_0_kernel
+  float acc[R][M];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int b = min(lane + u * kWave, nb - 1);
+    const bool live = lane + u * kWave < nb;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      uint32_t lo[4], hi[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo[i] = wq[u][r][i] & 0x0F0F0F0Fu;
+        hi[i] = (wq[u][r][i] >> 4) & 0x0F0F0F0Fu;
+      }
+      const float d4 = f16_bits_to_f32(d4h[u][r]);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const uint4_t aq0 = *reinterpret_cast<const uint4_t *>(lq + (size_t)m * K + 32 * b);
+        const uint4_t aq1 = *reinterpret_cast<const uint4_t *>(lq + (size_t)m * K + 32 * b + 16);
+        int32_t isum = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          isum = dot4_i8(lo[i], aq0[i], isum);
+          isum = dot4_i8(hi[i], aq1[i], isum);
+        }
+        const float t = fmaf(ld8[m * nb + b], (float)isum, -ls8[m * nb + b]);
+        const float a = fmaf(d4, t, acc[r][m]);
+        acc[r][m] = live ? a : acc[r][m];
+      }
+    }
+  }
+
+  constexpr int V = next_pow2(R * M);
+  float v[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) v[i] = (i < R * M) ? acc[i / M][i % M] : 0.0f;
+  const float total = wave_reduce_transpose<V>(v, lane);
+  constexpr int SHIFT = 6 - Log2<V>::value;
+  const int idx = lane >> SHIFT;
+  if ((lane & ((1 << SHIFT) - 1)) == 0 && idx < R * M) {
+    const int r = idx / M, m = idx % M;
+    const int n = n0 + r;
+    if (n < N) y[(size_t)m * N + n] = total;
+  }
+}
+
+template <int M, int U, bool FUSED>
+static hipError_t launch_lds_u(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
+                               const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
+                               const float *x, float *y, hipStream_t stream) {
+  using P = LdsAct<M, U, FUSED>;
+  const int rows = 2 * P::kW;
+  const int blocks = (N + rows - 1) / rows;
+  const size_t lds = (size_t)M * K + 8 * (size_t)M * (K >> 5);
+  hipLaunchKernelGGL((mmvq_q4_0_lds_kernel<M, U, FUSED>), dim3(blocks), dim3(64 * P::kW), lds,
+                     stream, w_qs, w_d, N, K, a_qs, a_d, a_s, x, y);
+  return hipGetLastError();
+}
+
+// K limit of the LDS-staged kernel: one round of at most 6 blocks per lane
+// (SKINNY_MAX_K_F32ACT).
+constexpr int kLdsMaxK = 2048 * 6;
+static_assert(kLdsMaxK == SKINNY_MAX_K_F32ACT, "documented limit");
+
+template <int M, bool FUSED>
+static hipError_t launch_lds(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
+                             const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
+                             const float *x, float *y, hipStream_t stream) {
+  const int per_lane = ((K >> 5) + kWave - 1) / kWave;
+#define SKINNY_LDS(U) return launch_lds_u<M, U, FUSED>(w_qs, w_d, N, K, a_qs, a_d, a_s, x, y, stream)
+  if (per_lane <= 2) SKINNY_LDS(2);
+  if (per_lane <= 3) SKINNY_LDS(3);
+  if (per_lane <= 4) SKINNY_LDS(4);
+  SKINNY_LDS(6);
+#undef SKINNY_LDS
 }
 
 template <int M, int R, int U>
@@ -455,6 +703,12 @@ hipError_t launch_mmvq_q4_0(const uint8_t *w_qs, const uint16_t *w_d, int N, int
     case 7: return launch_m<7>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
     default: return launch_m<8>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
   }
+}
+
+hipError_t launch_mmvq_q4_0_f32act(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
+                                   const float *x, int M, float *y, hipStream_t stream) {
+  if (M == 1) return launch_lds<1, true>(w_qs, w_d, N, K, nullptr, nullptr, nullptr, x, y, stream);
+  return launch_lds<2, true>(w_qs, w_d, N, K, nullptr, nullptr, nullptr, x, y, stream);
 }
 
 }  // namespace skinny

@@ -32,7 +32,8 @@ def L():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["skinny_status_string", "quantize_act_q8_1",
-                                           "mmvq_q4_0", "gemv_nvfp4_w4a16", "gemv_fp8_w8a16"])
+                                           "mmvq_q4_0", "mmvq_q4_0_f32act", "gemv_nvfp4_w4a16",
+                                           "gemv_fp8_w8a16"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -163,3 +164,17 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError, match="not built"):
         _lib.lib()
+
+
+def test_f32act_validation(L):
+    f = L.mmvq_q4_0_f32act
+    f.restype = ctypes.c_int
+    ok = dict(w=V(A), d=V(A), x=V(A), y=V(A))
+    def call(N=64, K=256, M=1, **kw):
+        a = dict(ok, **kw)
+        return f(a["w"], a["d"], N, K, a["x"], M, a["y"], None)
+    assert call(M=3) == -4 and call(M=-1) == -4          # decode widths only
+    assert call(K=12288 + 32) == -2 and call(K=48) == -2 and call(K=0) == -2
+    assert call(M=0) == 0 and call(N=0) == 0              # nothing to do
+    assert call(x=None) == -1 and call(w=None) == -1
+    assert call(x=V(A + 4)) == -3 and call(w=V(A + 8)) == -3 and call(y=V(A + 2)) == -3

@@ -162,7 +162,9 @@ def run_q4(w_qs, w_d, a_qs, a_d, a_s):
                                  # matrix-core paths: wide / mid / narrow, chunks of 4
                                  # and 8 steps, ragged tiles, unequal K slices and
                                  # one empty slice
-                                 (25000, 768), (9000, 1280), (40, 768), (700, 8192)])
+                                 (25000, 768), (9000, 1280), (40, 768), (700, 8192),
+                                 # four waves sharing one activation chunk, ragged
+                                 (30000, 1024)])
 def test_mmvq_q4_0_vs_oracle(M, N, K):
     w_qs, w_d = inputs.q4_0_weights(N, K, 7 * N + K)
     x = inputs.normal_f32(M, K, 3 * M + K)
@@ -206,6 +208,53 @@ def test_q4_0_pipeline_device_quantize():
     a_qs, a_d, a_s = oracle.quantize_q8_1(x)
     ref = oracle.mmvq_q4_0(w_qs, w_d, a_qs, a_d, a_s)
     check_f32(y, ref, q4_mag(w_qs, w_d, a_qs, a_d, a_s), K, "q4_0 pipeline")
+
+
+def run_q4_f32act(w_qs, w_d, x):
+    import skinny_gemm_amd as sk
+
+    return host(sk.mmvq_q4_0_f32act(dev(w_qs), dev(w_d), dev(x)))
+
+
+@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("N,K", [(1, 32), (4096 + 37, 256), (4099, 1376), (257, 11008),
+                                 (25000, 768), (40, 12288), (3000, 4096)])
+def test_mmvq_q4_0_f32act_equals_two_calls_and_oracle(M, N, K):
+    # one launch that quantizes in LDS: bit-identical to quantize_act_q8_1 +
+    # mmvq_q4_0 (the same block arithmetic and dot), and within the float
+    # tolerance of the oracle chain
+    import skinny_gemm_amd as sk
+
+    w_qs, w_d = inputs.q4_0_weights(N, K, 17 * N + K)
+    x = inputs.normal_f32(M, K, 5 * M + K)
+    y = run_q4_f32act(w_qs, w_d, x)
+    qs, d, s = sk.quantize_act_q8_1(dev(x))
+    y2 = host(sk.mmvq_q4_0(dev(w_qs), dev(w_d), qs, d, s))
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+    a_qs, a_d, a_s = oracle.quantize_q8_1(x)
+    ref = oracle.mmvq_q4_0(w_qs, w_d, a_qs, a_d, a_s)
+    check_f32(y, ref, q4_mag(w_qs, w_d, a_qs, a_d, a_s), K, "q4_0 f32act M=%d N=%d K=%d" % (M, N, K))
+
+
+def test_mmvq_q4_0_f32act_adversarial_blocks():
+    # integer blocks with unit scale, halves that round away from zero,
+    # all-zero blocks: exact integer results, equal to the two-call path
+    import skinny_gemm_amd as sk
+
+    M, N, K = 2, 1031, 4096
+    x = inputs.q8_1_unit_scale_source(M, K, 71)
+    x[0, 64:96] = 0.0                                   # an all-zero block
+    x[1, 128:160] = np.where(np.arange(32) % 2 == 0, 2.5, -2.5)   # ties
+    x[1, 128] = 127.0
+    w_qs, _ = inputs.q4_0_weights(N, K, 72)
+    w_d = np.full((N, K // 32), 0x3C00, np.uint16)
+    y = run_q4_f32act(w_qs, w_d, x)
+    qs, d, s = sk.quantize_act_q8_1(dev(x))
+    y2 = host(sk.mmvq_q4_0(dev(w_qs), dev(w_d), qs, d, s))
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+    a_qs, a_d, a_s = oracle.quantize_q8_1(x)
+    exact = oracle.mmvq_q4_0(w_qs, w_d, a_qs, a_d, a_s)
+    assert np.array_equal(y.astype(np.float64), exact)
 
 
 # ------------------------------------------------------------------ NVFP4
@@ -335,6 +384,19 @@ def test_q4_0_full_sizes_sampled(M):
         ref = oracle.mmvq_q4_0(w_qs[rows], w_d[rows], a_qs, a_d, a_s)
         mag = q4_mag(w_qs[rows], w_d[rows], a_qs, a_d, a_s)
         check_f32(y[:, rows], ref, mag, K, "q4_0 full M=%d %dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_q4_0_f32act_full_sizes_sampled(M):
+    for si, (N, K) in enumerate(LLAMA_Q4):
+        w_qs, w_d = inputs.q4_0_weights(N, K, inputs.seed(1, si, 0))
+        x = inputs.normal_f32(M, K, inputs.seed(2, si, 2) + M)
+        y = run_q4_f32act(w_qs, w_d, x)
+        rows = sample_rows(N, seed=si)
+        a_qs, a_d, a_s = oracle.quantize_q8_1(x)
+        ref = oracle.mmvq_q4_0(w_qs[rows], w_d[rows], a_qs, a_d, a_s)
+        mag = q4_mag(w_qs[rows], w_d[rows], a_qs, a_d, a_s)
+        check_f32(y[:, rows], ref, mag, K, "q4_0 f32act full M=%d %dx%d" % (M, N, K))
 
 
 @pytest.mark.parametrize("M", [1, 4, 8])
