@@ -1,7 +1,8 @@
 /*
  * skinny_gemm.h -- C ABI of libskinny_gemm.so: block-quantized matrix x
- * vector and skinny GEMM (M = 1..8 activation rows) for LLM decode and
- * speculative verification on AMD Instinct MI355X (gfx950).
+ * vector and skinny GEMM (M = 1..8 activation rows for Q4_0, 1..16 for the
+ * binary16-activation formats) for LLM decode and speculative verification
+ * on AMD Instinct MI355X (gfx950).
  *
  * Sources.  "Machine Learning on NVIDIA CMP" (sections "TL;DR", "llama.cpp
  * results", "The DP2A patch") describes decode as a quantized mat x vec
@@ -23,7 +24,8 @@
  *     nothing, keeps no state between calls, and is safe to call from
  *     several host threads.  Outputs must not overlap inputs.
  *   - A call validates its arguments on the host before any HIP call, then
- *     enqueues one kernel on `stream` and returns without synchronizing.
+ *     enqueues its kernel (two, for the split cases stated below) on
+ *     `stream` and returns without synchronizing.
  *     Faults during execution surface at the caller's next synchronization.
  *   - binary16 values are passed as their 16-bit patterns (uint16_t).
  *   - A call with M == 0 or N == 0 has nothing to compute: it returns
@@ -46,13 +48,15 @@ extern "C" {
 #define SKINNY_ERR_SHAPE       -2  /* K or N out of range, or K not a multiple of   */
                                    /* the format's block (see each function)        */
 #define SKINNY_ERR_ALIGN       -3  /* a pointer is not aligned as required          */
-#define SKINNY_ERR_M           -4  /* M outside 0..8 (GEMV entry points)            */
+#define SKINNY_ERR_M           -4  /* M outside the entry point's range             */
 #define SKINNY_ERR_LAUNCH      -5  /* the HIP launch reported an error              */
 
 /* Limits: 1 <= K <= SKINNY_MAX_K, 0 <= N <= SKINNY_MAX_N. */
 #define SKINNY_MAX_K  (1 << 20)
 #define SKINNY_MAX_N  (1 << 28)
-#define SKINNY_MAX_M_GEMV   8
+#define SKINNY_MAX_M_GEMV   8    /* mmvq_q4_0 */
+/* gemv_nvfp4_w4a16 and gemv_fp8_w8a16: two 8-row verification tiles. */
+#define SKINNY_MAX_M_F16ACT 16
 #define SKINNY_MAX_M_QUANT  65536
 /* mmvq_q4_0_f32act: decode widths only, one row of K in LDS per workgroup. */
 #define SKINNY_MAX_M_F32ACT 2
@@ -99,7 +103,7 @@ int quantize_act_q8_1(const float *x, int M, int K,
  *
  *   w_qs 16-byte aligned; w_d, a_d, a_s 2-byte aligned; a_qs 16-byte
  *   aligned; y float32 [M][N] row-major, 4-byte aligned.
- *   0 <= M <= 8; K % 32 == 0.
+ *   0 <= M <= SKINNY_MAX_M_GEMV; K % 32 == 0.
  * Block sums are exact integers; the float result matches the definition
  * to float32 summation-order rounding.
  */
@@ -142,7 +146,10 @@ int mmvq_q4_0_f32act(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
  *   y        binary16 [M][N] row-major, 2-byte aligned:
  *            y = binary16( sum_j (sum_{i<16} e2m1 * x) * (e4m3(scale_j) * g) ),
  *            accumulated in float32, rounded to nearest even once.
- *   0 <= M <= 8; K % 32 == 0.
+ *   0 <= M <= SKINNY_MAX_M_F16ACT; K % 32 == 0.  Rows 9..16 serve the wide
+ *   verification band of the same pages ("Native mixed-precision checkpoint
+ *   path", dispatch table): one weight pass for all M rows whenever
+ *   K % 256 == 0; otherwise rows 1..8 and 9..M take one pass each.
  */
 int gemv_nvfp4_w4a16(const uint8_t *w_codes, const uint8_t *w_scales,
                      float global_scale, int N, int K,
@@ -160,8 +167,11 @@ int gemv_nvfp4_w4a16(const uint8_t *w_codes, const uint8_t *w_scales,
  *   y   binary16 [M][N] row-major, 2-byte aligned:
  *       y = binary16( channel_scale[n] * sum_k e4m3(w[n][k]) * x[m][k] ),
  *       accumulated in float32.
- *   0 <= M <= 8; K % 16 == 0.  NaN weight codes (0x7F, 0xFF) give
- *   unspecified results.
+ *   0 <= M <= SKINNY_MAX_M_F16ACT; K % 16 == 0.  Rows 9..16 (the wide
+ *   verification band, "How QPN works" and "Native mixed-precision
+ *   checkpoint path": two 8-row tiles against one weight pass) share one
+ *   weight pass whenever K % 256 == 0; otherwise rows 1..8 and 9..M take one
+ *   pass each.  NaN weight codes (0x7F, 0xFF) give unspecified results.
  */
 int gemv_fp8_w8a16(const uint8_t *w, const float *channel_scale, int N, int K,
                    const uint16_t *x, int M, uint16_t *y, void *stream);

@@ -1,5 +1,5 @@
 // abi.hip -- the exported C entry points: host-side argument validation,
-// then one kernel launch on the caller's stream.  Validation makes no HIP
+// then the kernel launch(es) on the caller's stream.  Validation makes no HIP
 // call, so it runs (and is tested) on machines without a GPU.  An invalid
 // call returns its status code and enqueues nothing; a valid call never
 // switches to another kernel.
@@ -18,8 +18,8 @@ inline int shape_status(int N, int K, int kmult) {
   return SKINNY_OK;
 }
 
-inline int gemv_m_status(int M) {
-  if (M < 0 || M > SKINNY_MAX_M_GEMV) return SKINNY_ERR_M;
+inline int gemv_m_status(int M, int max_m) {
+  if (M < 0 || M > max_m) return SKINNY_ERR_M;
   return SKINNY_OK;
 }
 
@@ -54,7 +54,7 @@ int quantize_act_q8_1(const float *x, int M, int K, int8_t *qs, uint16_t *d, uin
 
 int mmvq_q4_0(const uint8_t *w_qs, const uint16_t *w_d, int N, int K, const int8_t *a_qs,
               const uint16_t *a_d, const uint16_t *a_s, int M, float *y, void *stream) {
-  int st = gemv_m_status(M);
+  int st = gemv_m_status(M, SKINNY_MAX_M_GEMV);
   if (st) return st;
   if ((st = shape_status(N, K, 32))) return st;
   if (M == 0 || N == 0) return SKINNY_OK;
@@ -81,7 +81,7 @@ int mmvq_q4_0_f32act(const uint8_t *w_qs, const uint16_t *w_d, int N, int K, con
 
 int gemv_nvfp4_w4a16(const uint8_t *w_codes, const uint8_t *w_scales, float global_scale,
                      int N, int K, const uint16_t *x, int M, uint16_t *y, void *stream) {
-  int st = gemv_m_status(M);
+  int st = gemv_m_status(M, SKINNY_MAX_M_F16ACT);
   if (st) return st;
   if ((st = shape_status(N, K, 32))) return st;
   if (M == 0 || N == 0) return SKINNY_OK;
@@ -94,7 +94,7 @@ int gemv_nvfp4_w4a16(const uint8_t *w_codes, const uint8_t *w_scales, float glob
 
 int gemv_fp8_w8a16(const uint8_t *w, const float *channel_scale, int N, int K,
                    const uint16_t *x, int M, uint16_t *y, void *stream) {
-  int st = gemv_m_status(M);
+  int st = gemv_m_status(M, SKINNY_MAX_M_F16ACT);
   if (st) return st;
   if ((st = shape_status(N, K, 16))) return st;
   if (M == 0 || N == 0) return SKINNY_OK;

@@ -1,4 +1,4 @@
-// gemv_fp8.hip -- FP8 E4M3 weights x binary16 activations, M = 1..8 rows,
+// gemv_fp8.hip -- FP8 E4M3 weights x binary16 activations, M = 1..16 rows,
 // per-output-channel float32 scale.
 //
 // "v100-skinny README", "How QPN works": the FP8 weights are one contiguous
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void gemv_fp8_kernel(
   }
 }
 
-// Matrix-core variant (3 <= M <= 8, K % 256 == 0).
+// Matrix-core variant (3 <= M <= 16, K % 256 == 0).
 //
 // Tile: 16 weight rows.  Lane l = (i = l % 16, g = l / 16) of a wave feeds
 // row 16t + i of the A operand of four v_mfma_f32_16x16x32_f16 per 128-K
@@ -154,12 +154,12 @@ struct Cfg {
   static constexpr int kActOff = kCi * 1024;
   static constexpr int kSt = kActOff + kAi * 1024;  // LDS bytes per wave
   static_assert(S == 2 || S == 4, "chunk steps");
-  static_assert(MP == 4 || MP == 8, "padded activation rows");
+  static_assert(MP == 4 || MP == 8 || MP == 16, "padded activation rows");
 };
-template <int T, int S>
+template <int T, int S, int AI>
 struct Chunk {
   uint4_t c[2 * T * S];
-  uint4_t a[8];
+  uint4_t a[AI];
 };
 }  // namespace f8
 
@@ -169,7 +169,7 @@ template <int T, int KS, int S, int MP>
 __global__ __launch_bounds__(64 * KS) void gemv_fp8_mfma_kernel(
     const uint8_t *w, const float *cs, int N, int K, const uint16_t *x, int M, uint16_t *y) {
   using C = f8::Cfg<T, S, MP>;
-  using R = f8::Chunk<T, S>;
+  using R = f8::Chunk<T, S, C::kAi>;
   extern __shared__ uint4_t smem4[];
   uint8_t *smem = reinterpret_cast<uint8_t *>(smem4);
   const int lane = threadIdx.x & 63;
@@ -316,10 +316,31 @@ static hipError_t launch_mfma_mp(const uint8_t *w, const float *cs, int N, int K
 #undef SKINNY_F8
 }
 
+// 9 <= M <= 16: sixteen activation rows per chunk, twice the activation
+// bytes per weight byte of M <= 8; measured on MI355X at M = 12 and 16, K
+// 5120..17408, N 5120..34816: wide matrices take four tiles per wave (each
+// activation chunk feeds four tiles), mid-width ones one, narrow ones split
+// K four ways.
+static hipError_t launch_mfma_wide(const uint8_t *w, const float *cs, int N, int K,
+                                   const uint16_t *x, int M, uint16_t *y, hipStream_t stream) {
+  const int tiles = (N + 15) / 16;
+  const bool s4 = K % 512 == 0;
+#define SKINNY_F8(T, KS, S) return launch_mfma_cfg<T, KS, S, 16>(w, cs, N, K, x, M, y, stream)
+  if (tiles >= 1536) SKINNY_F8(4, 1, 2);
+  if (tiles >= 512) {
+    if (s4) SKINNY_F8(1, 1, 4);
+    SKINNY_F8(1, 2, 2);
+  }
+  if (s4 && K >= 8192) SKINNY_F8(2, 4, 4);
+  SKINNY_F8(2, 4, 2);
+#undef SKINNY_F8
+}
+
 static hipError_t launch_mfma(const uint8_t *w, const float *cs, int N, int K, const uint16_t *x,
                               int M, uint16_t *y, hipStream_t stream) {
   if (M <= 4) return launch_mfma_mp<4>(w, cs, N, K, x, M, y, stream);
-  return launch_mfma_mp<8>(w, cs, N, K, x, M, y, stream);
+  if (M <= 8) return launch_mfma_mp<8>(w, cs, N, K, x, M, y, stream);
+  return launch_mfma_wide(w, cs, N, K, x, M, y, stream);
 }
 
 template <int M, int R, int U>
@@ -351,9 +372,9 @@ static hipError_t launch_m(const uint8_t *w, const float *cs, int N, int K, cons
   }
 }
 
-hipError_t launch_gemv_fp8(const uint8_t *w, const float *cs, int N, int K, const uint16_t *x,
-                           int M, uint16_t *y, hipStream_t stream) {
-  if (M >= kFp8MfmaMinM && K % 256 == 0) return launch_mfma(w, cs, N, K, x, M, y, stream);
+// Vector kernel for 1 <= M <= 8 rows.
+static hipError_t launch_vector(const uint8_t *w, const float *cs, int N, int K,
+                                const uint16_t *x, int M, uint16_t *y, hipStream_t stream) {
   switch (M) {
     case 1: return launch_m<1>(w, cs, N, K, x, y, stream);
     case 2: return launch_m<2>(w, cs, N, K, x, y, stream);
@@ -364,6 +385,18 @@ hipError_t launch_gemv_fp8(const uint8_t *w, const float *cs, int N, int K, cons
     case 7: return launch_m<7>(w, cs, N, K, x, y, stream);
     default: return launch_m<8>(w, cs, N, K, x, y, stream);
   }
+}
+
+// The matrix-core kernel takes every M >= 3 in one weight pass when K is a
+// whole number of 256-element chunks.  Otherwise the vector kernel serves
+// up to 8 rows per pass: rows 9..M take a second pass over the weights.
+hipError_t launch_gemv_fp8(const uint8_t *w, const float *cs, int N, int K, const uint16_t *x,
+                           int M, uint16_t *y, hipStream_t stream) {
+  if (M >= kFp8MfmaMinM && K % 256 == 0) return launch_mfma(w, cs, N, K, x, M, y, stream);
+  if (M <= 8) return launch_vector(w, cs, N, K, x, M, y, stream);
+  const hipError_t e = launch_vector(w, cs, N, K, x, 8, y, stream);
+  if (e != hipSuccess) return e;
+  return launch_vector(w, cs, N, K, x + (size_t)8 * K, M - 8, y + (size_t)8 * N, stream);
 }
 
 }  // namespace skinny

@@ -1,5 +1,5 @@
 // gemv_nvfp4.hip -- NVFP4 weights (E2M1 codes, E4M3 scale per 16 elements,
-// float32 per-tensor scale) x binary16 activations, M = 1..8 rows.
+// float32 per-tensor scale) x binary16 activations, M = 1..16 rows.
 //
 // "v100-skinny README", "How QPN works": packed codes stay compressed in
 // memory and are decoded only in registers where they are consumed; the
@@ -148,7 +148,7 @@ __device__ __forceinline__ void nvfp4_step(const uint4_t &wq, uint32_t sc, const
   }
 }
 
-// Matrix-core variant (3 <= M <= 8, K % 256 == 0).
+// Matrix-core variant (3 <= M <= 16, K % 256 == 0).
 //
 // Tile: 16 weight rows.  Lane l = (i = l % 16, g = l / 16) of a wave feeds
 // row 16t + i of the A operand of four v_mfma_f32_16x16x32_f16 per 128-K
@@ -160,60 +160,73 @@ __device__ __forceinline__ void nvfp4_step(const uint4_t &wq, uint32_t sc, const
 // in float32 across all of K, so no binary16 partial sum exists anywhere;
 // the per-tensor scale multiplies the finished sum.
 //
-// Data movement.  Each wave streams its own T tiles over its own slice of
-// K, independently of the other waves (no barrier until the final sum), in
-// chunks of S steps.  A chunk -- codes, group scales and the matching MP
-// activation rows (rows past M repeat row M - 1) -- is read with 128-bit
-// loads in row-contiguous order (each 1 KB load instruction covers whole
-// 128-byte lines) into registers one chunk ahead of its use; registers, not
-// LDS, hold the bytes in flight.  When its turn comes the chunk is written
-// to a wave-private LDS buffer and read back in the operand layout, its
-// registers immediately refilled with the next chunk.  Loads are issued
-// in the order they are consumed, so each wait covers exactly one chunk.
+// Data movement.  A workgroup is WR x KS waves: WR waves own different
+// tiles (T each) and share one K slice, KS slices split K.  K is walked in
+// chunks of S steps.  Every wave reads its own codes and group scales, and
+// a 1/WR share of the slice's activation chunk (MP rows; rows past M repeat
+// row M - 1), with 128-bit loads in row-contiguous order (each 1 KB load
+// instruction covers whole 128-byte lines) into registers one chunk ahead
+// of its use; registers, not LDS, hold the bytes in flight.  When a chunk's
+// turn comes its weights are written to a wave-private LDS buffer and its
+// activation share to the slice's activation buffer (double-buffered when
+// WR > 1, with one barrier per chunk; a lone wave needs neither), then read
+// back in the operand layout while the registers refill with the next
+// chunk.  Sharing cuts the activation bytes each wave pulls from L2 WR-fold;
+// at M = 8 a tile's chunk holds fewer weight bytes than activation bytes,
+// and the two streams share the vector memory path.  Loads are issued in
+// the order they are consumed, so each wait covers exactly one chunk.
 // LDS layout: 1 KB blocks as written by one store instruction (lane l ->
 // bytes 16 l); the 16-byte columns of each block are XOR-swizzled so the
-// operand-layout reads (16 rows at one column) hit distinct banks.  The
-// workgroup's KS waves split K; their partial tiles are summed in LDS.
+// operand-layout reads (16 rows at one column) hit distinct banks.  The KS
+// partial tiles are summed in LDS.
 namespace nv {
-template <int T, int S, int MP>
+template <int T, int WR, int KS, int S, int MP>
 struct Cfg {
+  static constexpr int kWaves = WR * KS;
   static constexpr int kRows = 16 * T;              // weight rows per wave
   static constexpr int kRpi = 16 / S;               // code rows per 1 KB block
   static constexpr int kCi = T * S;                 // code loads per chunk
   static constexpr int kSclB = kRows * 8 * S;       // scale bytes per chunk
+  static constexpr int kWst = kCi * 1024 + kSclB;   // wave weight buffer
   static constexpr int kRpa = 4 / S;                // activation rows per 1 KB block
   static constexpr int kAi = MP / kRpa;             // activation loads per chunk
-  static constexpr int kSclOff = kCi * 1024;
-  static constexpr int kActOff = kSclOff + kSclB;
-  static constexpr int kSt = kActOff + kAi * 1024;  // LDS bytes per wave
+  static constexpr int kApw = (kAi + WR - 1) / WR;  // activation loads per wave
+  static constexpr int kNab = WR > 1 ? 2 : 1;       // activation buffers per slice
+  static constexpr int kAst = kAi * 1024;           // one activation buffer
+  static constexpr int kActBase = kWaves * kWst;
+  static constexpr int kLds = kActBase + KS * kNab * kAst;
   static_assert(S == 2 || S == 4, "chunk steps");
-  static_assert(MP == 4 || MP == 8, "padded activation rows");
+  static_assert(MP == 4 || MP == 8 || MP == 16, "padded activation rows");
   static_assert(kSclB <= 1024, "one scale load per chunk");
+  static_assert(kWaves * T * kWave * 16 <= kLds, "reduction buffer");
+  static_assert(kLds <= 160 * 1024, "LDS per workgroup");
 };
 }  // namespace nv
 
-template <int T, int S>
+template <int T, int S, int APW>
 struct NvChunk {
   uint4_t c[T * S];
   uint4_t s;
-  uint4_t a[8];
+  uint4_t a[APW];
 };
 
 // (No __restrict__ on the inputs: the issue fences below must be able to
 // order their loads.)
-template <int T, int KS, int S, int MP>
-__global__ __launch_bounds__(64 * KS) void gemv_nvfp4_mfma_kernel(
+template <int T, int WR, int KS, int S, int MP>
+__global__ __launch_bounds__(64 * WR * KS) void gemv_nvfp4_mfma_kernel(
     const uint8_t *codes, const uint8_t *scales, float g,
     int N, int K, const uint16_t *x, int M, uint16_t *y) {
-  using C = nv::Cfg<T, S, MP>;
-  using R = NvChunk<T, S>;
+  using C = nv::Cfg<T, WR, KS, S, MP>;
+  using R = NvChunk<T, S, C::kApw>;
   extern __shared__ uint4_t smem4[];
   uint8_t *smem = reinterpret_cast<uint8_t *>(smem4);
   const int lane = threadIdx.x & 63;
-  const int ks = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int wr = wave % WR, ks = wave / WR;
   const int i = lane & 15, grp = lane >> 4;
-  const int n0 = blockIdx.x * C::kRows;
-  uint8_t *ws = smem + ks * C::kSt;
+  const int n0 = blockIdx.x * (C::kRows * WR) + C::kRows * wr;
+  uint8_t *ws = smem + wave * C::kWst;
+  uint8_t *abuf = smem + C::kActBase + ks * C::kNab * C::kAst;
 
   const size_t rowc = (size_t)(K >> 1), rows_ = (size_t)(K >> 4);
   const int nct = K / (128 * S);
@@ -232,28 +245,32 @@ __global__ __launch_bounds__(64 * KS) void gemv_nvfp4_mfma_kernel(
   const int sl = lane % (C::kSclB / 16);       // lanes past the scale bytes repeat one
   const uint8_t *ssrc = scales + (size_t)min(n0 + sl % C::kRows, N - 1) * rows_ +
                         16 * (sl / C::kRows);
-  const uint16_t *asrc[C::kAi];
+  // activation pieces of this wave: p = wr, wr + WR, ... (the last repeated)
+  const uint16_t *asrc[C::kApw];
+  int apiece[C::kApw];
 #pragma unroll
-  for (int a = 0; a < C::kAi; ++a) {
-    const int r = min(a * C::kRpa + (lane % C::kRpa), M - 1);
-    const int j = (lane / C::kRpa) ^ a;
-    asrc[a] = x + (size_t)r * K + 8 * j;
+  for (int u = 0; u < C::kApw; ++u) {
+    const int p = min(wr + WR * u, C::kAi - 1);
+    apiece[u] = p;
+    const int r = min(p * C::kRpa + (lane % C::kRpa), M - 1);
+    const int j = (lane / C::kRpa) ^ p;
+    asrc[u] = x + (size_t)r * K + 8 * j;
   }
   auto load = [&](int c, R &rg) {
 #pragma unroll
     for (int q = 0; q < C::kCi; ++q) rg.c[q] = load16_nt(csrc[q] + (size_t)c * (64 * S));
     rg.s = load16_nt(ssrc + (size_t)c * (8 * S));
 #pragma unroll
-    for (int a = 0; a < C::kAi; ++a) rg.a[a] = load16(asrc[a] + (size_t)c * (128 * S));
+    for (int u = 0; u < C::kApw; ++u) rg.a[u] = load16(asrc[u] + (size_t)c * (128 * S));
     issue_fence();   // keep each chunk's loads together and ahead of later work
   };
-  auto store = [&](const R &rg) {
+  auto store = [&](const R &rg, uint8_t *ab) {
 #pragma unroll
     for (int q = 0; q < C::kCi; ++q) *reinterpret_cast<uint4_t *>(ws + 1024 * q + 16 * lane) = rg.c[q];
-    if (sact) *reinterpret_cast<uint4_t *>(ws + C::kSclOff + 16 * lane) = rg.s;
+    if (sact) *reinterpret_cast<uint4_t *>(ws + C::kCi * 1024 + 16 * lane) = rg.s;
 #pragma unroll
-    for (int a = 0; a < C::kAi; ++a)
-      *reinterpret_cast<uint4_t *>(ws + C::kActOff + 1024 * a + 16 * lane) = rg.a[a];
+    for (int u = 0; u < C::kApw; ++u)
+      *reinterpret_cast<uint4_t *>(ab + 1024 * apiece[u] + 16 * lane) = rg.a[u];
   };
 
   float4_t acc[T];
@@ -261,15 +278,15 @@ __global__ __launch_bounds__(64 * KS) void gemv_nvfp4_mfma_kernel(
   for (int t = 0; t < T; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
 
   const int ar = i & (MP - 1), aa = ar / C::kRpa;   // activation row (columns >= MP wrap)
-  const int aoff = C::kActOff + 1024 * aa + 16 * (ar % C::kRpa);
-  auto consume = [&]() {
+  const int aoff = 1024 * aa + 16 * (ar % C::kRpa);
+  auto consume = [&](const uint8_t *ab) {
 #pragma unroll
     for (int st = 0; st < S; ++st) {
       uint4_t xv[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int j = 16 * st + 4 * grp + u;
-        xv[u] = *reinterpret_cast<const uint4_t *>(ws + aoff + 16 * C::kRpa * (j ^ aa));
+        xv[u] = *reinterpret_cast<const uint4_t *>(ab + aoff + 16 * C::kRpa * (j ^ aa));
       }
 #pragma unroll
       for (int t = 0; t < T; ++t) {
@@ -278,21 +295,29 @@ __global__ __launch_bounds__(64 * KS) void gemv_nvfp4_mfma_kernel(
         const uint4_t wq = *reinterpret_cast<const uint4_t *>(
             ws + 1024 * q + 16 * (C::kRpi * (j ^ (q & (S - 1))) + r % C::kRpi));
         const uint32_t sc = *reinterpret_cast<const uint16_t *>(
-            ws + C::kSclOff + 16 * ((st >> 1) * C::kRows + r) + 8 * (st & 1) + 2 * grp);
+            ws + C::kCi * 1024 + 16 * ((st >> 1) * C::kRows + r) + 8 * (st & 1) + 2 * grp);
         nvfp4_step(wq, sc, xv, acc[t]);
       }
     }
   };
 
-  if (cb < ce) {
-    // The load past the slice re-reads its last chunk into registers that
-    // are never stored, so every path issues the same loads.
+  // A lone wave walks its own slice.  Waves that share activations run
+  // cps steps in lockstep (the barrier); steps past a slice's end load its
+  // last chunk again and compute nothing, so every path issues the same
+  // loads (the load past the last step likewise re-reads into registers
+  // that are never stored).
+  const int steps = WR > 1 ? cps : ce - cb;
+  if (steps > 0) {
+    const int cl = max(ce - 1, 0);                       // a valid chunk to re-read
     R r0;
-    load(cb, r0);
-    for (int c = cb; c < ce; ++c) {
-      store(r0);
-      load(min(c + 1, ce - 1), r0);
-      consume();
+    load(min(cb, cl), r0);
+    for (int k = 0; k < steps; ++k) {
+      const int c = cb + k;
+      uint8_t *ab = abuf + (k & (C::kNab - 1)) * C::kAst;
+      store(r0, ab);
+      if constexpr (WR > 1) wg_barrier();
+      load(min(c + 1, cl), r0);
+      if (c < ce) consume(ab);
     }
   }
 
@@ -300,13 +325,13 @@ __global__ __launch_bounds__(64 * KS) void gemv_nvfp4_mfma_kernel(
     wg_barrier();
     float4_t *red = reinterpret_cast<float4_t *>(smem);
 #pragma unroll
-    for (int t = 0; t < T; ++t) red[(ks * T + t) * kWave + lane] = acc[t];
+    for (int t = 0; t < T; ++t) red[(wave * T + t) * kWave + lane] = acc[t];
     wg_barrier();
     if (ks == 0) {
 #pragma unroll
       for (int t = 0; t < T; ++t)
 #pragma unroll
-        for (int v = 1; v < KS; ++v) acc[t] += red[(v * T + t) * kWave + lane];
+        for (int v = 1; v < KS; ++v) acc[t] += red[((v * WR + wr) * T + t) * kWave + lane];
     }
   }
   if (ks == 0 && i < M) {
@@ -321,21 +346,20 @@ __global__ __launch_bounds__(64 * KS) void gemv_nvfp4_mfma_kernel(
   }
 }
 
-template <int T, int KS, int S, int MP>
+template <int T, int WR, int KS, int S, int MP>
 static hipError_t launch_mfma_cfg(const uint8_t *codes, const uint8_t *scales, float g, int N,
                                   int K, const uint16_t *x, int M, uint16_t *y,
                                   hipStream_t stream) {
-  using C = nv::Cfg<T, S, MP>;
-  constexpr int kLds = KS * C::kSt;
-  static_assert(T * kWave * 16 <= C::kSt, "reduction buffer");
-  static_assert(kLds <= 160 * 1024, "LDS per workgroup");
+  using C = nv::Cfg<T, WR, KS, S, MP>;
   if (K % (128 * S) != 0) return hipErrorInvalidValue;   // chunks must tile K
   // workgroups above 64 KB of LDS must be allowed once per kernel
-  static const hipError_t lds_ok = allow_lds((const void *)gemv_nvfp4_mfma_kernel<T, KS, S, MP>, kLds);
+  static const hipError_t lds_ok =
+      allow_lds((const void *)gemv_nvfp4_mfma_kernel<T, WR, KS, S, MP>, C::kLds);
   if (lds_ok != hipSuccess) return lds_ok;
-  const int blocks = (N + C::kRows - 1) / C::kRows;
-  hipLaunchKernelGGL((gemv_nvfp4_mfma_kernel<T, KS, S, MP>), dim3(blocks), dim3(64 * KS), kLds,
-                     stream, codes, scales, g, N, K, x, M, y);
+  const int rows = C::kRows * WR;
+  const int blocks = (N + rows - 1) / rows;
+  hipLaunchKernelGGL((gemv_nvfp4_mfma_kernel<T, WR, KS, S, MP>), dim3(blocks),
+                     dim3(64 * C::kWaves), C::kLds, stream, codes, scales, g, N, K, x, M, y);
   return hipGetLastError();
 }
 
@@ -349,7 +373,7 @@ static hipError_t launch_mfma_mp(const uint8_t *codes, const uint8_t *scales, fl
                                  hipStream_t stream) {
   const int tiles = (N + 15) / 16;
   const bool s4 = K % 512 == 0;
-#define SKINNY_NV(T, KS, S) return launch_mfma_cfg<T, KS, S, MP>(codes, scales, g, N, K, x, M, y, stream)
+#define SKINNY_NV(T, KS, S) return launch_mfma_cfg<T, 1, KS, S, MP>(codes, scales, g, N, K, x, M, y, stream)
   if (tiles >= 1536) {
     if (s4) SKINNY_NV(2, 1, 4);
     SKINNY_NV(2, 1, 2);
@@ -363,10 +387,30 @@ static hipError_t launch_mfma_mp(const uint8_t *codes, const uint8_t *scales, fl
 #undef SKINNY_NV
 }
 
+// 9 <= M <= 16: sixteen activation rows per chunk, twice the activation
+// bytes per weight byte of M <= 8, so here four waves sharing each
+// activation chunk pays on matrices wide enough to fill the chip with
+// 4-wave workgroups (measured on MI355X at M = 12 and 16, K 5120..17408,
+// N 5120..34816: 2.45 -> 2.70 TB/s on 5120 x 34816); narrow ones split K.
+static hipError_t launch_mfma_wide(const uint8_t *codes, const uint8_t *scales, float g, int N,
+                                   int K, const uint16_t *x, int M, uint16_t *y,
+                                   hipStream_t stream) {
+  const int tiles = (N + 15) / 16;
+#define SKINNY_NV(T, WR, KS, S) \
+  return launch_mfma_cfg<T, WR, KS, S, 16>(codes, scales, g, N, K, x, M, y, stream)
+  if (tiles >= 512) {
+    if (K % 512 == 0) SKINNY_NV(1, 4, 1, 4);
+    SKINNY_NV(2, 2, 1, 2);
+  }
+  SKINNY_NV(2, 1, 4, 2);
+#undef SKINNY_NV
+}
+
 static hipError_t launch_mfma(const uint8_t *codes, const uint8_t *scales, float g, int N,
                               int K, const uint16_t *x, int M, uint16_t *y, hipStream_t stream) {
   if (M <= 4) return launch_mfma_mp<4>(codes, scales, g, N, K, x, M, y, stream);
-  return launch_mfma_mp<8>(codes, scales, g, N, K, x, M, y, stream);
+  if (M <= 8) return launch_mfma_mp<8>(codes, scales, g, N, K, x, M, y, stream);
+  return launch_mfma_wide(codes, scales, g, N, K, x, M, y, stream);
 }
 
 template <int M, int R, int U>
@@ -399,10 +443,10 @@ static hipError_t launch_m(const uint8_t *codes, const uint8_t *scales, float g,
   }
 }
 
-hipError_t launch_gemv_nvfp4(const uint8_t *codes, const uint8_t *scales, float g, int N, int K,
-                             const uint16_t *x, int M, uint16_t *y, hipStream_t stream) {
-  if (M >= kNvfp4MfmaMinM && K % 256 == 0)
-    return launch_mfma(codes, scales, g, N, K, x, M, y, stream);
+// Vector kernel for 1 <= M <= 8 rows.
+static hipError_t launch_vector(const uint8_t *codes, const uint8_t *scales, float g, int N,
+                                int K, const uint16_t *x, int M, uint16_t *y,
+                                hipStream_t stream) {
   switch (M) {
     case 1: return launch_m<1>(codes, scales, g, N, K, x, y, stream);
     case 2: return launch_m<2>(codes, scales, g, N, K, x, y, stream);
@@ -413,6 +457,20 @@ hipError_t launch_gemv_nvfp4(const uint8_t *codes, const uint8_t *scales, float 
     case 7: return launch_m<7>(codes, scales, g, N, K, x, y, stream);
     default: return launch_m<8>(codes, scales, g, N, K, x, y, stream);
   }
+}
+
+// The matrix-core kernel takes every M >= 3 in one weight pass when K is a
+// whole number of 256-element chunks.  Otherwise the vector kernel serves
+// up to 8 rows per pass: rows 9..M take a second pass over the weights.
+hipError_t launch_gemv_nvfp4(const uint8_t *codes, const uint8_t *scales, float g, int N, int K,
+                             const uint16_t *x, int M, uint16_t *y, hipStream_t stream) {
+  if (M >= kNvfp4MfmaMinM && K % 256 == 0)
+    return launch_mfma(codes, scales, g, N, K, x, M, y, stream);
+  if (M <= 8) return launch_vector(codes, scales, g, N, K, x, M, y, stream);
+  const hipError_t e = launch_vector(codes, scales, g, N, K, x, 8, y, stream);
+  if (e != hipSuccess) return e;
+  return launch_vector(codes, scales, g, N, K, x + (size_t)8 * K, M - 8, y + (size_t)8 * N,
+                       stream);
 }
 
 }  // namespace skinny

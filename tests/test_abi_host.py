@@ -76,11 +76,13 @@ def qa(L, x=A, M=1, K=256, qs=A, d=A, s=A):
     return L.quantize_act_q8_1(V(x), M, K, V(qs), V(d), V(s), None)
 
 
-@pytest.mark.parametrize("fn", [q4, nv, f8])
-def test_gemv_rejects_m_out_of_range(L, fn):
-    assert fn(L, M=9) == -4
+@pytest.mark.parametrize("fn,max_m", [(q4, 8), (nv, 16), (f8, 16)])
+def test_gemv_rejects_m_out_of_range(L, fn, max_m):
+    assert fn(L, M=max_m + 1) == -4
     assert fn(L, M=-1) == -4
     assert fn(L, M=1000) == -4
+    # the largest M passes M validation (stopped here by a NULL pointer)
+    assert fn(L, M=max_m, y=0) == -1
 
 
 @pytest.mark.parametrize("fn,kmult", [(q4, 32), (nv, 32), (f8, 16)])

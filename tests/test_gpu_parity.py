@@ -265,7 +265,7 @@ def run_nvfp4(codes, scales, g, x):
     return host(sk.gemv_nvfp4_w4a16(dev(codes), dev(scales), g, dev(x)), np.uint16)
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8, 9, 12, 16])
 @pytest.mark.parametrize("N,K,g", [(1, 32, 1.0), (4096 + 19, 320, 1.0), (1030, 5120, 0.5),
                                    (129, 17408, 2.0 ** -3),
                                    # matrix-core paths: wide / mid / narrow, chunk of 2
@@ -320,6 +320,30 @@ def test_gemv_nvfp4_outliers():
     check_f16(y, y_acc, nvfp4_mag(codes, scales, 1.0, xb), K, "nvfp4 outliers")
 
 
+def test_gemv_nvfp4_sixteen_rows_bit_exact():
+    # M = 16 on the matrix-core path (K % 256 == 0): row n holds code n % 16
+    # at element n under group scale n (NaN codes replaced by 1.0), every
+    # other code +0; x row m is 1 at the elements k with k % 16 == m, so
+    # y[m][n] = e2m1(n % 16) * e4m3(n) when n % 16 == m and 0 otherwise --
+    # one exact term per output, which pins the mapping of all 16 columns
+    N = K = 256
+    codes = np.zeros((N, K // 2), np.uint8)
+    n = np.arange(N)
+    codes[n, n // 2] = np.where(n % 2 == 0, n % 16, (n % 16) << 4).astype(np.uint8)
+    scales = np.zeros((N, K // 16), np.uint8)
+    sc = np.arange(256)
+    sc[[0x7F, 0xFF]] = 0x38
+    scales[n, n // 16] = sc
+    x = np.zeros((16, K), np.float16)
+    for m in range(16):
+        x[m, m::16] = 1.0
+    xb = x.view(np.uint16)
+    y = run_nvfp4(codes, scales, 1.0, xb)
+    _, want = oracle.gemv_nvfp4_w4a16(codes, scales, 1.0, xb)
+    assert np.array_equal(y, want)
+    assert np.count_nonzero(f16(want)) > 200
+
+
 # ------------------------------------------------------------------ FP8
 
 def run_fp8(w, cs, x):
@@ -328,7 +352,7 @@ def run_fp8(w, cs, x):
     return host(sk.gemv_fp8_w8a16(dev(w), dev(cs), dev(x)), np.uint16)
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8, 9, 12, 16])
 @pytest.mark.parametrize("N,K", [(1, 16), (4096 + 3, 272), (1030, 5120), (129, 17408),
                                  # matrix-core paths, as for NVFP4
                                  (25000, 768), (9000, 1280), (40, 768)])
@@ -356,6 +380,26 @@ def test_gemv_fp8_every_code_bit_exact():
     y = run_fp8(w, cs, xb)
     _, want = oracle.gemv_fp8_w8a16(w, cs, xb)
     assert np.array_equal(y, want)
+
+
+def test_gemv_fp8_sixteen_rows_bit_exact():
+    # M = 16 on the matrix-core path: row n holds code n at element n; x row
+    # m is 1 at the elements k with k % 16 == m, so y[m][n] = e4m3(n) when
+    # n % 16 == m and 0 otherwise
+    N = K = 256
+    w = np.zeros((N, K), np.uint8)
+    codes = np.arange(256)
+    codes[[0x7F, 0xFF]] = 0x38
+    w[np.arange(N), np.arange(N)] = codes
+    cs = np.ones(N, np.float32)
+    x = np.zeros((16, K), np.float16)
+    for m in range(16):
+        x[m, m::16] = 1.0
+    xb = x.view(np.uint16)
+    y = run_fp8(w, cs, xb)
+    _, want = oracle.gemv_fp8_w8a16(w, cs, xb)
+    assert np.array_equal(y, want)
+    assert np.count_nonzero(f16(want)) > 200
 
 
 # ------------------------------------------------------------------ full sizes (sampled rows)
@@ -399,7 +443,7 @@ def test_q4_0_f32act_full_sizes_sampled(M):
         check_f32(y[:, rows], ref, mag, K, "q4_0 f32act full M=%d %dx%d" % (M, N, K))
 
 
-@pytest.mark.parametrize("M", [1, 4, 8])
+@pytest.mark.parametrize("M", [1, 4, 8, 16])
 def test_nvfp4_full_sizes_sampled(M):
     for si, (N, K) in enumerate(QWEN_FP):
         codes, scales, g = inputs.nvfp4_weights(N, K, inputs.seed(3, si, 0))
@@ -411,7 +455,7 @@ def test_nvfp4_full_sizes_sampled(M):
                   "nvfp4 full M=%d %dx%d" % (M, N, K))
 
 
-@pytest.mark.parametrize("M", [1, 4, 8])
+@pytest.mark.parametrize("M", [1, 4, 8, 16])
 def test_fp8_full_sizes_sampled(M):
     for si, (N, K) in enumerate(QWEN_FP):
         w, cs = inputs.fp8_weights(N, K, inputs.seed(4, si, 0))
@@ -480,7 +524,14 @@ def test_empty_and_invalid_calls_on_device():
     cs = torch.ones(64, device="cuda")
     y = sk.gemv_fp8_w8a16(w, cs, z)
     assert tuple(y.shape) == (0, 64)
-    x9 = torch.zeros((9, 4096), dtype=torch.float16, device="cuda")
+    x17 = torch.zeros((17, 4096), dtype=torch.float16, device="cuda")
     with pytest.raises(sk.SkinnyError) as e:
-        sk.gemv_fp8_w8a16(w, cs, x9)
+        sk.gemv_fp8_w8a16(w, cs, x17)
+    assert e.value.status == -4
+    # Q4_0 takes at most 8 rows
+    qs, d, s = sk.quantize_act_q8_1(torch.zeros((9, 4096), device="cuda"))
+    w_qs = torch.zeros((64, 2048), dtype=torch.uint8, device="cuda")
+    w_d = torch.zeros((64, 128), dtype=torch.int16, device="cuda")
+    with pytest.raises(sk.SkinnyError) as e:
+        sk.mmvq_q4_0(w_qs, w_d, qs, d, s)
     assert e.value.status == -4
