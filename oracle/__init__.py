@@ -59,6 +59,10 @@ def _load():
     lib.oracle_q4_0_blocksums.restype = None
     lib.oracle_mmvq_q4_0.argtypes = [P, P, I, I, P, P, P, I, P]
     lib.oracle_mmvq_q4_0.restype = None
+    lib.oracle_mmvq_q4_k.argtypes = [P, P, I, I, P, P, P, I, P]
+    lib.oracle_mmvq_q4_k.restype = None
+    lib.oracle_mmvq_q6_k.argtypes = [P, P, P, P, I, I, P, P, I, P]
+    lib.oracle_mmvq_q6_k.restype = None
     lib.oracle_gemv_nvfp4_w4a16.argtypes = [P, P, ctypes.c_float, I, I, P, I, P, P]
     lib.oracle_gemv_nvfp4_w4a16.restype = None
     lib.oracle_gemv_fp8_w8a16.argtypes = [P, P, I, I, P, I, P, P]
@@ -149,6 +153,43 @@ def mmvq_q4_0(w_qs, w_d, a_qs, a_d, a_s) -> np.ndarray:
     assert w_d.shape == (N, K // 32) and a_d.shape == (M, K // 32) and a_s.shape == (M, K // 32)
     y = np.empty((M, N), np.float64)
     _load().oracle_mmvq_q4_0(_p(w_qs), _p(w_d), N, K, _p(a_qs), _p(a_d), _p(a_s), M, _p(y))
+    return y
+
+
+def mmvq_q4_k(w_qs, w_hdr, a_qs, a_d, a_s) -> np.ndarray:
+    """Q4_K weights (qs [N][K/2], hdr [N][K/256][16]) x Q8_1 -> y [M][N] float64."""
+    w_qs = _c(w_qs, np.uint8)
+    w_hdr = _c(w_hdr, np.uint8)
+    a_qs = _c(a_qs, np.int8)
+    a_d = _c(a_d, np.uint16)
+    a_s = _c(a_s, np.uint16)
+    N, K2 = w_qs.shape
+    M, K = a_qs.shape
+    assert K == 2 * K2 and K % 256 == 0
+    assert w_hdr.shape == (N, K // 256, 16)
+    assert a_d.shape == (M, K // 32) and a_s.shape == (M, K // 32)
+    y = np.empty((M, N), np.float64)
+    _load().oracle_mmvq_q4_k(_p(w_qs), _p(w_hdr), N, K, _p(a_qs), _p(a_d), _p(a_s), M, _p(y))
+    return y
+
+
+def mmvq_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d) -> np.ndarray:
+    """Q6_K weights (ql [N][K/2], qh [N][K/4], sc int8 [N][K/16], d [N][K/256])
+    x Q8_1 -> y [M][N] float64."""
+    w_ql = _c(w_ql, np.uint8)
+    w_qh = _c(w_qh, np.uint8)
+    w_sc = _c(w_sc, np.int8)
+    w_d = _c(w_d, np.uint16)
+    a_qs = _c(a_qs, np.int8)
+    a_d = _c(a_d, np.uint16)
+    N, K2 = w_ql.shape
+    M, K = a_qs.shape
+    assert K == 2 * K2 and K % 256 == 0
+    assert w_qh.shape == (N, K // 4) and w_sc.shape == (N, K // 16) and w_d.shape == (N, K // 256)
+    assert a_d.shape == (M, K // 32)
+    y = np.empty((M, N), np.float64)
+    _load().oracle_mmvq_q6_k(_p(w_ql), _p(w_qh), _p(w_sc), _p(w_d), N, K, _p(a_qs), _p(a_d), M,
+                             _p(y))
     return y
 
 

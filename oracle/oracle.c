@@ -17,6 +17,9 @@
  *     is folded into the group scales, each 16-element group being flushed
  *     into an FP32 accumulator; FP8 weights are one E4M3 byte per weight.
  *     Weights stay packed and are decoded only where they are consumed.
+ *   - The same page's model table runs Q4_K and Q6_K models through that
+ *     MMVQ dot; their super-block arithmetic is the published GGUF K-quant
+ *     definition (not on the pages), stated next to those functions.
  *   The pages do not spell out Q8_1, the nibble order, the FP8 scale
  *   granularity or the exact rounding rules; the readings taken here are the
  *   ones listed next to each function.
@@ -238,6 +241,116 @@ void oracle_mmvq_q4_0(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                 double d8 = oracle_f16_to_double(a_d[(size_t)m * nb + b]);
                 double s8 = oracle_f16_to_double(a_s[(size_t)m * nb + b]);
                 acc += d4 * (d8 * (double)isum - 8.0 * s8);
+            }
+            y[(size_t)m * N + n] = acc;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* K-quant weights (Q4_K, Q6_K) x Q8_1 activations.                          */
+/* ------------------------------------------------------------------------ */
+
+/* The CMP page ("llama.cpp results", table of models and quants) runs
+ * Q4_K_M and Q6_K models through the same MMVQ int8 dot as Q4_0 but does not
+ * define the formats.  The arithmetic below is the published GGUF K-quant
+ * definition: super-blocks of 256 weights with per-sub-block integer scales.
+ * The byte layouts are planar arrangements of our own with the same bits per
+ * weight (the pages show no layout).
+ *
+ * Q4_K, per row and super-block S (256 weights = 8 sub-blocks of 32):
+ *   qs  [N][K/2]: codes q in 0..15, same nibble order as Q4_0 (block b of
+ *       32: byte j low nibble = element 32b+j, high nibble = 32b+16+j);
+ *   hdr [N][K/256][16]: bytes 0-1 d (binary16), bytes 2-3 dmin (binary16),
+ *       bytes 4..15 = p[0..11] holding the 6-bit scale sc_j and 6-bit min
+ *       m_j of sub-block j = 0..7: sc_j = p[j] & 63,
+ *       m_j = (p[j] >> 6) | (((p[8 + j/2] >> (4 (j%2))) & 15) << 2).
+ *   weight = d * sc_j * q - dmin * m_j.
+ * With Q8_1 activations (d8, s8 = d8 * sum q8 per block of 32), sub-block j
+ * of super-block S is activation block b = 8S + j and contributes
+ *   d * sc_j * d8_b * isum_b - dmin * m_j * s8_b,
+ * isum_b = sum_{i<32} q * q8 (exact int32): the min is applied once per block
+ * through the Q8_1 sum term, as Q4_0's -8 is. */
+static inline void q4k_scale_min(const uint8_t *p, int j, int *sc, int *m)
+{
+    *sc = p[j] & 63;
+    *m = (p[j] >> 6) | (((p[8 + j / 2] >> (4 * (j % 2))) & 15) << 2);
+}
+
+void oracle_mmvq_q4_k(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
+                      const int8_t *a_qs, const uint16_t *a_d,
+                      const uint16_t *a_s, int M, double *y)
+{
+    int nb = K / 32, ns = K / 256;
+#pragma omp parallel for schedule(static)
+    for (int n = 0; n < N; ++n) {
+        const uint8_t *row = w_qs + (size_t)n * (K / 2);
+        for (int m = 0; m < M; ++m) {
+            const int8_t *a = a_qs + (size_t)m * K;
+            double acc = 0.0;
+            for (int b = 0; b < nb; ++b) {
+                const uint8_t *h = w_hdr + ((size_t)n * ns + b / 8) * 16;
+                int sc, mn;
+                q4k_scale_min(h + 4, b % 8, &sc, &mn);
+                double d = oracle_f16_to_double((uint16_t)(h[0] | (h[1] << 8)));
+                double dmin = oracle_f16_to_double((uint16_t)(h[2] | (h[3] << 8)));
+                int32_t isum = 0;
+                for (int i = 0; i < 32; ++i)
+                    isum += q4_code(row, 32 * b + i) * (int32_t)a[32 * b + i];
+                double d8 = oracle_f16_to_double(a_d[(size_t)m * nb + b]);
+                double s8 = oracle_f16_to_double(a_s[(size_t)m * nb + b]);
+                acc += d * sc * (d8 * (double)isum) - dmin * mn * s8;
+            }
+            y[(size_t)m * N + n] = acc;
+        }
+    }
+}
+
+/* Q6_K, per row and super-block S (256 weights = 16 sub-blocks of 16):
+ *   ql [N][K/2]: low 4 bits of each 6-bit code, Q4_0 nibble order per block
+ *       of 32;
+ *   qh [N][K/4]: high 2 bits, 8 bytes per block b of 32: byte 4h + t
+ *       (h = 0, 1; t = 0..3), bits 2c..2c+1 = high bits of element
+ *       32b + 16h + 4c + t (c = 0..3);
+ *   sc [N][K/16]: int8 scale of each sub-block of 16;
+ *   d  [N][K/256]: binary16.
+ *   code q = low | (high << 4) in 0..63, weight = d * sc * (q - 32).
+ * With Q8_1 activations, block b of 32 holds sub-blocks 2b and 2b+1:
+ *   d * d8_b * (sc_2b * sum_{i<16} (q-32) q8 + sc_2b+1 * sum_{16<=i<32} (q-32) q8),
+ * the bracket an exact integer; no Q8_1 sum term is needed. */
+static inline int q6_code(const uint8_t *ql_row, const uint8_t *qh_row, int k)
+{
+    int b = k / 32, i = k % 32;
+    int lo = q4_code(ql_row, k);
+    int h = i / 16, c = (i % 16) / 4, t = i % 4;
+    int hi = (qh_row[b * 8 + 4 * h + t] >> (2 * c)) & 3;
+    return lo | (hi << 4);
+}
+
+void oracle_mmvq_q6_k(const uint8_t *w_ql, const uint8_t *w_qh, const int8_t *w_sc,
+                      const uint16_t *w_d, int N, int K, const int8_t *a_qs,
+                      const uint16_t *a_d, int M, double *y)
+{
+    int nb = K / 32;
+#pragma omp parallel for schedule(static)
+    for (int n = 0; n < N; ++n) {
+        const uint8_t *ql = w_ql + (size_t)n * (K / 2);
+        const uint8_t *qh = w_qh + (size_t)n * (K / 4);
+        const int8_t *sc = w_sc + (size_t)n * (K / 16);
+        for (int m = 0; m < M; ++m) {
+            const int8_t *a = a_qs + (size_t)m * K;
+            double acc = 0.0;
+            for (int b = 0; b < nb; ++b) {
+                int64_t itot = 0;
+                for (int half = 0; half < 2; ++half) {
+                    int32_t part = 0;
+                    for (int i = 16 * half; i < 16 * half + 16; ++i)
+                        part += (q6_code(ql, qh, 32 * b + i) - 32) * (int32_t)a[32 * b + i];
+                    itot += (int64_t)sc[2 * b + half] * part;
+                }
+                double d = oracle_f16_to_double(w_d[(size_t)n * (K / 256) + b / 8]);
+                double d8 = oracle_f16_to_double(a_d[(size_t)m * nb + b]);
+                acc += d * (d8 * (double)itot);
             }
             y[(size_t)m * N + n] = acc;
         }

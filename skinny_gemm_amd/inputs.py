@@ -19,6 +19,12 @@ Distributions (one per workload):
   * FP8 weights: E4M3 of N(0, 0.05) (clamped to +-448, round to nearest
     even); per-output-channel float32 scales ~ U[0.5, 2].
   * binary16 activations: N(0, 1) drawn in float64, rounded to binary16.
+  * Q4_K weights: uniform random bytes for the 4-bit codes and for the 12
+    packed scale/min bytes of each super-block (every 6-bit field uniform
+    over 0..63); d and dmin ~ U[6.2e-5, 2e-4] rounded to binary16.
+  * Q6_K weights: uniform random bytes for the low and high code bits (codes
+    uniform over 0..63) and for the int8 sub-block scales; d ~ U[6.2e-5,
+    2e-4] rounded to binary16.
 
 Seeds: ``seed(config, shape, tensor)`` = 1000*config + 10*shape + tensor,
 tensor 0 = codes/weights, 1 = scales, 2 = activations.
@@ -82,6 +88,31 @@ def fp8_weights(N: int, K: int, base_seed: int):
     return w, cs
 
 
+def q4_k_weights(N: int, K: int, base_seed: int):
+    """-> (w_qs uint8 [N][K/2], w_hdr uint8 [N][K/256][16]: binary16 d and
+    dmin in bytes 0-3, then 12 packed scale/min bytes)."""
+    ns = K // 256
+    w_qs = _rng(base_seed + 0).integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    r = _rng(base_seed + 1)
+    hdr = np.empty((N, ns, 16), np.uint8)
+    dd = r.uniform(6.2e-5, 2e-4, size=(N, ns, 2)).astype(np.float16)
+    hdr[:, :, 0:4] = dd.view(np.uint8).reshape(N, ns, 4)
+    hdr[:, :, 4:16] = r.integers(0, 256, size=(N, ns, 12), dtype=np.uint8)
+    return w_qs, hdr
+
+
+def q6_k_weights(N: int, K: int, base_seed: int):
+    """-> (w_ql uint8 [N][K/2], w_qh uint8 [N][K/4], w_sc int8 [N][K/16],
+    w_d uint16 [N][K/256] binary16 bits)."""
+    r = _rng(base_seed + 0)
+    w_ql = r.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    w_qh = r.integers(0, 256, size=(N, K // 4), dtype=np.uint8)
+    r = _rng(base_seed + 1)
+    w_sc = r.integers(-128, 128, size=(N, K // 16)).astype(np.int8)
+    w_d = r.uniform(6.2e-5, 2e-4, size=(N, K // 256)).astype(np.float16).view(np.uint16)
+    return w_ql, w_qh, w_sc, w_d
+
+
 def q8_1_unit_scale_source(M: int, K: int, s: int) -> np.ndarray:
     """float32 integer-valued activations for the exact-integer gate.
 
@@ -114,6 +145,38 @@ def q4_0_weights_torch(N: int, K: int, base_seed: int, device):
     u = torch.rand((N, K // 32), dtype=torch.float32, device=device, generator=g)
     w_d = (0.002 + 0.018 * u).to(torch.float16).view(torch.int16)
     return w_qs, w_d
+
+
+def q4_k_weights_torch(N: int, K: int, base_seed: int, device):
+    """Device-side draw with the distributions of ``q4_k_weights``.
+    -> (w_qs uint8 [N][K/2], w_hdr uint8 [N][K/256][16])."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(base_seed))
+    ns = K // 256
+    w_qs = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device=device, generator=g)
+    hdr = torch.randint(0, 256, (N, ns, 16), dtype=torch.uint8, device=device, generator=g)
+    u = torch.rand((N, ns, 2), dtype=torch.float32, device=device, generator=g)
+    dd = (6.2e-5 + 1.38e-4 * u).to(torch.float16)
+    hdr[:, :, 0:4] = dd.view(torch.uint8).reshape(N, ns, 4)
+    return w_qs, hdr
+
+
+def q6_k_weights_torch(N: int, K: int, base_seed: int, device):
+    """Device-side draw with the distributions of ``q6_k_weights``.
+    -> (w_ql uint8 [N][K/2], w_qh uint8 [N][K/4], w_sc int8 [N][K/16],
+    w_d int16 [N][K/256] binary16 bits)."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(base_seed))
+    w_ql = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device=device, generator=g)
+    w_qh = torch.randint(0, 256, (N, K // 4), dtype=torch.uint8, device=device, generator=g)
+    w_sc = torch.randint(-128, 128, (N, K // 16), dtype=torch.int8, device=device, generator=g)
+    u = torch.rand((N, K // 256), dtype=torch.float32, device=device, generator=g)
+    w_d = (6.2e-5 + 1.38e-4 * u).to(torch.float16).view(torch.int16)
+    return w_ql, w_qh, w_sc, w_d
 
 
 def normal_f32_torch(M: int, K: int, s: int, device):

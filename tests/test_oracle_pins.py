@@ -332,6 +332,181 @@ def test_q4_0_bruteforce_is_sensitive():
     assert np.max(np.abs(no_offset - y)) > 1e-2 * np.max(np.abs(y))
 
 
+# ------------------------------------------------------------ K-quants x Q8_1
+
+def q4_k_fields(hdr):
+    """hdr [N][ns][16] -> d, dmin [N][ns] float64; sc, m [N][ns*8] int."""
+    N, ns, _ = hdr.shape
+    d = f16_bits_to_f64(hdr[:, :, 0:2].copy().view(np.uint16)[:, :, 0])
+    dmin = f16_bits_to_f64(hdr[:, :, 2:4].copy().view(np.uint16)[:, :, 0])
+    p = hdr[:, :, 4:16].astype(np.int64)
+    sc = p[:, :, 0:8] & 63
+    hi = np.stack([(p[:, :, 8 + j // 2] >> (4 * (j % 2))) & 15 for j in range(8)], axis=2)
+    m = (p[:, :, 0:8] >> 6) | (hi << 2)
+    return d, dmin, sc.reshape(N, ns * 8), m.reshape(N, ns * 8)
+
+
+def brute_q4_k(w_qs, w_hdr, a_qs, a_d):
+    """Dequantize (d sc q - dmin m per weight) and the Q8_1 codes to fp64,
+    then one matmul: no sum term."""
+    d, dmin, sc, m = q4_k_fields(w_hdr)
+    W = unpack_q4_0(w_qs).astype(np.float64) * np.repeat(np.repeat(d, 8, axis=1) * sc, 32, axis=1) \
+        - np.repeat(np.repeat(dmin, 8, axis=1) * m, 32, axis=1)
+    A = a_qs.astype(np.float64) * np.repeat(f16_bits_to_f64(a_d), 32, axis=1)
+    return A @ W.T
+
+
+def unpack_q6_k(w_ql, w_qh):
+    """-> [N][K] codes 0..63 (low nibbles in Q4_0 order, high bits from qh)."""
+    N, K2 = w_ql.shape
+    K = 2 * K2
+    lo = unpack_q4_0(w_ql)
+    qh = w_qh.reshape(N, K // 32, 2, 4).astype(np.int64)          # [n][b][h][t]
+    hi = np.empty((N, K // 32, 2, 4, 4), np.int64)                 # [n][b][h][c][t]
+    for c in range(4):
+        hi[:, :, :, c, :] = (qh >> (2 * c)) & 3
+    return lo | (hi.reshape(N, K) << 4)
+
+
+def brute_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d):
+    q = unpack_q6_k(w_ql, w_qh)
+    scale = np.repeat(w_sc.astype(np.float64), 16, axis=1) * np.repeat(f16_bits_to_f64(w_d), 256, axis=1)
+    W = (q - 32).astype(np.float64) * scale
+    A = a_qs.astype(np.float64) * np.repeat(f16_bits_to_f64(a_d), 32, axis=1)
+    return A @ W.T
+
+
+def test_q4_k_golden_superblock():
+    rec = read_golden("q4_k_superblock.txt")[0]
+    hdr = np.zeros((1, 1, 16), np.uint8)
+    hdr[0, 0, 0:2] = np.array([int(rec["d"][0], 16)], np.uint16).view(np.uint8)
+    hdr[0, 0, 2:4] = np.array([int(rec["dmin"][0], 16)], np.uint16).view(np.uint8)
+    hdr[0, 0, 4:16] = [int(v, 16) for v in rec["p"]]
+    w_qs = np.repeat(np.array([int(v, 16) for v in rec["block_byte"]], np.uint8), 16)[None, :]
+    halves = [int(v) for v in rec["a_half_values"]]
+    a_qs = np.repeat(np.array(halves, np.int8), 16)[None, :]
+    a_d = np.array([[int(v, 16) for v in rec["a_d"]]], np.uint16)
+    a_s = np.array([[int(v, 16) for v in rec["a_s"]]], np.uint16)
+    y = oracle.mmvq_q4_k(w_qs, hdr, a_qs, a_d, a_s)
+    assert y[0, 0] == float(rec["y"][0])
+
+
+def test_q6_k_golden_superblock():
+    rec = read_golden("q6_k_superblock.txt")[0]
+    K = 256
+    w_ql = np.zeros((1, K // 2), np.uint8)
+    w_ql[0, :16] = [int(v, 16) for v in rec["ql0"]]
+    w_qh = np.zeros((1, K // 4), np.uint8)
+    w_qh[0, :8] = [int(v, 16) for v in rec["qh0"]]
+    w_sc = np.array([[int(v) for v in rec["sc"]]], np.int8)
+    w_d = np.array([[int(rec["d"][0], 16)]], np.uint16)
+    a_qs = np.ones((1, K), np.int8)
+    sp = [int(v) for v in rec["a_special"]]
+    for i in range(0, len(sp), 2):
+        a_qs[0, sp[i]] = sp[i + 1]
+    a_d = np.full((1, K // 32), int(rec["a_d"][0], 16), np.uint16)
+    y = oracle.mmvq_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d)
+    assert y[0, 0] == float(rec["y"][0])
+    # and the fixture's code table agrees with an independent unpacking
+    q = unpack_q6_k(w_ql, w_qh)[0, :32]
+    assert list(q[[0, 4, 5, 12, 16, 20, 21, 28]]) == [40, 40, 63, 0, 33, 16, 33, 33]
+
+
+def test_q4_k_reduces_to_q4_0():
+    # sc_j = 1, m_j = 8, d = dmin = d0: weight = d0 (q - 8), i.e. Q4_0 with d0
+    # in every block of the super-block
+    M, N, K = 3, 21, 1024
+    w_qs, _ = inputs.q4_0_weights(N, K, 41)
+    d0 = inputs.q4_0_weights(N, K // 8, 42)[1][:, : K // 256]       # binary16 bits [N][ns]
+    hdr = np.zeros((N, K // 256, 16), np.uint8)
+    hdr[:, :, 0:2] = d0.view(np.uint8).reshape(N, K // 256, 2)
+    hdr[:, :, 2:4] = hdr[:, :, 0:2]
+    hdr[:, :, 4:12] = 0x01                       # sc 1, low bits of m = 8 & 3 = 0
+    hdr[:, :, 12:16] = 0x22                      # high bits of m = 8 >> 2 = 2
+    x = inputs.normal_f32(M, K, 43)
+    a_qs, a_d, a_s = oracle.quantize_q8_1(x)
+    y_k = oracle.mmvq_q4_k(w_qs, hdr, a_qs, a_d, a_s)
+    y_0 = oracle.mmvq_q4_0(w_qs, np.repeat(d0, 8, axis=1), a_qs, a_d, a_s)
+    assert np.allclose(y_k, y_0, rtol=1e-12, atol=1e-12 * np.abs(y_0).max())
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 7, 256), (4, 37, 1024), (8, 16, 4096)])
+def test_q4_k_vs_fp64_bruteforce(M, N, K):
+    w_qs, w_hdr = inputs.q4_k_weights(N, K, 300 + K)
+    x = inputs.normal_f32(M, K, 400 + K)
+    a_qs, a_d, a_s = oracle.quantize_q8_1(x)
+    y = oracle.mmvq_q4_k(w_qs, w_hdr, a_qs, a_d, a_s)
+    y_bf = brute_q4_k(w_qs, w_hdr, a_qs, a_d)
+    # bound: binary16 rounding of s8 times dmin m per block, plus fp64 sums
+    nb = K // 32
+    d, dmin, sc, m = q4_k_fields(w_hdr)
+    dm = np.repeat(dmin, 8, axis=1) * m                          # [N][nb]
+    d8 = f16_bits_to_f64(a_d)
+    s8 = f16_bits_to_f64(a_s)
+    sq = a_qs.astype(np.int64).reshape(M, nb, 32).sum(axis=2)
+    bound = np.abs(s8 - d8 * sq) @ np.abs(dm).T
+    mag = (np.abs(a_qs.astype(np.float64)) * np.repeat(d8, 32, axis=1)) @ np.abs(
+        unpack_q4_0(w_qs) * np.repeat(np.repeat(d, 8, axis=1) * sc, 32, axis=1)
+        - np.repeat(dm, 32, axis=1)).T
+    bound += (nb + 3) * 2.0 ** -52 * (mag + np.abs(s8) @ np.abs(dm).T)
+    assert np.all(np.abs(y - y_bf) <= bound + 1e-300)
+    assert np.max(bound / mag) < 1e-3
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 7, 256), (4, 37, 1024), (8, 16, 4096)])
+def test_q6_k_vs_fp64_bruteforce(M, N, K):
+    w_ql, w_qh, w_sc, w_d = inputs.q6_k_weights(N, K, 500 + K)
+    x = inputs.normal_f32(M, K, 600 + K)
+    a_qs, a_d, _ = oracle.quantize_q8_1(x)
+    y = oracle.mmvq_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d)
+    y_bf = brute_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d)
+    q = unpack_q6_k(w_ql, w_qh)
+    scale = np.repeat(np.abs(w_sc.astype(np.float64)), 16, axis=1) * np.repeat(f16_bits_to_f64(w_d), 256, axis=1)
+    mag = (np.abs(a_qs.astype(np.float64)) * np.repeat(f16_bits_to_f64(a_d), 32, axis=1)) @ \
+        (np.abs(q - 32) * scale).T
+    # the block brackets are exact integers: only binary64 rounding remains
+    assert np.all(np.abs(y - y_bf) <= (K // 32 + 3) * 2.0 ** -52 * mag + 1e-300)
+
+
+def test_q6_k_unit_scale_exact():
+    # d = 1, sc = 1, integer activations with d8 = 1: y = sum (q - 32) q8 exactly
+    M, N, K = 3, 11, 2048
+    x = inputs.q8_1_unit_scale_source(M, K, 51)
+    a_qs, a_d, _ = oracle.quantize_q8_1(x)
+    w_ql, w_qh, _, _ = inputs.q6_k_weights(N, K, 52)
+    w_sc = np.ones((N, K // 16), np.int8)
+    w_d = np.full((N, K // 256), 0x3C00, np.uint16)
+    y = oracle.mmvq_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d)
+    exact = a_qs.astype(np.int64) @ (unpack_q6_k(w_ql, w_qh) - 32).T
+    assert np.array_equal(y, exact.astype(np.float64))
+
+
+def test_k_quant_bruteforce_is_sensitive():
+    M, N, K = 2, 9, 512
+    x = inputs.normal_f32(M, K, 61)
+    a_qs, a_d, a_s = oracle.quantize_q8_1(x)
+    w_qs, w_hdr = inputs.q4_k_weights(N, K, 62)
+    y = oracle.mmvq_q4_k(w_qs, w_hdr, a_qs, a_d, a_s)
+    tol = 1e-2 * np.max(np.abs(y))
+    # swapping the scale and min fields, or dropping the min, is noticed
+    swapped = w_hdr.copy()
+    swapped[:, :, 4:8], swapped[:, :, 8:12] = w_hdr[:, :, 8:12], w_hdr[:, :, 4:8]
+    assert np.max(np.abs(brute_q4_k(w_qs, swapped, a_qs, a_d) - y)) > tol
+    no_min = w_hdr.copy()
+    no_min[:, :, 2:4] = 0
+    assert np.max(np.abs(brute_q4_k(w_qs, no_min, a_qs, a_d) - y)) > tol
+    # Q6_K: a wrong high-bit position or a dropped -32 is noticed
+    w_ql, w_qh, w_sc, w_d = inputs.q6_k_weights(N, K, 63)
+    y6 = oracle.mmvq_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d)
+    tol6 = 1e-2 * np.max(np.abs(y6))
+    rolled = np.roll(w_qh.reshape(N, -1, 8), 1, axis=2).reshape(N, -1)
+    assert np.max(np.abs(brute_q6_k(w_ql, rolled, w_sc, w_d, a_qs, a_d) - y6)) > tol6
+    q = unpack_q6_k(w_ql, w_qh)
+    scale = np.repeat(w_sc.astype(np.float64), 16, axis=1) * np.repeat(f16_bits_to_f64(w_d), 256, axis=1)
+    no_offset = (a_qs.astype(np.float64) * np.repeat(f16_bits_to_f64(a_d), 32, axis=1)) @ (q * scale).T
+    assert np.max(np.abs(no_offset - y6)) > tol6
+
+
 # ------------------------------------------------------------ NVFP4 W4A16
 
 def test_nvfp4_golden_row():
