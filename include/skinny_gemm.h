@@ -54,7 +54,7 @@ extern "C" {
 /* Limits: 1 <= K <= SKINNY_MAX_K, 0 <= N <= SKINNY_MAX_N. */
 #define SKINNY_MAX_K  (1 << 20)
 #define SKINNY_MAX_N  (1 << 28)
-#define SKINNY_MAX_M_GEMV   8    /* mmvq_q4_0 */
+#define SKINNY_MAX_M_GEMV   8    /* mmvq_q4_0, mmvq_q4_k, mmvq_q6_k */
 /* gemv_nvfp4_w4a16 and gemv_fp8_w8a16: two 8-row verification tiles. */
 #define SKINNY_MAX_M_F16ACT 16
 #define SKINNY_MAX_M_QUANT  65536
@@ -130,6 +130,54 @@ int mmvq_q4_0(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
  */
 int mmvq_q4_0_f32act(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                      const float *x, int M, float *y, void *stream);
+
+/*
+ * mmvq_q4_k -- y = A * W^T for Q4_K weights and Q8_1 activations.
+ *
+ * "Machine Learning on NVIDIA CMP", "llama.cpp results": Q4_K models decode
+ * through the same MMVQ 4-way int8 dot as Q4_0.  The pages do not define the
+ * format; this is the published GGUF K-quant arithmetic in a planar layout
+ * of our own (4.5 bits per weight, as the original):
+ *   w_qs  [N][K/2] bytes, 4-bit codes q in Q4_0 nibble order per block of
+ *         32 (byte j: element j low nibble, element j+16 high nibble).
+ *   w_hdr [N][K/256][16] bytes per super-block of 256: bytes 0-1 d and 2-3
+ *         dmin (binary16), bytes 4..15 = p[0..11] with, for sub-block
+ *         j = 0..7 of 32, sc_j = p[j] & 63 and
+ *         m_j = (p[j] >> 6) | (((p[8 + j/2] >> (4 (j%2))) & 15) << 2).
+ *   weight = d * sc_j * q - dmin * m_j.
+ * For each m, n:  y = sum_b d sc d8 isum_b - dmin m s8_b,
+ * isum_b = sum_{i<32} q * q8 (exact int32); the min enters through the Q8_1
+ * sum term s8.  Accumulated in float32.
+ *   w_qs, w_hdr, a_qs 16-byte aligned; a_d, a_s 2-byte aligned; y float32
+ *   [M][N], 4-byte aligned.  0 <= M <= SKINNY_MAX_M_GEMV; K % 256 == 0.
+ */
+int mmvq_q4_k(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
+              const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
+              int M, float *y, void *stream);
+
+/*
+ * mmvq_q6_k -- y = A * W^T for Q6_K weights and Q8_1 activations.
+ *
+ * As mmvq_q4_k ("llama.cpp results": Q6_K models on the same int8 dot); the
+ * published GGUF Q6_K arithmetic in a planar layout of our own (6.5625 bits
+ * per weight, as the original):
+ *   w_ql [N][K/2]  low 4 bits of the 6-bit codes, Q4_0 nibble order per
+ *        block of 32.
+ *   w_qh [N][K/4]  high 2 bits, 8 bytes per block of 32: byte 4h + t
+ *        (h = 0, 1; t = 0..3), bits 2c..2c+1 = element 16h + 4c + t.
+ *   w_sc [N][K/16] int8 scale of each sub-block of 16.
+ *   w_d  [N][K/256] binary16.
+ *   weight = d * sc_j * (q - 32), q = low | high << 4 in 0..63.
+ * For each m, n:  y = sum_b d d8_b (sc_2b isum_lo + sc_2b+1 isum_hi), the
+ * isums over the two 16-element halves of block b with codes q - 32 (exact
+ * integers; the Q8_1 sum term is not used).  Accumulated in float32.
+ *   w_ql, a_qs 16-byte aligned; w_qh 8-byte aligned; w_sc, w_d, a_d
+ *   2-byte aligned; y float32 [M][N], 4-byte aligned.
+ *   0 <= M <= SKINNY_MAX_M_GEMV; K % 256 == 0.
+ */
+int mmvq_q6_k(const uint8_t *w_ql, const uint8_t *w_qh, const int8_t *w_sc,
+              const uint16_t *w_d, int N, int K, const int8_t *a_qs,
+              const uint16_t *a_d, int M, float *y, void *stream);
 
 /*
  * gemv_nvfp4_w4a16 -- y = x * W^T for NVFP4 weights and binary16 activations.

@@ -1,5 +1,6 @@
 """skinny_gemm_amd -- block-quantized matrix x vector and skinny GEMM
-(M = 1..8) for AMD Instinct MI355X (gfx950).
+(M = 1..16) for AMD Instinct MI355X (gfx950): Q4_0, Q4_K and Q6_K weights
+with Q8_1 activations, NVFP4 and FP8 weights with binary16 activations.
 
 The computation lives in libskinny_gemm.so (hand-written HIP kernels behind
 the C ABI declared in include/skinny_gemm.h).  This package is its thin
@@ -15,6 +16,8 @@ from ._lib import (  # noqa: F401
     library_path,
     mmvq_q4_0,
     mmvq_q4_0_f32act,
+    mmvq_q4_k,
+    mmvq_q6_k,
     quantize_act_q8_1,
     status_string,
 )

@@ -23,7 +23,7 @@ ERR_M = -4
 ERR_LAUNCH = -5
 
 EXPORTS = ("skinny_status_string", "quantize_act_q8_1", "mmvq_q4_0", "mmvq_q4_0_f32act",
-           "gemv_nvfp4_w4a16", "gemv_fp8_w8a16")
+           "mmvq_q4_k", "mmvq_q6_k", "gemv_nvfp4_w4a16", "gemv_fp8_w8a16")
 
 _lib = None
 
@@ -57,6 +57,10 @@ def lib():
     L.mmvq_q4_0.restype = I
     L.mmvq_q4_0_f32act.argtypes = [P, P, I, I, P, I, P, P]
     L.mmvq_q4_0_f32act.restype = I
+    L.mmvq_q4_k.argtypes = [P, P, I, I, P, P, P, I, P, P]
+    L.mmvq_q4_k.restype = I
+    L.mmvq_q6_k.argtypes = [P, P, P, P, I, I, P, P, I, P, P]
+    L.mmvq_q6_k.restype = I
     L.gemv_nvfp4_w4a16.argtypes = [P, P, ctypes.c_float, I, I, P, I, P, P]
     L.gemv_nvfp4_w4a16.restype = I
     L.gemv_fp8_w8a16.argtypes = [P, P, I, I, P, I, P, P]
@@ -168,6 +172,49 @@ def mmvq_q4_0_f32act(w_qs, w_d, x, y=None, stream=None):
     _req(y, "y", (torch.float32,), (M, N))
     _check("mmvq_q4_0_f32act", lib().mmvq_q4_0_f32act(_ptr(w_qs), _ptr(w_d), N, K, _ptr(x), M,
                                                        _ptr(y), _stream(stream)))
+    return y
+
+
+def mmvq_q4_k(w_qs, w_hdr, a_qs, a_d, a_s, y=None, stream=None):
+    """Q4_K weights (qs [N][K/2], hdr [N][K/256][16]), Q8_1 activations
+    -> y float32 [M][N]."""
+    torch = _torch()
+    _req(w_qs, "w_qs", (torch.uint8,))
+    N, K2 = w_qs.shape
+    K = 2 * K2
+    _req(w_hdr, "w_hdr", (torch.uint8,), (N, K // 256, 16))
+    _req(a_qs, "a_qs", (torch.int8,))
+    M = a_qs.shape[0]
+    _req(a_qs, "a_qs", (torch.int8,), (M, K))
+    _req(a_d, "a_d", _f16_bits_dtypes(), (M, K // 32))
+    _req(a_s, "a_s", _f16_bits_dtypes(), (M, K // 32))
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=w_qs.device)
+    _req(y, "y", (torch.float32,), (M, N))
+    _check("mmvq_q4_k", lib().mmvq_q4_k(_ptr(w_qs), _ptr(w_hdr), N, K, _ptr(a_qs), _ptr(a_d),
+                                         _ptr(a_s), M, _ptr(y), _stream(stream)))
+    return y
+
+
+def mmvq_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d, y=None, stream=None):
+    """Q6_K weights (ql [N][K/2], qh [N][K/4], sc int8 [N][K/16], d [N][K/256]),
+    Q8_1 activations (codes and d8) -> y float32 [M][N]."""
+    torch = _torch()
+    _req(w_ql, "w_ql", (torch.uint8,))
+    N, K2 = w_ql.shape
+    K = 2 * K2
+    _req(w_qh, "w_qh", (torch.uint8,), (N, K // 4))
+    _req(w_sc, "w_sc", (torch.int8,), (N, K // 16))
+    _req(w_d, "w_d", _f16_bits_dtypes(), (N, K // 256))
+    _req(a_qs, "a_qs", (torch.int8,))
+    M = a_qs.shape[0]
+    _req(a_qs, "a_qs", (torch.int8,), (M, K))
+    _req(a_d, "a_d", _f16_bits_dtypes(), (M, K // 32))
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=w_ql.device)
+    _req(y, "y", (torch.float32,), (M, N))
+    _check("mmvq_q6_k", lib().mmvq_q6_k(_ptr(w_ql), _ptr(w_qh), _ptr(w_sc), _ptr(w_d), N, K,
+                                         _ptr(a_qs), _ptr(a_d), M, _ptr(y), _stream(stream)))
     return y
 
 

@@ -1,0 +1,341 @@
+// mmvq_kquant.hip -- K-quant weights (Q4_K, Q6_K) x Q8_1 activations,
+// M = 1..8 rows.
+//
+// "Machine Learning on NVIDIA CMP" ("llama.cpp results", model table):
+// Q4_K and Q6_K models decode through the same MMVQ 4-way int8 dot as Q4_0.
+// The pages do not define these formats; the arithmetic is the published
+// GGUF K-quant one (super-blocks of 256 weights with per-sub-block integer
+// scales), in planar byte layouts at the same bits per weight:
+//
+//   Q4_K  qs  [N][K/2]        4-bit codes, Q4_0 nibble order per block of 32
+//         hdr [N][K/256][16]  binary16 d, binary16 dmin, then 12 bytes p
+//                             holding sc_j = p[j] & 63 and
+//                             m_j = (p[j] >> 6) | (nibble j of p[8..11]) << 2
+//         weight = d * sc_j * q - dmin * m_j      (sub-block j of 32)
+//   Q6_K  ql [N][K/2]   low 4 bits, Q4_0 nibble order per block of 32
+//         qh [N][K/4]   high 2 bits: 8 bytes per block, byte 4h + t bits
+//                       2c..2c+1 belong to element 16h + 4c + t
+//         sc [N][K/16]  int8 scale per sub-block of 16;  d [N][K/256] binary16
+//         weight = d * sc_j * (q - 32)
+//
+// Per block b of 32 (one Q8_1 block, exact int32 block sums):
+//   Q4_K: acc += d sc d8 isum - dmin m s8      (the min through the sum term)
+//   Q6_K: acc += d d8 (sc_2b isum_lo + sc_2b+1 isum_hi), codes q - 32 formed
+//         in registers ((q | 0x80) - 0x20) ^ 0x80 per byte, no borrow.
+//
+// Mapping, as the Q4_0 vector kernel: one wave = R weight rows over the
+// full K; lane l takes blocks b = l, l + 64, ... in rounds of U blocks, all
+// loaded before any is used; the lane's Q8_1 block is loaded once and reused
+// for all R rows; a transposing butterfly leaves one output per lane.  Since
+// 64 is a multiple of 8, a lane always sees sub-block j = l % 8 of a Q4_K
+// super-block, so its scale/min bit positions are fixed per lane.
+// Bytes per call: Q4_K N*K*(1/2 + 1/16) + Q6_K N*K*(1/2 + 1/4 + 1/16 + 1/128),
+// plus M*K*(1 + 4/32) (Q4_K) or M*K*(1 + 2/32) (Q6_K) activations and
+// 4*M*N output.
+#include "device.h"
+#include "launch.h"
+
+namespace skinny {
+
+constexpr int kq_pow2(int v) { return v <= 1 ? 1 : 2 * kq_pow2((v + 1) / 2); }
+
+// Leaves one finished output per lane: y[m][n0 + r] for the lane's index.
+template <int R, int M>
+__device__ __forceinline__ void kq_store(float (&acc)[R][M], int lane, int n0, int N, float *y) {
+  constexpr int V = kq_pow2(R * M);
+  float v[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) v[i] = (i < R * M) ? acc[i / M][i % M] : 0.0f;
+  const float total = wave_reduce_transpose<V>(v, lane);
+  constexpr int SHIFT = 6 - Log2<V>::value;
+  const int idx = lane >> SHIFT;
+  if ((lane & ((1 << SHIFT) - 1)) == 0 && idx < R * M) {
+    const int r = idx / M, m = idx % M;
+    const int n = n0 + r;
+    if (n < N) y[(size_t)m * N + n] = total;
+  }
+}
+
+// (No __restrict__ on the inputs: the issue barrier below must be able to
+// keep a round's loads ahead of its arithmetic.)
+template <int M, int R, int U>
+__global__ __launch_bounds__(256) void mmvq_q4_k_kernel(
+    const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K, const int8_t *a_qs,
+    const uint16_t *a_d, const uint16_t *a_s, float *y) {
+  const int lane = threadIdx.x & 63;
+  const int n0 = (blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6)) * R;
+  if (n0 >= N) return;
+  const int nb = K >> 5;
+
+  const uint8_t *wrow[R];
+  const uint8_t *hrow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int n = min(n0 + r, N - 1);          // ragged tail: recompute the last row
+    wrow[r] = w_qs + (size_t)n * (size_t)(K >> 1);
+    hrow[r] = w_hdr + (size_t)n * (size_t)(K >> 8) * 16;
+  }
+  // sub-block j = lane % 8: scale/min byte p[j] is header byte 4 + j (dword
+  // 1 + j / 4), the high min bits nibble j % 2 of p[8 + j / 2] (dword 3)
+  const int j = lane & 7;
+  const int s_sh = 8 * (j & 3);
+  const int h_sh = 8 * (j >> 1) + 4 * (j & 1);
+  const bool s_hi = j >= 4;
+
+  float acc[R][M];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+
+  // blocks past the row end load block nb - 1 again and are not accumulated
+  for (int b0 = lane; b0 < nb; b0 += U * kWave) {
+    uint4_t wq[U][R], hd[U][R];
+    uint4_t aq0[U][M], aq1[U][M];
+    uint16_t d8h[U][M], s8h[U][M];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int b = min(b0 + u * kWave, nb - 1);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        wq[u][r] = load16_nt(wrow[r] + 16 * b);
+        hd[u][r] = load16_nt(hrow[r] + 16 * (b >> 3));
+      }
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const int8_t *ap = a_qs + (size_t)m * K + 32 * b;
+        aq0[u][m] = load16(ap);
+        aq1[u][m] = load16(ap + 16);
+        d8h[u][m] = a_d[(size_t)m * nb + b];
+        s8h[u][m] = a_s[(size_t)m * nb + b];
+      }
+    }
+    issue_all();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool live = b0 + u * kWave < nb;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint4_t h = hd[u][r];
+        const uint32_t pb = (s_hi ? h[2] : h[1]) >> s_sh;
+        const uint32_t sc = pb & 63u;
+        const uint32_t mn = ((pb >> 6) & 3u) | (((h[3] >> h_sh) & 15u) << 2);
+        const float dsc = f16_bits_to_f32((uint16_t)(h[0] & 0xFFFFu)) * (float)sc;
+        const float dmm = f16_bits_to_f32((uint16_t)(h[0] >> 16)) * (float)mn;
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          lo[i] = wq[u][r][i] & 0x0F0F0F0Fu;
+          hi[i] = (wq[u][r][i] >> 4) & 0x0F0F0F0Fu;
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          int32_t isum = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            isum = dot4_i8(lo[i], aq0[u][m][i], isum);
+            isum = dot4_i8(hi[i], aq1[u][m][i], isum);
+          }
+          const float t = fmaf(dsc * f16_bits_to_f32(d8h[u][m]), (float)isum,
+                               -(dmm * f16_bits_to_f32(s8h[u][m])));
+          const float a = acc[r][m] + t;
+          acc[r][m] = live ? a : acc[r][m];
+        }
+      }
+    }
+  }
+  kq_store<R, M>(acc, lane, n0, N, y);
+}
+
+// High bits of the four elements of low-nibble word i (byte t <- bits 2i,
+// 2i+1 of byte t of h), placed at bits 4..5 of each byte.
+__device__ __forceinline__ uint32_t q6_high(uint32_t h, int i) {
+  const uint32_t v = i == 0 ? h << 4 : i == 1 ? h << 2 : i == 2 ? h : h >> 2;
+  return v & 0x30303030u;
+}
+
+// Four 6-bit codes q -> four int8 values q - 32: setting bit 7 first keeps
+// the byte-wise subtraction from borrowing across bytes.
+__device__ __forceinline__ uint32_t q6_centre(uint32_t q) {
+  return ((q | 0x80808080u) - 0x20202020u) ^ 0x80808080u;
+}
+
+template <int M, int R, int U>
+__global__ __launch_bounds__(256) void mmvq_q6_k_kernel(
+    const uint8_t *w_ql, const uint8_t *w_qh, const int8_t *w_sc, const uint16_t *w_d, int N,
+    int K, const int8_t *a_qs, const uint16_t *a_d, float *y) {
+  const int lane = threadIdx.x & 63;
+  const int n0 = (blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6)) * R;
+  if (n0 >= N) return;
+  const int nb = K >> 5;
+
+  const uint8_t *lrow[R];
+  const uint8_t *hrow[R];
+  const uint16_t *srow[R];
+  const uint16_t *drow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int n = min(n0 + r, N - 1);
+    lrow[r] = w_ql + (size_t)n * (size_t)(K >> 1);
+    hrow[r] = w_qh + (size_t)n * (size_t)(K >> 2);
+    srow[r] = reinterpret_cast<const uint16_t *>(w_sc + (size_t)n * (size_t)(K >> 4));
+    drow[r] = w_d + (size_t)n * (size_t)(K >> 8);
+  }
+
+  float acc[R][M];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+
+  for (int b0 = lane; b0 < nb; b0 += U * kWave) {
+    uint4_t wl[U][R];
+    uint2_t wh[U][R];
+    uint16_t scw[U][R], dh[U][R];
+    uint4_t aq0[U][M], aq1[U][M];
+    uint16_t d8h[U][M];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int b = min(b0 + u * kWave, nb - 1);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        wl[u][r] = load16_nt(lrow[r] + 16 * b);
+        wh[u][r] = load8_nt(hrow[r] + 8 * b);
+        scw[u][r] = load_u16_nt(srow[r] + b);
+        dh[u][r] = load_u16_nt(drow[r] + (b >> 3));
+      }
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const int8_t *ap = a_qs + (size_t)m * K + 32 * b;
+        aq0[u][m] = load16(ap);
+        aq1[u][m] = load16(ap + 16);
+        d8h[u][m] = a_d[(size_t)m * nb + b];
+      }
+    }
+    issue_all();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool live = b0 + u * kWave < nb;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          lo[i] = q6_centre((wl[u][r][i] & 0x0F0F0F0Fu) | q6_high(wh[u][r].x, i));
+          hi[i] = q6_centre(((wl[u][r][i] >> 4) & 0x0F0F0F0Fu) | q6_high(wh[u][r].y, i));
+        }
+        const int32_t sa = (int32_t)(int8_t)(scw[u][r] & 0xFFu);
+        const int32_t sb = (int32_t)(int8_t)(scw[u][r] >> 8);
+        const float d6 = f16_bits_to_f32(dh[u][r]);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          int32_t ia = 0, ib = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            ia = dot4_i8(lo[i], aq0[u][m][i], ia);
+            ib = dot4_i8(hi[i], aq1[u][m][i], ib);
+          }
+          const int32_t itot = sa * ia + sb * ib;
+          const float a = fmaf(d6 * f16_bits_to_f32(d8h[u][m]), (float)itot, acc[r][m]);
+          acc[r][m] = live ? a : acc[r][m];
+        }
+      }
+    }
+  }
+  kq_store<R, M>(acc, lane, n0, N, y);
+}
+
+template <int M, int R, int U>
+static hipError_t launch_q4k_mru(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
+                                 const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
+                                 float *y, hipStream_t stream) {
+  const int waves = (N + R - 1) / R;
+  hipLaunchKernelGGL((mmvq_q4_k_kernel<M, R, U>), dim3((waves + 3) / 4), dim3(256), 0, stream,
+                     w_qs, w_hdr, N, K, a_qs, a_d, a_s, y);
+  return hipGetLastError();
+}
+
+template <int M, int R, int U>
+static hipError_t launch_q6k_mru(const uint8_t *w_ql, const uint8_t *w_qh, const int8_t *w_sc,
+                                 const uint16_t *w_d, int N, int K, const int8_t *a_qs,
+                                 const uint16_t *a_d, float *y, hipStream_t stream) {
+  const int waves = (N + R - 1) / R;
+  hipLaunchKernelGGL((mmvq_q6_k_kernel<M, R, U>), dim3((waves + 3) / 4), dim3(256), 0, stream,
+                     w_ql, w_qh, w_sc, w_d, N, K, a_qs, a_d, y);
+  return hipGetLastError();
+}
+
+// Launch shapes measured on MI355X over the Qwen3-8B projections (K 4096 and
+// 12288, N 4096 to 24576) at M = 1, 2, 4, 8.  At M <= 2 a lane takes its
+// whole share of a row in one round up to 6 blocks (K <= 12288), two rows
+// per wave, four on wide matrices.  Wider M takes one or two blocks per
+// round (the activation registers grow with M) and four rows per wave on
+// wide or long matrices.
+template <int M>
+static hipError_t launch_q4k_m(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
+                               const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
+                               float *y, hipStream_t stream) {
+  const int per_lane = ((K >> 5) + kWave - 1) / kWave;
+#define SKINNY_Q4K(R, U) return launch_q4k_mru<M, R, U>(w_qs, w_hdr, N, K, a_qs, a_d, a_s, y, stream)
+  if constexpr (M <= 2) {
+    if (per_lane <= 2) {
+      if (N >= 16384) SKINNY_Q4K(4, 2);
+      SKINNY_Q4K(2, 2);
+    }
+    if (per_lane <= 4) SKINNY_Q4K(2, 4);
+    SKINNY_Q4K(2, 6);
+  } else {
+    if (N >= 16384 || K >= 8192) SKINNY_Q4K(4, 1);
+    SKINNY_Q4K(2, 1);
+  }
+#undef SKINNY_Q4K
+}
+
+template <int M>
+static hipError_t launch_q6k_m(const uint8_t *w_ql, const uint8_t *w_qh, const int8_t *w_sc,
+                               const uint16_t *w_d, int N, int K, const int8_t *a_qs,
+                               const uint16_t *a_d, float *y, hipStream_t stream) {
+  const int per_lane = ((K >> 5) + kWave - 1) / kWave;
+#define SKINNY_Q6K(R, U) \
+  return launch_q6k_mru<M, R, U>(w_ql, w_qh, w_sc, w_d, N, K, a_qs, a_d, y, stream)
+  if constexpr (M <= 2) {
+    if (per_lane <= 2) {
+      if (M == 2 && N >= 16384) SKINNY_Q6K(4, 2);
+      SKINNY_Q6K(2, 2);
+    }
+    if (per_lane <= 4) SKINNY_Q6K(2, 4);
+    SKINNY_Q6K(2, 6);
+  } else {
+    if (N >= 16384) SKINNY_Q6K(4, 1);
+    SKINNY_Q6K(2, 2);
+  }
+#undef SKINNY_Q6K
+}
+
+hipError_t launch_mmvq_q4_k(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
+                            const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s, int M,
+                            float *y, hipStream_t stream) {
+  switch (M) {
+#define SKINNY_Q4K(MM) \
+  case MM: return launch_q4k_m<MM>(w_qs, w_hdr, N, K, a_qs, a_d, a_s, y, stream);
+    SKINNY_Q4K(1) SKINNY_Q4K(2) SKINNY_Q4K(3) SKINNY_Q4K(4)
+    SKINNY_Q4K(5) SKINNY_Q4K(6) SKINNY_Q4K(7)
+#undef SKINNY_Q4K
+    default: return launch_q4k_m<8>(w_qs, w_hdr, N, K, a_qs, a_d, a_s, y, stream);
+  }
+}
+
+hipError_t launch_mmvq_q6_k(const uint8_t *w_ql, const uint8_t *w_qh, const int8_t *w_sc,
+                            const uint16_t *w_d, int N, int K, const int8_t *a_qs,
+                            const uint16_t *a_d, int M, float *y, hipStream_t stream) {
+  switch (M) {
+#define SKINNY_Q6K(MM) \
+  case MM: return launch_q6k_m<MM>(w_ql, w_qh, w_sc, w_d, N, K, a_qs, a_d, y, stream);
+    SKINNY_Q6K(1) SKINNY_Q6K(2) SKINNY_Q6K(3) SKINNY_Q6K(4)
+    SKINNY_Q6K(5) SKINNY_Q6K(6) SKINNY_Q6K(7)
+#undef SKINNY_Q6K
+    default: return launch_q6k_m<8>(w_ql, w_qh, w_sc, w_d, N, K, a_qs, a_d, y, stream);
+  }
+}
+
+}  // namespace skinny

@@ -32,8 +32,8 @@ def L():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["skinny_status_string", "quantize_act_q8_1",
-                                           "mmvq_q4_0", "mmvq_q4_0_f32act", "gemv_nvfp4_w4a16",
-                                           "gemv_fp8_w8a16"])
+                                           "mmvq_q4_0", "mmvq_q4_0_f32act", "mmvq_q4_k",
+                                           "mmvq_q6_k", "gemv_nvfp4_w4a16", "gemv_fp8_w8a16"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -72,11 +72,19 @@ def f8(L, w=A, cs=A, N=64, K=256, x=A, M=1, y=A):
     return L.gemv_fp8_w8a16(V(w), V(cs), N, K, V(x), M, V(y), None)
 
 
+def q4k(L, w=A, h=A, N=64, K=256, aq=A, ad=A, as_=A, M=1, y=A):
+    return L.mmvq_q4_k(V(w), V(h), N, K, V(aq), V(ad), V(as_), M, V(y), None)
+
+
+def q6k(L, ql=A, qh=A, sc=A, d=A, N=64, K=256, aq=A, ad=A, M=1, y=A):
+    return L.mmvq_q6_k(V(ql), V(qh), V(sc), V(d), N, K, V(aq), V(ad), M, V(y), None)
+
+
 def qa(L, x=A, M=1, K=256, qs=A, d=A, s=A):
     return L.quantize_act_q8_1(V(x), M, K, V(qs), V(d), V(s), None)
 
 
-@pytest.mark.parametrize("fn,max_m", [(q4, 8), (nv, 16), (f8, 16)])
+@pytest.mark.parametrize("fn,max_m", [(q4, 8), (q4k, 8), (q6k, 8), (nv, 16), (f8, 16)])
 def test_gemv_rejects_m_out_of_range(L, fn, max_m):
     assert fn(L, M=max_m + 1) == -4
     assert fn(L, M=-1) == -4
@@ -180,3 +188,29 @@ def test_f32act_validation(L):
     assert call(M=0) == 0 and call(N=0) == 0              # nothing to do
     assert call(x=None) == -1 and call(w=None) == -1
     assert call(x=V(A + 4)) == -3 and call(w=V(A + 8)) == -3 and call(y=V(A + 2)) == -3
+
+
+@pytest.mark.parametrize("fn", [q4k, q6k])
+def test_k_quant_validation(L, fn):
+    # K must be a whole number of 256-weight super-blocks
+    for K in (0, 32, 128, 256 + 32, 4096 + 128, (1 << 20) + 256):
+        assert fn(L, K=K) == -2, K
+    assert fn(L, K=1 << 20, y=0) == -1
+    assert fn(L, N=-1) == -2
+    # no-ops
+    assert fn(L, M=0, y=0, aq=0) == 0
+    assert fn(L, N=0, y=0, aq=0) == 0
+
+
+def test_k_quant_null_and_alignment(L):
+    for kw in ("w", "h", "aq", "ad", "as_", "y"):
+        assert q4k(L, **{kw: 0}) == -1, kw
+    for kw, off in (("w", 8), ("h", 8), ("aq", 8), ("ad", 1), ("as_", 1), ("y", 2)):
+        assert q4k(L, **{kw: A + off}) == -3, kw
+    for kw in ("ql", "qh", "sc", "d", "aq", "ad", "y"):
+        assert q6k(L, **{kw: 0}) == -1, kw
+    for kw, off in (("ql", 8), ("qh", 4), ("sc", 1), ("d", 1), ("aq", 8), ("ad", 1), ("y", 2)):
+        assert q6k(L, **{kw: A + off}) == -3, kw
+    # the weaker requirements really are weaker
+    assert q6k(L, qh=A + 8, y=0) == -1
+    assert q6k(L, sc=A + 2, y=0) == -1

@@ -257,6 +257,125 @@ def test_mmvq_q4_0_f32act_adversarial_blocks():
     assert np.array_equal(y.astype(np.float64), exact)
 
 
+# ------------------------------------------------------------------ K-quants
+
+def q4_k_fields(hdr):
+    """hdr [N][ns][16] -> d, dmin [N][ns] float64; sc, m [N][ns*8]."""
+    N, ns, _ = hdr.shape
+    d = f16(hdr[:, :, 0:2].copy().view(np.uint16)[:, :, 0])
+    dmin = f16(hdr[:, :, 2:4].copy().view(np.uint16)[:, :, 0])
+    p = hdr[:, :, 4:16].astype(np.int64)
+    sc = p[:, :, 0:8] & 63
+    hi = np.stack([(p[:, :, 8 + j // 2] >> (4 * (j % 2))) & 15 for j in range(8)], axis=2)
+    return d, dmin, sc.reshape(N, ns * 8), ((p[:, :, 0:8] >> 6) | (hi << 2)).reshape(N, ns * 8)
+
+
+def q4_k_mag(w_qs, w_hdr, a_qs, a_d, a_s):
+    d, dmin, sc, m = q4_k_fields(w_hdr)
+    W = unpack_q4_0(w_qs) * np.repeat(np.repeat(np.abs(d), 8, axis=1) * sc, 32, axis=1)
+    A = np.abs(a_qs.astype(np.float64)) * np.repeat(np.abs(f16(a_d)), 32, axis=1)
+    return A @ W.T + np.abs(f16(a_s)) @ (np.repeat(np.abs(dmin), 8, axis=1) * m).T
+
+
+def unpack_q6_k(w_ql, w_qh):
+    N, K2 = w_ql.shape
+    K = 2 * K2
+    qh = w_qh.reshape(N, K // 32, 2, 4).astype(np.int64)
+    hi = np.stack([(qh >> (2 * c)) & 3 for c in range(4)], axis=3)     # [n][b][h][c][t]
+    return unpack_q4_0(w_ql) | (hi.reshape(N, K) << 4)
+
+
+def q6_k_mag(w_ql, w_qh, w_sc, w_d, a_qs, a_d):
+    W = np.abs(unpack_q6_k(w_ql, w_qh) - 32) * np.repeat(np.abs(w_sc.astype(np.float64)), 16, axis=1) \
+        * np.repeat(np.abs(f16(w_d)), 256, axis=1)
+    A = np.abs(a_qs.astype(np.float64)) * np.repeat(np.abs(f16(a_d)), 32, axis=1)
+    return A @ W.T
+
+
+def run_q4_k(w_qs, w_hdr, a_qs, a_d, a_s):
+    import skinny_gemm_amd as sk
+
+    return host(sk.mmvq_q4_k(dev(w_qs), dev(w_hdr), dev(a_qs), dev(a_d), dev(a_s)))
+
+
+def run_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d):
+    import skinny_gemm_amd as sk
+
+    return host(sk.mmvq_q6_k(dev(w_ql), dev(w_qh), dev(w_sc), dev(w_d), dev(a_qs), dev(a_d)))
+
+
+KQ_SHAPES = [(1, 256), (4096 + 37, 256), (4099, 1280), (257, 12288), (1000, 4096), (63, 16384),
+             (16384 + 9, 512)]   # last: the four-row wide-matrix shapes
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("N,K", KQ_SHAPES)
+def test_mmvq_q4_k_vs_oracle(M, N, K):
+    w_qs, w_hdr = inputs.q4_k_weights(N, K, 7 * N + K)
+    x = inputs.normal_f32(M, K, 3 * M + K)
+    a_qs, a_d, a_s = oracle.quantize_q8_1(x)
+    y = run_q4_k(w_qs, w_hdr, a_qs, a_d, a_s)
+    ref = oracle.mmvq_q4_k(w_qs, w_hdr, a_qs, a_d, a_s)
+    check_f32(y, ref, q4_k_mag(w_qs, w_hdr, a_qs, a_d, a_s), K,
+              "q4_k M=%d N=%d K=%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("N,K", KQ_SHAPES)
+def test_mmvq_q6_k_vs_oracle(M, N, K):
+    w_ql, w_qh, w_sc, w_d = inputs.q6_k_weights(N, K, 11 * N + K)
+    x = inputs.normal_f32(M, K, 5 * M + K)
+    a_qs, a_d, _ = oracle.quantize_q8_1(x)
+    y = run_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d)
+    ref = oracle.mmvq_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d)
+    check_f32(y, ref, q6_k_mag(w_ql, w_qh, w_sc, w_d, a_qs, a_d), K,
+              "q6_k M=%d N=%d K=%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_k_quant_integer_gate_bit_exact(M):
+    # unit scales and integer activations (d8 = 1, s8 = sum q8 exactly):
+    # every term is an integer below 2^24, so any summation order gives the
+    # exact result
+    N, K = 300, 4096
+    x = inputs.q8_1_unit_scale_source(M, K, 70 + M)
+    a_qs, a_d, a_s = oracle.quantize_q8_1(x)
+    w_qs, w_hdr = inputs.q4_k_weights(N, K, 71)
+    w_hdr[:, :, 0:2] = np.array([0x3C00], np.uint16).view(np.uint8)       # d = 1
+    w_hdr[:, :, 2:4] = np.array([0x3C00], np.uint16).view(np.uint8)       # dmin = 1
+    w_hdr[:, :, 4:12] &= 0x07                                              # sc <= 7, m low bits 0
+    w_hdr[:, :, 12:16] &= 0x11                                             # m in {0, 4}
+    y = run_q4_k(w_qs, w_hdr, a_qs, a_d, a_s)
+    ref = oracle.mmvq_q4_k(w_qs, w_hdr, a_qs, a_d, a_s)
+    assert np.all(np.abs(ref) < 2 ** 24) and np.array_equal(ref, np.round(ref))
+    assert np.array_equal(y.astype(np.float64), ref)
+    w_ql, w_qh, w_sc, _ = inputs.q6_k_weights(N, K, 72)
+    w_sc = (w_sc.astype(np.int64) % 5 - 2).astype(np.int8)                # sc in -2..2
+    w_d = np.full((N, K // 256), 0x3C00, np.uint16)
+    y6 = run_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d)
+    ref6 = oracle.mmvq_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d)
+    assert np.all(np.abs(ref6) < 2 ** 24) and np.array_equal(ref6, np.round(ref6))
+    assert np.array_equal(y6.astype(np.float64), ref6)
+
+
+def test_k_quant_pipeline_device_quantize():
+    # quantize_act_q8_1 on the device feeding both K-quant GEMVs
+    import skinny_gemm_amd as sk
+
+    M, N, K = 3, 2048 + 5, 4096
+    x = inputs.normal_f32(M, K, 81)
+    qs, d, s = sk.quantize_act_q8_1(dev(x))
+    a_qs, a_d, a_s = oracle.quantize_q8_1(x)
+    w_qs, w_hdr = inputs.q4_k_weights(N, K, 82)
+    y = host(sk.mmvq_q4_k(dev(w_qs), dev(w_hdr), qs, d, s))
+    check_f32(y, oracle.mmvq_q4_k(w_qs, w_hdr, a_qs, a_d, a_s),
+              q4_k_mag(w_qs, w_hdr, a_qs, a_d, a_s), K, "q4_k pipeline")
+    w_ql, w_qh, w_sc, w_d = inputs.q6_k_weights(N, K, 83)
+    y6 = host(sk.mmvq_q6_k(dev(w_ql), dev(w_qh), dev(w_sc), dev(w_d), qs, d))
+    check_f32(y6, oracle.mmvq_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d),
+              q6_k_mag(w_ql, w_qh, w_sc, w_d, a_qs, a_d), K, "q6_k pipeline")
+
+
 # ------------------------------------------------------------------ NVFP4
 
 def run_nvfp4(codes, scales, g, x):
