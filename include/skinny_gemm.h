@@ -1,8 +1,8 @@
 /*
  * skinny_gemm.h -- C ABI of libskinny_gemm.so: block-quantized matrix x
- * vector and skinny GEMM (M = 1..8 activation rows for Q4_0, 1..16 for the
- * binary16-activation formats) for LLM decode and speculative verification
- * on AMD Instinct MI355X (gfx950).
+ * vector and skinny GEMM (M = 1..8 activation rows for the Q8_1 formats,
+ * 1..16 for NVFP4, 1..96 for FP8) for LLM decode and speculative
+ * verification on AMD Instinct MI355X (gfx950).
  *
  * Sources.  "Machine Learning on NVIDIA CMP" (sections "TL;DR", "llama.cpp
  * results", "The DP2A patch") describes decode as a quantized mat x vec
@@ -24,7 +24,7 @@
  *     nothing, keeps no state between calls, and is safe to call from
  *     several host threads.  Outputs must not overlap inputs.
  *   - A call validates its arguments on the host before any HIP call, then
- *     enqueues its kernel (two, for the split cases stated below) on
+ *     enqueues its kernel (several, for the split cases stated below) on
  *     `stream` and returns without synchronizing.
  *     Faults during execution surface at the caller's next synchronization.
  *   - binary16 values are passed as their 16-bit patterns (uint16_t).
@@ -55,8 +55,10 @@ extern "C" {
 #define SKINNY_MAX_K  (1 << 20)
 #define SKINNY_MAX_N  (1 << 28)
 #define SKINNY_MAX_M_GEMV   8    /* mmvq_q4_0, mmvq_q4_k, mmvq_q6_k */
-/* gemv_nvfp4_w4a16 and gemv_fp8_w8a16: two 8-row verification tiles. */
+/* gemv_nvfp4_w4a16: two 8-row verification tiles. */
 #define SKINNY_MAX_M_F16ACT 16
+/* gemv_fp8_w8a16: also the "chunked" band up to 96 rows. */
+#define SKINNY_MAX_M_FP8    96
 #define SKINNY_MAX_M_QUANT  65536
 /* mmvq_q4_0_f32act: decode widths only, one row of K in LDS per workgroup. */
 #define SKINNY_MAX_M_F32ACT 2
@@ -215,11 +217,12 @@ int gemv_nvfp4_w4a16(const uint8_t *w_codes, const uint8_t *w_scales,
  *   y   binary16 [M][N] row-major, 2-byte aligned:
  *       y = binary16( channel_scale[n] * sum_k e4m3(w[n][k]) * x[m][k] ),
  *       accumulated in float32.
- *   0 <= M <= SKINNY_MAX_M_F16ACT; K % 16 == 0.  Rows 9..16 (the wide
- *   verification band, "How QPN works" and "Native mixed-precision
- *   checkpoint path": two 8-row tiles against one weight pass) share one
- *   weight pass whenever K % 256 == 0; otherwise rows 1..8 and 9..M take one
- *   pass each.  NaN weight codes (0x7F, 0xFF) give unspecified results.
+ *   0 <= M <= SKINNY_MAX_M_FP8; K % 16 == 0.  Rows 9..16 (the wide
+ *   verification band, "How QPN works": two 8-row tiles against one weight
+ *   pass) and 17..96 (the "chunked" FP8 band of the dispatch table in
+ *   "Native mixed-precision checkpoint path") share one weight pass
+ *   whenever K % 256 == 0; otherwise each group of up to 8 rows takes its
+ *   own pass.  NaN weight codes (0x7F, 0xFF) give unspecified results.
  */
 int gemv_fp8_w8a16(const uint8_t *w, const float *channel_scale, int N, int K,
                    const uint16_t *x, int M, uint16_t *y, void *stream);

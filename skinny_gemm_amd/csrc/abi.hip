@@ -123,7 +123,7 @@ int gemv_nvfp4_w4a16(const uint8_t *w_codes, const uint8_t *w_scales, float glob
 
 int gemv_fp8_w8a16(const uint8_t *w, const float *channel_scale, int N, int K,
                    const uint16_t *x, int M, uint16_t *y, void *stream) {
-  int st = gemv_m_status(M, SKINNY_MAX_M_F16ACT);
+  int st = gemv_m_status(M, SKINNY_MAX_M_FP8);
   if (st) return st;
   if ((st = shape_status(N, K, 16))) return st;
   if (M == 0 || N == 0) return SKINNY_OK;

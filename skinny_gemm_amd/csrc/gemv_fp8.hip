@@ -1,4 +1,4 @@
-// gemv_fp8.hip -- FP8 E4M3 weights x binary16 activations, M = 1..16 rows,
+// gemv_fp8.hip -- FP8 E4M3 weights x binary16 activations, M = 1..96 rows,
 // per-output-channel float32 scale.
 //
 // "v100-skinny README", "How QPN works": the FP8 weights are one contiguous
@@ -107,76 +107,91 @@ __global__ __launch_bounds__(256) void gemv_fp8_kernel(
   }
 }
 
-// Matrix-core variant (3 <= M <= 16, K % 256 == 0).
+// Matrix-core variant (3 <= M <= 96, K % 256 == 0).
 //
 // Tile: 16 weight rows.  Lane l = (i = l % 16, g = l / 16) of a wave feeds
 // row 16t + i of the A operand of four v_mfma_f32_16x16x32_f16 per 128-K
 // step: its 32 weight bytes (elements k0 .. k0+31, k0 = 128 s + 32 g)
 // decode exactly to binary16 (every E4M3 value is a binary16 value).  The B
-// operands are the activations x[i][k0 + 8t .. +8] (columns i >= M are
-// computed and dropped).  Float32 accumulation across all of K; the channel
-// scale multiplies the finished sum.
+// operands are the activations x[16c + i][k0 + 8u .. +8] of column tile c:
+// one column tile for M <= 16 (columns i >= M computed and dropped), MT =
+// MP / 16 of them above, each decoded A operand feeding MT matrix-core
+// instructions (the "chunked" FP8 band of the pages' dispatch table).
+// Float32 accumulation across all of K; the channel scale multiplies the
+// finished sum.
 //
-// Data movement, as for the NVFP4 kernel: each wave streams its own T tiles
-// over its own slice of K with no barrier until the final sum, in chunks of
-// S steps.  A chunk -- weight bytes and the matching MP activation rows
-// (rows past M repeat row M - 1) -- is read with 128-bit loads in
-// row-contiguous order into registers one chunk ahead of its use, then
-// written to a wave-private LDS buffer (1 KB blocks, 16-byte columns
-// XOR-swizzled per block so the operand-layout reads hit distinct banks)
-// and read back in the operand layout.  Loads are issued in the order they
-// are consumed, so each wait covers exactly one chunk.  The workgroup's KS
-// waves split K; their partial tiles are summed in LDS.
-__device__ __forceinline__ void fp8_step(const uint4_t (&wq)[2], const uint4_t (&xv)[4],
-                                         float4_t &acc) {
+// Data movement, as for the NVFP4 kernel.  A workgroup is WR x KS waves:
+// WR waves own different tiles (T each) and share one K slice, KS slices
+// split K.  K is walked in chunks of S steps.  Every wave reads its own
+// weight bytes and a 1/WR share of the slice's activation chunk (MP rows;
+// rows past M repeat row M - 1), with 128-bit loads in row-contiguous order
+// into registers one chunk ahead of its use; at its turn the chunk goes to
+// LDS -- weights to a wave-private buffer, activations to the slice's buffer
+// (double-buffered when WR > 1, with one barrier per chunk) -- in 1 KB blocks
+// whose 16-byte columns are XOR-swizzled so the operand-layout reads hit
+// distinct banks, and is read back in the operand layout.  Loads are issued
+// in the order they are consumed, so each wait covers exactly one chunk.
+// The KS partial tiles are summed in LDS.
+__device__ __forceinline__ void fp8_decode(const uint4_t (&wq)[2], half8_t (&a)[4]) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const uint32_t w0 = wq[t >> 1][2 * (t & 1)];
-    const uint32_t w1 = wq[t >> 1][2 * (t & 1) + 1];
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t w0 = wq[u >> 1][2 * (u & 1)];
+    const uint32_t w1 = wq[u >> 1][2 * (u & 1) + 1];
     const half2_t h0 = e4m3x2_to_h2<false>(w0);
     const half2_t h1 = e4m3x2_to_h2<true>(w0);
     const half2_t h2 = e4m3x2_to_h2<false>(w1);
     const half2_t h3 = e4m3x2_to_h2<true>(w1);
-    const half8_t a = {h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
-    acc = mfma_16x16x32_f16(a, __builtin_bit_cast(half8_t, xv[t]), acc);
+    a[u] = half8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
   }
 }
 
 namespace f8 {
-template <int T, int S, int MP>
+template <int T, int WR, int KS, int S, int MP>
 struct Cfg {
+  static constexpr int kWaves = WR * KS;
+  static constexpr int kMT = MP > 16 ? MP / 16 : 1;  // column tiles
   static constexpr int kRows = 16 * T;              // weight rows per wave
   static constexpr int kRpi = 8 / S;                // weight rows per 1 KB block
-  static constexpr int kSwz = 2 * S - 1;            // column swizzle mask
+  static constexpr int kSwz = 2 * S - 1;            // weight column swizzle mask
   static constexpr int kCi = 2 * T * S;             // weight loads per chunk
+  static constexpr int kWst = kCi * 1024;           // wave weight buffer
   static constexpr int kRpa = 4 / S;                // activation rows per 1 KB block
+  static constexpr int kACols = 16 * S;             // 16-byte columns per activation row
   static constexpr int kAi = MP / kRpa;             // activation loads per chunk
-  static constexpr int kActOff = kCi * 1024;
-  static constexpr int kSt = kActOff + kAi * 1024;  // LDS bytes per wave
-  static_assert(S == 2 || S == 4, "chunk steps");
-  static_assert(MP == 4 || MP == 8 || MP == 16, "padded activation rows");
+  static constexpr int kApw = (kAi + WR - 1) / WR;  // activation loads per wave
+  static constexpr int kNab = WR > 1 ? 2 : 1;       // activation buffers per slice
+  static constexpr int kAst = kAi * 1024;
+  static constexpr int kActBase = kWaves * kWst;
+  static constexpr int kLds = kActBase + KS * kNab * kAst;
+  static_assert(S == 1 || S == 2 || S == 4, "chunk steps");
+  static_assert(MP == 4 || MP == 8 || (MP % 16 == 0 && MP <= 96), "padded activation rows");
+  static_assert(kWaves * T * kMT * kWave * 16 <= kLds, "reduction buffer");
+  static_assert(kLds <= 160 * 1024, "LDS per workgroup");
 };
-template <int T, int S, int AI>
+template <int T, int S, int APW>
 struct Chunk {
   uint4_t c[2 * T * S];
-  uint4_t a[AI];
+  uint4_t a[APW];
 };
 }  // namespace f8
 
 // (No __restrict__ on the inputs: the issue fence below must be able to
 // order their loads.)
-template <int T, int KS, int S, int MP>
-__global__ __launch_bounds__(64 * KS) void gemv_fp8_mfma_kernel(
+template <int T, int WR, int KS, int S, int MP>
+__global__ __launch_bounds__(64 * WR * KS) void gemv_fp8_mfma_kernel(
     const uint8_t *w, const float *cs, int N, int K, const uint16_t *x, int M, uint16_t *y) {
-  using C = f8::Cfg<T, S, MP>;
-  using R = f8::Chunk<T, S, C::kAi>;
+  using C = f8::Cfg<T, WR, KS, S, MP>;
+  using R = f8::Chunk<T, S, C::kApw>;
+  constexpr int MT = C::kMT;
   extern __shared__ uint4_t smem4[];
   uint8_t *smem = reinterpret_cast<uint8_t *>(smem4);
   const int lane = threadIdx.x & 63;
-  const int ks = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int wr = wave % WR, ks = wave / WR;
   const int i = lane & 15, grp = lane >> 4;
-  const int n0 = blockIdx.x * C::kRows;
-  uint8_t *ws = smem + ks * C::kSt;
+  const int n0 = blockIdx.x * (C::kRows * WR) + C::kRows * wr;
+  uint8_t *ws = smem + wave * C::kWst;
+  uint8_t *abuf = smem + C::kActBase + ks * C::kNab * C::kAst;
 
   const int nct = K / (128 * S);
   const int cps = (nct + KS - 1) / KS;
@@ -189,67 +204,112 @@ __global__ __launch_bounds__(64 * KS) void gemv_fp8_mfma_kernel(
     const int j = (lane / C::kRpi) ^ (q & C::kSwz);
     wsrc[q] = w + (size_t)min(n0 + r, N - 1) * (size_t)K + 16 * j;
   }
-  const uint16_t *asrc[C::kAi];
+  // activation pieces of this wave: p = wr, wr + WR, ... (the last repeated)
+  const uint16_t *asrc[C::kApw];
+  int apiece[C::kApw];
 #pragma unroll
-  for (int a = 0; a < C::kAi; ++a) {
-    const int r = min(a * C::kRpa + (lane % C::kRpa), M - 1);
-    const int j = (lane / C::kRpa) ^ a;
-    asrc[a] = x + (size_t)r * K + 8 * j;
+  for (int u = 0; u < C::kApw; ++u) {
+    const int p = min(wr + WR * u, C::kAi - 1);
+    apiece[u] = p;
+    const int r = min(p * C::kRpa + (lane % C::kRpa), M - 1);
+    const int j = (lane / C::kRpa) ^ (p & (C::kACols - 1));
+    asrc[u] = x + (size_t)r * K + 8 * j;
   }
   auto load = [&](int c, R &rg) {
 #pragma unroll
     for (int q = 0; q < C::kCi; ++q) rg.c[q] = load16_nt(wsrc[q] + (size_t)c * (128 * S));
 #pragma unroll
-    for (int a = 0; a < C::kAi; ++a) rg.a[a] = load16(asrc[a] + (size_t)c * (128 * S));
+    for (int u = 0; u < C::kApw; ++u) rg.a[u] = load16(asrc[u] + (size_t)c * (128 * S));
     issue_fence();   // keep each chunk's loads together and ahead of later work
   };
-  auto store = [&](const R &rg) {
+  auto store = [&](const R &rg, uint8_t *ab) {
 #pragma unroll
     for (int q = 0; q < C::kCi; ++q) *reinterpret_cast<uint4_t *>(ws + 1024 * q + 16 * lane) = rg.c[q];
 #pragma unroll
-    for (int a = 0; a < C::kAi; ++a)
-      *reinterpret_cast<uint4_t *>(ws + C::kActOff + 1024 * a + 16 * lane) = rg.a[a];
+    for (int u = 0; u < C::kApw; ++u)
+      *reinterpret_cast<uint4_t *>(ab + 1024 * apiece[u] + 16 * lane) = rg.a[u];
   };
 
-  float4_t acc[T];
+  float4_t acc[T][MT];
 #pragma unroll
-  for (int t = 0; t < T; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int c = 0; c < MT; ++c) acc[t][c] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int ar = i & (MP - 1), aa = ar / C::kRpa;   // activation row (columns >= MP wrap)
-  const int aoff = C::kActOff + 1024 * aa + 16 * (ar % C::kRpa);
-  auto consume = [&]() {
+  // activation row of column tile c for this lane (columns >= MP wrap when
+  // MP < 16)
+  auto arow = [&](int c) { return MP >= 16 ? 16 * c + i : (i & (MP - 1)); };
+  auto decode = [&](int st, int t, half8_t (&a)[4]) {
+    const int r = 16 * t + i, q = r / C::kRpi;
+    uint4_t wq[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int j = 8 * st + 2 * grp + h;
+      wq[h] = *reinterpret_cast<const uint4_t *>(
+          ws + 1024 * q + 16 * (C::kRpi * (j ^ (q & C::kSwz)) + r % C::kRpi));
+    }
+    fp8_decode(wq, a);
+  };
+  auto act = [&](const uint8_t *ab, int st, int c, uint4_t (&xv)[4]) {
+    const int ar = arow(c), aa = ar / C::kRpa;
+    const uint8_t *ap = ab + 1024 * aa + 16 * (ar % C::kRpa);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = 16 * st + 4 * grp + u;
+      xv[u] = *reinterpret_cast<const uint4_t *>(ap + 16 * C::kRpa * (j ^ (aa & (C::kACols - 1))));
+    }
+  };
+  auto consume = [&](const uint8_t *ab) {
 #pragma unroll
     for (int st = 0; st < S; ++st) {
-      uint4_t xv[4];
+      if constexpr (MT == 1) {
+        // one column tile: decode each weight tile just before its products
+        uint4_t xv[4];
+        act(ab, st, 0, xv);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j = 16 * st + 4 * grp + u;
-        xv[u] = *reinterpret_cast<const uint4_t *>(ws + aoff + 16 * C::kRpa * (j ^ aa));
-      }
+        for (int t = 0; t < T; ++t) {
+          half8_t a[4];
+          decode(st, t, a);
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        const int r = 16 * t + i, q = r / C::kRpi;
-        uint4_t wq[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int j = 8 * st + 2 * grp + h;
-          wq[h] = *reinterpret_cast<const uint4_t *>(
-              ws + 1024 * q + 16 * (C::kRpi * (j ^ (q & C::kSwz)) + r % C::kRpi));
+          for (int u = 0; u < 4; ++u)
+            acc[t][0] = mfma_16x16x32_f16(a[u], __builtin_bit_cast(half8_t, xv[u]), acc[t][0]);
         }
-        fp8_step(wq, xv, acc[t]);
+      } else {
+        // several column tiles: decode every weight tile once, reuse it MT times
+        half8_t a[T][4];
+#pragma unroll
+        for (int t = 0; t < T; ++t) decode(st, t, a[t]);
+#pragma unroll
+        for (int c = 0; c < MT; ++c) {
+          uint4_t xv[4];
+          act(ab, st, c, xv);
+#pragma unroll
+          for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              acc[t][c] = mfma_16x16x32_f16(a[t][u], __builtin_bit_cast(half8_t, xv[u]), acc[t][c]);
+        }
       }
     }
   };
 
-  if (cb < ce) {
-    // The load past the slice re-reads its last chunk into registers that
-    // are never stored, so every path issues the same loads.
+  // A lone wave walks its own slice.  Waves that share activations run cps
+  // steps in lockstep (the barrier); steps past a slice's end load its last
+  // chunk again and compute nothing, so every path issues the same loads
+  // (the load past the last step likewise re-reads into registers that are
+  // never stored).
+  const int steps = WR > 1 ? cps : ce - cb;
+  if (steps > 0) {
+    const int cl = max(ce - 1, 0);                       // a valid chunk to re-read
     R r0;
-    load(cb, r0);
-    for (int c = cb; c < ce; ++c) {
-      store(r0);
-      load(min(c + 1, ce - 1), r0);
-      consume();
+    load(min(cb, cl), r0);
+    for (int k = 0; k < steps; ++k) {
+      const int c = cb + k;
+      uint8_t *ab = abuf + (k & (C::kNab - 1)) * C::kAst;
+      store(r0, ab);
+      if constexpr (WR > 1) wg_barrier();
+      load(min(c + 1, cl), r0);
+      if (c < ce) consume(ab);
     }
   }
 
@@ -257,40 +317,49 @@ __global__ __launch_bounds__(64 * KS) void gemv_fp8_mfma_kernel(
     wg_barrier();
     float4_t *red = reinterpret_cast<float4_t *>(smem);
 #pragma unroll
-    for (int t = 0; t < T; ++t) red[(ks * T + t) * kWave + lane] = acc[t];
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int c = 0; c < MT; ++c) red[((wave * T + t) * MT + c) * kWave + lane] = acc[t][c];
     wg_barrier();
     if (ks == 0) {
 #pragma unroll
       for (int t = 0; t < T; ++t)
 #pragma unroll
-        for (int v = 1; v < KS; ++v) acc[t] += red[(v * T + t) * kWave + lane];
+        for (int c = 0; c < MT; ++c)
+#pragma unroll
+          for (int v = 1; v < KS; ++v) acc[t][c] += red[(((v * WR + wr) * T + t) * MT + c) * kWave + lane];
     }
   }
-  if (ks == 0 && i < M) {
+  if (ks == 0) {
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
+    for (int c = 0; c < MT; ++c) {
+      const int m = MP >= 16 ? 16 * c + i : i;
+      if (m < M) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int n = n0 + 16 * t + 4 * grp + r;
-        if (n < N) y[(size_t)i * N + n] = f32_to_f16_bits(acc[t][r] * cs[n]);
+        for (int t = 0; t < T; ++t) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int n = n0 + 16 * t + 4 * grp + r;
+            if (n < N) y[(size_t)m * N + n] = f32_to_f16_bits(acc[t][c][r] * cs[n]);
+          }
+        }
       }
     }
   }
 }
 
-template <int T, int KS, int S, int MP>
+template <int T, int WR, int KS, int S, int MP>
 static hipError_t launch_mfma_cfg(const uint8_t *w, const float *cs, int N, int K,
                                   const uint16_t *x, int M, uint16_t *y, hipStream_t stream) {
-  using C = f8::Cfg<T, S, MP>;
-  constexpr int kLds = KS * C::kSt;
-  static_assert(T * kWave * 16 <= C::kSt, "reduction buffer");
-  static_assert(kLds <= 160 * 1024, "LDS per workgroup");
+  using C = f8::Cfg<T, WR, KS, S, MP>;
   if (K % (128 * S) != 0) return hipErrorInvalidValue;   // chunks must tile K
-  static const hipError_t lds_ok = allow_lds((const void *)gemv_fp8_mfma_kernel<T, KS, S, MP>, kLds);
+  static const hipError_t lds_ok =
+      allow_lds((const void *)gemv_fp8_mfma_kernel<T, WR, KS, S, MP>, C::kLds);
   if (lds_ok != hipSuccess) return lds_ok;
-  const int blocks = (N + C::kRows - 1) / C::kRows;
-  hipLaunchKernelGGL((gemv_fp8_mfma_kernel<T, KS, S, MP>), dim3(blocks), dim3(64 * KS), kLds,
-                     stream, w, cs, N, K, x, M, y);
+  const int rows = C::kRows * WR;
+  const int blocks = (N + rows - 1) / rows;
+  hipLaunchKernelGGL((gemv_fp8_mfma_kernel<T, WR, KS, S, MP>), dim3(blocks),
+                     dim3(64 * C::kWaves), C::kLds, stream, w, cs, N, K, x, M, y);
   return hipGetLastError();
 }
 
@@ -301,7 +370,7 @@ static hipError_t launch_mfma_mp(const uint8_t *w, const float *cs, int N, int K
                                  const uint16_t *x, int M, uint16_t *y, hipStream_t stream) {
   const int tiles = (N + 15) / 16;
   const bool s4 = K % 512 == 0;
-#define SKINNY_F8(T, KS, S) return launch_mfma_cfg<T, KS, S, MP>(w, cs, N, K, x, M, y, stream)
+#define SKINNY_F8(T, KS, S) return launch_mfma_cfg<T, 1, KS, S, MP>(w, cs, N, K, x, M, y, stream)
   if (tiles >= 1536) {
     if (M <= 4) SKINNY_F8(1, 1, 2);
     SKINNY_F8(2, 1, 2);
@@ -325,7 +394,7 @@ static hipError_t launch_mfma_wide(const uint8_t *w, const float *cs, int N, int
                                    const uint16_t *x, int M, uint16_t *y, hipStream_t stream) {
   const int tiles = (N + 15) / 16;
   const bool s4 = K % 512 == 0;
-#define SKINNY_F8(T, KS, S) return launch_mfma_cfg<T, KS, S, 16>(w, cs, N, K, x, M, y, stream)
+#define SKINNY_F8(T, KS, S) return launch_mfma_cfg<T, 1, KS, S, 16>(w, cs, N, K, x, M, y, stream)
   if (tiles >= 1536) SKINNY_F8(4, 1, 2);
   if (tiles >= 512) {
     if (s4) SKINNY_F8(1, 1, 4);
@@ -336,11 +405,46 @@ static hipError_t launch_mfma_wide(const uint8_t *w, const float *cs, int N, int
 #undef SKINNY_F8
 }
 
+// 17 <= M <= 96: MP / 16 column tiles per decoded weight operand.  The
+// activation chunk (MP rows) outweighs the weights, so two to eight waves
+// share it through LDS, and LDS then leaves room for a K split only with
+// short chunks.  Measured on MI355X at M = 32, 64, 96 over K 5120..17408, N
+// 5120..34816: wide matrices favour more sharing waves, narrow ones a K
+// split; narrow matrices at M >= 64 stay limited by their few workgroups
+// (0.6 TB/s on 17408 x 5120 at M = 96, against 1.6 on 5120 x 34816).
+template <int MP>
+static hipError_t launch_mfma_chunked_mp(const uint8_t *w, const float *cs, int N, int K,
+                                         const uint16_t *x, int M, uint16_t *y,
+                                         hipStream_t stream) {
+  const int tiles = (N + 15) / 16;
+#define SKINNY_F8(T, WR, KS, S) \
+  return launch_mfma_cfg<T, WR, KS, S, MP>(w, cs, N, K, x, M, y, stream)
+  if constexpr (MP <= 48) {
+    if (tiles >= 1536) SKINNY_F8(2, 2, 1, 2);
+    SKINNY_F8(1, 4, 2, 2);
+  } else if constexpr (MP == 64) {
+    if (tiles >= 1536) SKINNY_F8(1, 4, 1, 2);
+    SKINNY_F8(1, 2, 1, 2);
+  } else {
+    if (tiles >= 1536) SKINNY_F8(1, 8, 1, 1);
+    if (tiles >= 512) SKINNY_F8(1, 4, 1, 2);
+    SKINNY_F8(1, 2, 2, 1);
+  }
+#undef SKINNY_F8
+}
+
 static hipError_t launch_mfma(const uint8_t *w, const float *cs, int N, int K, const uint16_t *x,
                               int M, uint16_t *y, hipStream_t stream) {
   if (M <= 4) return launch_mfma_mp<4>(w, cs, N, K, x, M, y, stream);
   if (M <= 8) return launch_mfma_mp<8>(w, cs, N, K, x, M, y, stream);
-  return launch_mfma_wide(w, cs, N, K, x, M, y, stream);
+  if (M <= 16) return launch_mfma_wide(w, cs, N, K, x, M, y, stream);
+  switch ((M + 15) / 16) {
+    case 2: return launch_mfma_chunked_mp<32>(w, cs, N, K, x, M, y, stream);
+    case 3: return launch_mfma_chunked_mp<48>(w, cs, N, K, x, M, y, stream);
+    case 4: return launch_mfma_chunked_mp<64>(w, cs, N, K, x, M, y, stream);
+    case 5: return launch_mfma_chunked_mp<80>(w, cs, N, K, x, M, y, stream);
+    default: return launch_mfma_chunked_mp<96>(w, cs, N, K, x, M, y, stream);
+  }
 }
 
 template <int M, int R, int U>
@@ -389,14 +493,16 @@ static hipError_t launch_vector(const uint8_t *w, const float *cs, int N, int K,
 
 // The matrix-core kernel takes every M >= 3 in one weight pass when K is a
 // whole number of 256-element chunks.  Otherwise the vector kernel serves
-// up to 8 rows per pass: rows 9..M take a second pass over the weights.
+// up to 8 rows per pass over the weights: rows 1..8, 9..16, ...
 hipError_t launch_gemv_fp8(const uint8_t *w, const float *cs, int N, int K, const uint16_t *x,
                            int M, uint16_t *y, hipStream_t stream) {
   if (M >= kFp8MfmaMinM && K % 256 == 0) return launch_mfma(w, cs, N, K, x, M, y, stream);
-  if (M <= 8) return launch_vector(w, cs, N, K, x, M, y, stream);
-  const hipError_t e = launch_vector(w, cs, N, K, x, 8, y, stream);
-  if (e != hipSuccess) return e;
-  return launch_vector(w, cs, N, K, x + (size_t)8 * K, M - 8, y + (size_t)8 * N, stream);
+  for (int m0 = 0; m0 < M; m0 += 8) {
+    const hipError_t e = launch_vector(w, cs, N, K, x + (size_t)m0 * K, min(8, M - m0),
+                                       y + (size_t)m0 * N, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace skinny

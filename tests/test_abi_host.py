@@ -84,7 +84,7 @@ def qa(L, x=A, M=1, K=256, qs=A, d=A, s=A):
     return L.quantize_act_q8_1(V(x), M, K, V(qs), V(d), V(s), None)
 
 
-@pytest.mark.parametrize("fn,max_m", [(q4, 8), (q4k, 8), (q6k, 8), (nv, 16), (f8, 16)])
+@pytest.mark.parametrize("fn,max_m", [(q4, 8), (q4k, 8), (q6k, 8), (nv, 16), (f8, 96)])
 def test_gemv_rejects_m_out_of_range(L, fn, max_m):
     assert fn(L, M=max_m + 1) == -4
     assert fn(L, M=-1) == -4

@@ -483,6 +483,41 @@ def test_gemv_fp8_vs_oracle(M, N, K):
     check_f16(y, y_acc, fp8_mag(w, cs, x), K, "fp8 M=%d N=%d K=%d" % (M, N, K))
 
 
+@pytest.mark.parametrize("M", [17, 31, 48, 64, 80, 96])
+@pytest.mark.parametrize("N,K", [(4096 + 3, 272),     # K % 256 != 0: passes of 8 rows
+                                 (1030, 5120),        # narrow: K split (one-step chunks at M > 64)
+                                 (3000, 1280),
+                                 (9000, 768),         # mid
+                                 (24576 + 40, 256),   # wide: more waves share each chunk
+                                 (40, 768)])
+def test_gemv_fp8_chunked_vs_oracle(M, N, K):
+    w, cs = inputs.fp8_weights(N, K, 13 * N + K)
+    x = inputs.normal_f16_bits(M, K, 6 * M + K)
+    y = run_fp8(w, cs, x)
+    y_acc, _ = oracle.gemv_fp8_w8a16(w, cs, x)
+    check_f16(y, y_acc, fp8_mag(w, cs, x), K, "fp8 M=%d N=%d K=%d" % (M, N, K))
+
+
+def test_gemv_fp8_ninety_six_rows_bit_exact():
+    # M = 96 on the chunked path: row n holds code n at element n; x row m is
+    # 1 at the elements k with k % 96 == m (so each output has at most one
+    # exact term) -- pins the mapping of all six column tiles
+    N, K = 256, 256
+    w = np.zeros((N, K), np.uint8)
+    codes = np.arange(256)
+    codes[[0x7F, 0xFF]] = 0x38
+    w[np.arange(N), np.arange(N)] = codes
+    cs = np.ones(N, np.float32)
+    x = np.zeros((96, K), np.float16)
+    for m in range(96):
+        x[m, m::96] = 1.0
+    xb = x.view(np.uint16)
+    y = run_fp8(w, cs, xb)
+    _, want = oracle.gemv_fp8_w8a16(w, cs, xb)
+    assert np.array_equal(y, want)
+    assert np.count_nonzero(f16(want)) > 200
+
+
 def test_gemv_fp8_every_code_bit_exact():
     # row n holds code n at element n % 16; x row m is one-hot at m and m+8
     N, K = 256, 16
@@ -574,7 +609,7 @@ def test_nvfp4_full_sizes_sampled(M):
                   "nvfp4 full M=%d %dx%d" % (M, N, K))
 
 
-@pytest.mark.parametrize("M", [1, 4, 8, 16])
+@pytest.mark.parametrize("M", [1, 4, 8, 16, 32, 96])
 def test_fp8_full_sizes_sampled(M):
     for si, (N, K) in enumerate(QWEN_FP):
         w, cs = inputs.fp8_weights(N, K, inputs.seed(4, si, 0))
@@ -643,9 +678,15 @@ def test_empty_and_invalid_calls_on_device():
     cs = torch.ones(64, device="cuda")
     y = sk.gemv_fp8_w8a16(w, cs, z)
     assert tuple(y.shape) == (0, 64)
-    x17 = torch.zeros((17, 4096), dtype=torch.float16, device="cuda")
+    x97 = torch.zeros((97, 4096), dtype=torch.float16, device="cuda")
     with pytest.raises(sk.SkinnyError) as e:
-        sk.gemv_fp8_w8a16(w, cs, x17)
+        sk.gemv_fp8_w8a16(w, cs, x97)
+    assert e.value.status == -4
+    # NVFP4 takes at most 16 rows
+    codes = torch.zeros((64, 2048), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((64, 256), dtype=torch.uint8, device="cuda")
+    with pytest.raises(sk.SkinnyError) as e:
+        sk.gemv_nvfp4_w4a16(codes, scales, 1.0, x97[:17])
     assert e.value.status == -4
     # Q4_0 takes at most 8 rows
     qs, d, s = sk.quantize_act_q8_1(torch.zeros((9, 4096), device="cuda"))
