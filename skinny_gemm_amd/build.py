@@ -34,6 +34,9 @@ def compile_flags():
         "-I", CSRC, "-I", INCLUDE,
         # keep the compiler from forming packed-fp32 instructions
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # matrix-core results in ordinary VGPRs: the integer block sums feed
+        # float epilogues directly instead of through accumulation registers
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-Wall", "-Wno-unused-function",
     ]
 

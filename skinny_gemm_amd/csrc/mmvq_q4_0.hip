@@ -196,16 +196,25 @@ struct Chunk {
 };
 }  // namespace q4
 
-__device__ __forceinline__ void q4_mfma_step(const uint2_t &wq, const int4_t &aop, float d4,
-                                             const float4_t &sa, const float4_t &sb,
-                                             float4_t &acc) {
+// The exact int32 block sums of one 64-K step: the lane's 8 code bytes split
+// into 16 codes (low nibbles, then high nibbles) against the activation
+// operand.
+__device__ __forceinline__ int4_t q4_mfma_isum(const uint2_t &wq, const int4_t &aop) {
   int4_t bop;
   bop[0] = (int)(wq.x & 0x0F0F0F0Fu);
   bop[1] = (int)(wq.y & 0x0F0F0F0Fu);
   bop[2] = (int)((wq.x >> 4) & 0x0F0F0F0Fu);
   bop[3] = (int)((wq.y >> 4) & 0x0F0F0F0Fu);
   const int4_t zero = {0, 0, 0, 0};
-  const int4_t isum = mfma_16x16x64_i8(aop, bop, zero);
+  return mfma_16x16x64_i8(aop, bop, zero);
+}
+
+// Float32 block epilogue of one step: acc += d4 * (d8 * isum - 8 s8) for the
+// lane's four activation rows, (d8, 8 s8) pairs in sa (rows 0, 1) and sb
+// (rows 2, 3).
+__device__ __forceinline__ void q4_mfma_epilogue(const int4_t &isum, float d4,
+                                                 const float4_t &sa, const float4_t &sb,
+                                                 float4_t &acc) {
   acc[0] = fmaf(d4, fmaf(sa[0], (float)isum[0], -sa[1]), acc[0]);
   acc[1] = fmaf(d4, fmaf(sa[2], (float)isum[1], -sa[3]), acc[1]);
   acc[2] = fmaf(d4, fmaf(sb[0], (float)isum[2], -sb[1]), acc[2]);
@@ -313,26 +322,40 @@ __global__ __launch_bounds__(64 * WR * KS) void mmvq_q4_0_mfma_kernel(
   const int ahi = abase + 16 * C::kRpa * ((2 * hb + 1) ^ ablk);
   const uint8_t *zero = smem + C::kZeroOff;
   constexpr int kAStride = 64 * C::kRpa;                   // bytes per step (4 columns)
+  // The chunk's operand reads and integer block dots come first, so the
+  // matrix-core latency overlaps the following reads; the float epilogues
+  // follow.  Off-diagonal lanes read the zero area, whose 1 KB covers every
+  // step's offset, so the choice is made once per chunk.
+  static_assert(kAStride * (S - 1) + 16 <= 1024, "zero area covers the chunk");
   auto consume = [&](const uint8_t *ab) {
+    const uint8_t *blo = live ? ab + alo : zero;
+    const uint8_t *bhi = live ? ab + ahi : zero + 8;
+    int4_t isum[S][T];
 #pragma unroll
     for (int st = 0; st < S; ++st) {
-      const int bl = 2 * st + hb;                          // this lane's block in the chunk
-      const uint8_t *plo = live ? ab + alo + kAStride * st : zero;
-      const uint8_t *phi = live ? ab + ahi + kAStride * st : zero + 8;
-      const uint2_t lo = *reinterpret_cast<const uint2_t *>(plo);
-      const uint2_t hi = *reinterpret_cast<const uint2_t *>(phi);
+      const uint2_t lo = *reinterpret_cast<const uint2_t *>(blo + kAStride * st);
+      const uint2_t hi = *reinterpret_cast<const uint2_t *>(bhi + kAStride * st);
       const int4_t aop = {(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
-      const float4_t *asf = reinterpret_cast<const float4_t *>(ab + C::kAsOff + 64 * bl + 32 * bh);
-      const float4_t sa = asf[0], sb = asf[1];
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         const int r = 16 * t + j, q = r / C::kRpi;
         const int col = (2 * st + hb) ^ (q & C::kSwz);
         const uint2_t wq = *reinterpret_cast<const uint2_t *>(
             wbuf + 1024 * q + 16 * (C::kRpi * col + r % C::kRpi) + 8 * bh);
+        isum[st][t] = q4_mfma_isum(wq, aop);
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < S; ++st) {
+      const int bl = 2 * st + hb;                          // this lane's block in the chunk
+      const float4_t *asf = reinterpret_cast<const float4_t *>(ab + C::kAsOff + 64 * bl + 32 * bh);
+      const float4_t sa = asf[0], sb = asf[1];
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const int r = 16 * t + j;
         const float d4 = f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(
             wbuf + C::kCi * 1024 + 16 * ((bl >> 3) * C::kRows + r) + 2 * (bl & 7)));
-        q4_mfma_step(wq, aop, d4, sa, sb, acc[t]);
+        q4_mfma_epilogue(isum[st][t], d4, sa, sb, acc[t]);
       }
     }
   };
