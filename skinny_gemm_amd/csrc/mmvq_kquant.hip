@@ -312,9 +312,18 @@ static hipError_t launch_q6k_m(const uint8_t *w_ql, const uint8_t *w_qh, const i
 #undef SKINNY_Q6K
 }
 
+// From M = 5 the Q4_0 matrix-core kernel takes Q4_K (its header array has
+// the geometry of the Q4_0 block scales), except mid-width short matrices.
+// Measured on MI355X over the Qwen3-8B projections at M = 8: 4096 x 24576
+// 2.5 -> 3.5, 12288 x 4096 1.9 -> 2.3, 4096 x 4096 1.46 -> 1.54 TB/s on the
+// matrix cores, while 4096 x 6144 (384 tiles) and every shape at M = 4 keep
+// the vector kernel.
 hipError_t launch_mmvq_q4_k(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
                             const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s, int M,
                             float *y, hipStream_t stream) {
+  const int tiles = (N + 15) / 16;
+  if (M >= 5 && (tiles >= 512 || tiles <= 256 || K >= 8192))
+    return launch_mmvq_q4_k_mfma(w_qs, w_hdr, N, K, a_qs, a_d, a_s, M, y, stream);
   switch (M) {
 #define SKINNY_Q4K(MM) \
   case MM: return launch_q4k_m<MM>(w_qs, w_hdr, N, K, a_qs, a_d, a_s, y, stream);

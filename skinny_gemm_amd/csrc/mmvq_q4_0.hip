@@ -221,9 +221,26 @@ __device__ __forceinline__ void q4_mfma_epilogue(const int4_t &isum, float d4,
   acc[3] = fmaf(d4, fmaf(sb[2], (float)isum[3], -sb[3]), acc[3]);
 }
 
+// Q4_K epilogue of one step (KQ): the lane's sub-block scale and min come
+// from its super-block header, acc += d sc d8 isum - dmin m s8, with the
+// staged activation pairs (d8, 8 s8) and dmm8 = dmin m / 8 (exact).
+__device__ __forceinline__ void q4k_mfma_epilogue(const int4_t &isum, float dsc, float dmm8,
+                                                  const float4_t &sa, const float4_t &sb,
+                                                  float4_t &acc) {
+  acc[0] = fmaf(dsc, sa[0] * (float)isum[0], fmaf(-dmm8, sa[1], acc[0]));
+  acc[1] = fmaf(dsc, sa[2] * (float)isum[1], fmaf(-dmm8, sa[3], acc[1]));
+  acc[2] = fmaf(dsc, sb[0] * (float)isum[2], fmaf(-dmm8, sb[1], acc[2]));
+  acc[3] = fmaf(dsc, sb[2] * (float)isum[3], fmaf(-dmm8, sb[3], acc[3]));
+}
+
 // (No __restrict__ on the inputs: the issue fence below must be able to
 // order their loads.)
-template <int T, int WR, int KS, int S, int MP, int D>
+//
+// KQ selects Q4_K weights: the same 4-bit codes, and in place of the block
+// scales w_d a header array of the same geometry (K/16 bytes per row: one
+// 16-byte header {d, dmin, 12 scale/min bytes} per 8 blocks), so staging is
+// unchanged and only the epilogue decodes the lane's sub-block scale and min.
+template <int T, int WR, int KS, int S, int MP, int D, bool KQ = false>
 __global__ __launch_bounds__(64 * WR * KS) void mmvq_q4_0_mfma_kernel(
     const uint8_t *w_qs, const uint16_t *w_d, int N, int K, const int8_t *a_qs,
     const uint16_t *a_d, const uint16_t *a_s, int M, float *y) {
@@ -353,9 +370,21 @@ __global__ __launch_bounds__(64 * WR * KS) void mmvq_q4_0_mfma_kernel(
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         const int r = 16 * t + j;
-        const float d4 = f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(
-            wbuf + C::kCi * 1024 + 16 * ((bl >> 3) * C::kRows + r) + 2 * (bl & 7)));
-        q4_mfma_epilogue(isum[st][t], d4, sa, sb, acc[t]);
+        if constexpr (KQ) {
+          const uint8_t *h = wbuf + C::kCi * 1024 + 16 * ((bl >> 3) * C::kRows + r);
+          const int sj = bl & 7;                           // sub-block in the super-block
+          const uint32_t dd = *reinterpret_cast<const uint32_t *>(h);
+          const uint32_t pb = h[4 + sj], ph = h[12 + (sj >> 1)];
+          const uint32_t sc = pb & 63u;
+          const uint32_t mn = (pb >> 6) | (((ph >> (4 * (sj & 1))) & 15u) << 2);
+          const float dsc = f16_bits_to_f32((uint16_t)(dd & 0xFFFFu)) * (float)sc;
+          const float dmm8 = f16_bits_to_f32((uint16_t)(dd >> 16)) * (float)mn * 0.125f;
+          q4k_mfma_epilogue(isum[st][t], dsc, dmm8, sa, sb, acc[t]);
+        } else {
+          const float d4 = f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(
+              wbuf + C::kCi * 1024 + 16 * ((bl >> 3) * C::kRows + r) + 2 * (bl & 7)));
+          q4_mfma_epilogue(isum[st][t], d4, sa, sb, acc[t]);
+        }
       }
     }
   };
@@ -421,18 +450,18 @@ __global__ __launch_bounds__(64 * WR * KS) void mmvq_q4_0_mfma_kernel(
   }
 }
 
-template <int T, int WR, int KS, int S, int MP, int D>
+template <int T, int WR, int KS, int S, int MP, int D, bool KQ>
 static hipError_t launch_mfma_cfg(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                                   const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
                                   int M, float *y, hipStream_t stream) {
   using C = q4::Cfg<T, WR, KS, S, MP>;
   if (K % (64 * S) != 0) return hipErrorInvalidValue;   // chunks must tile K
   static const hipError_t lds_ok =
-      allow_lds((const void *)mmvq_q4_0_mfma_kernel<T, WR, KS, S, MP, D>, C::kLds);
+      allow_lds((const void *)mmvq_q4_0_mfma_kernel<T, WR, KS, S, MP, D, KQ>, C::kLds);
   if (lds_ok != hipSuccess) return lds_ok;
   const int rows = C::kRows * WR;
   const int blocks = (N + rows - 1) / rows;
-  hipLaunchKernelGGL((mmvq_q4_0_mfma_kernel<T, WR, KS, S, MP, D>), dim3(blocks),
+  hipLaunchKernelGGL((mmvq_q4_0_mfma_kernel<T, WR, KS, S, MP, D, KQ>), dim3(blocks),
                      dim3(64 * C::kWaves), C::kLds, stream, w_qs, w_d, N, K, a_qs, a_d, a_s,
                      M, y);
   return hipGetLastError();
@@ -443,14 +472,14 @@ static hipError_t launch_mfma_cfg(const uint8_t *w_qs, const uint16_t *w_d, int 
 // split K instead so that enough waves stream (measured on MI355X at M = 4
 // and 8 over the Llama-2-7B shapes: 2000 tiles four-way sharing, 1376 tiles
 // two-way, 768 tiles a two-way K split, 256 tiles an eight-way split).
-template <int MP>
+template <int MP, bool KQ>
 static hipError_t launch_mfma_mp(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                                  const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
                                  int M, float *y, hipStream_t stream) {
   const int tiles = (N + 15) / 16;
   const bool s8 = K % 512 == 0;
 #define SKINNY_Q4(T, WR, KS, S) \
-  return launch_mfma_cfg<T, WR, KS, S, MP, 1>(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream)
+  return launch_mfma_cfg<T, WR, KS, S, MP, 1, KQ>(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream)
   if (tiles >= 1800) {
     if (s8) SKINNY_Q4(1, 4, 1, 8);
     SKINNY_Q4(1, 4, 1, 4);
@@ -467,11 +496,12 @@ static hipError_t launch_mfma_mp(const uint8_t *w_qs, const uint16_t *w_d, int N
 #undef SKINNY_Q4
 }
 
+template <bool KQ>
 static hipError_t launch_mfma(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                               const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
                               int M, float *y, hipStream_t stream) {
-  if (M <= 4) return launch_mfma_mp<4>(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream);
-  return launch_mfma_mp<8>(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream);
+  if (M <= 4) return launch_mfma_mp<4, KQ>(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream);
+  return launch_mfma_mp<8, KQ>(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream);
 }
 
 // Vector kernel with the activation rows staged in LDS (M <= 2, one round of
@@ -715,7 +745,7 @@ hipError_t launch_mmvq_q4_0(const uint8_t *w_qs, const uint16_t *w_d, int N, int
                             int M, float *y, hipStream_t stream) {
   const bool small = M <= kQ4VectorMaxM && N < 8192 && K < 8192;
   if (M >= kQ4MfmaMinM && K % 256 == 0 && !small)
-    return launch_mfma(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream);
+    return launch_mfma<false>(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream);
   switch (M) {
     case 1: return launch_m<1>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
     case 2: return launch_m<2>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
@@ -732,6 +762,15 @@ hipError_t launch_mmvq_q4_0_f32act(const uint8_t *w_qs, const uint16_t *w_d, int
                                    const float *x, int M, float *y, hipStream_t stream) {
   if (M == 1) return launch_lds<1, true>(w_qs, w_d, N, K, nullptr, nullptr, nullptr, x, y, stream);
   return launch_lds<2, true>(w_qs, w_d, N, K, nullptr, nullptr, nullptr, x, y, stream);
+}
+
+// Q4_K weights on the matrix-core kernel (3 <= M <= 8, K % 256 == 0): the
+// super-block headers take the place of the Q4_0 block scales.
+hipError_t launch_mmvq_q4_k_mfma(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
+                                 const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
+                                 int M, float *y, hipStream_t stream) {
+  return launch_mfma<true>(w_qs, reinterpret_cast<const uint16_t *>(w_hdr), N, K, a_qs, a_d, a_s,
+                           M, y, stream);
 }
 
 }  // namespace skinny

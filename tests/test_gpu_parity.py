@@ -305,7 +305,8 @@ def run_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d):
 
 
 KQ_SHAPES = [(1, 256), (4096 + 37, 256), (4099, 1280), (257, 12288), (1000, 4096), (63, 16384),
-             (16384 + 9, 512)]   # last: the four-row wide-matrix shapes
+             (16384 + 9, 512),   # four-row vector shapes; two waves share activations (M >= 3)
+             (28800 + 5, 512)]   # four waves share activations (Q4_K, M >= 3)
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
