@@ -504,8 +504,8 @@ static hipError_t launch_mfma(const uint8_t *w_qs, const uint16_t *w_d, int N, i
   return launch_mfma_mp<8, KQ>(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream);
 }
 
-// Vector kernel with the activation rows staged in LDS (M <= 2, one round of
-// U blocks per lane, K <= 2048 U).  A workgroup of W waves (two weight rows
+// Vector kernel with the activation rows staged in LDS (any M <= 8, one round
+// of U blocks per lane, K <= 2048 U).  A workgroup of W waves (two weight rows
 // each) reads the Q8_1 activation rows once -- or, FUSED, reads the float32
 // rows and quantizes them into LDS itself with the same block arithmetic as
 // quantize_act_q8_1 -- so activation bytes per weight byte drop W-fold
@@ -516,24 +516,24 @@ static hipError_t launch_mfma(const uint8_t *w_qs, const uint16_t *w_d, int N, i
 // LDS: codes int8 [M][K] | d8 float [M][K/32] | 8 s8 float [M][K/32].
 // The dot is exactly the plain kernel's (same blocks per lane, same order,
 // same reduction), so the result equals mmvq_q4_0 on the same Q8_1 input.
-template <int M, int U, bool FUSED>
+template <int M, int U, bool FUSED, int W = 8>
 struct LdsAct {
-  static constexpr int kW = 8;                                     // waves per workgroup
+  static constexpr int kW = W;                                     // waves per workgroup
   static constexpr int kMaxNb = kWave * U;                         // blocks per row (max)
   // activation 16-byte loads per lane: plain = codes + d + s pieces;
   // fused = two per 8-element group
+  // (plain: M * K / 32 must be a multiple of 8, checked by the launcher)
   static constexpr int kPieces = FUSED ? (M * kMaxNb * 4) : (M * kMaxNb * 2 + M * kMaxNb / 4);
   static constexpr int kA = (kPieces + kW * kWave - 1) / (kW * kWave);
 };
 
 // (No __restrict__ on the inputs: the issue fence below must be able to
 // keep the activation loads ahead of the weight loads.)
-template <int M, int U, bool FUSED>
-__global__ __launch_bounds__(512) void mmvq_q4_0_lds_kernel(
+template <int M, int U, bool FUSED, int W = 8>
+__global__ __launch_bounds__(64 * W) void mmvq_q4_0_lds_kernel(
     const uint8_t *w_qs, const uint16_t *w_d, int N, int K, const int8_t *a_qs,
     const uint16_t *a_d, const uint16_t *a_s, const float *x, float *y) {
-  using P = LdsAct<M, U, FUSED>;
-  static_assert(P::kW * kWave == 512, "launch bounds");
+  using P = LdsAct<M, U, FUSED, W>;
   constexpr int R = 2;
   extern __shared__ uint4_t smem4[];
   int8_t *lq = reinterpret_cast<int8_t *>(smem4);
@@ -675,15 +675,17 @@ __global__ __launch_bounds__(512) void mmvq_q4_0_lds_kernel(
   }
 }
 
-template <int M, int U, bool FUSED>
+template <int M, int U, bool FUSED, int W = 8>
 static hipError_t launch_lds_u(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                                const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
                                const float *x, float *y, hipStream_t stream) {
-  using P = LdsAct<M, U, FUSED>;
+  using P = LdsAct<M, U, FUSED, W>;
   const int rows = 2 * P::kW;
   const int blocks = (N + rows - 1) / rows;
   const size_t lds = (size_t)M * K + 8 * (size_t)M * (K >> 5);
-  hipLaunchKernelGGL((mmvq_q4_0_lds_kernel<M, U, FUSED>), dim3(blocks), dim3(64 * P::kW), lds,
+  const hipError_t lds_ok = allow_lds((const void *)mmvq_q4_0_lds_kernel<M, U, FUSED, W>, (int)lds);
+  if (lds_ok != hipSuccess) return lds_ok;
+  hipLaunchKernelGGL((mmvq_q4_0_lds_kernel<M, U, FUSED, W>), dim3(blocks), dim3(64 * P::kW), lds,
                      stream, w_qs, w_d, N, K, a_qs, a_d, a_s, x, y);
   return hipGetLastError();
 }
@@ -693,12 +695,12 @@ static hipError_t launch_lds_u(const uint8_t *w_qs, const uint16_t *w_d, int N, 
 constexpr int kLdsMaxK = 2048 * 6;
 static_assert(kLdsMaxK == SKINNY_MAX_K_F32ACT, "documented limit");
 
-template <int M, bool FUSED>
+template <int M, bool FUSED, int W = 8>
 static hipError_t launch_lds(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                              const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
                              const float *x, float *y, hipStream_t stream) {
   const int per_lane = ((K >> 5) + kWave - 1) / kWave;
-#define SKINNY_LDS(U) return launch_lds_u<M, U, FUSED>(w_qs, w_d, N, K, a_qs, a_d, a_s, x, y, stream)
+#define SKINNY_LDS(U) return launch_lds_u<M, U, FUSED, W>(w_qs, w_d, N, K, a_qs, a_d, a_s, x, y, stream)
   if (per_lane <= 2) SKINNY_LDS(2);
   if (per_lane <= 3) SKINNY_LDS(3);
   if (per_lane <= 4) SKINNY_LDS(4);
@@ -740,9 +742,39 @@ static hipError_t launch_m(const uint8_t *w_qs, const uint16_t *w_d, int N, int 
   }
 }
 
+// Plain LDS-staged vector kernel for 3 <= M <= 8: four waves per workgroup
+// on narrow matrices, eight otherwise.
+template <int M>
+static hipError_t launch_lds_plain(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
+                                   const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
+                                   float *y, hipStream_t stream) {
+  if (N <= 4096 && K <= 4096)
+    return launch_lds<M, false, 4>(w_qs, w_d, N, K, a_qs, a_d, a_s, nullptr, y, stream);
+  return launch_lds<M, false, 8>(w_qs, w_d, N, K, a_qs, a_d, a_s, nullptr, y, stream);
+}
+
 hipError_t launch_mmvq_q4_0(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                             const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
                             int M, float *y, hipStream_t stream) {
+  // M = 3..5, and narrow matrices at M = 6..8: the activation rows staged in
+  // LDS once per workgroup beat the matrix cores (measured on MI355X over the
+  // Llama-2-7B shapes: 4096 x 22016 at M = 3 15.0 -> 10.8 us, at M = 4 15.2
+  // -> 12.9 us, at M = 5 14.2 -> 13.1 us; 4096 x 4096 at M = 8 6.3 -> 5.5
+  // us; wider M on wider matrices stays on the matrix cores).
+  // The plain staging copies the Q8_1 scales in 16-byte pieces of 8, so it
+  // needs M * K / 32 to be a multiple of 8.
+  const bool lds_ok = K <= kLdsMaxK && (M * (K >> 5)) % 8 == 0;
+  const bool narrow = N <= 4096 && K <= 4096;
+  if (M >= 3 && lds_ok && (M <= 5 || narrow)) {
+    switch (M) {
+      case 3: return launch_lds_plain<3>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+      case 4: return launch_lds_plain<4>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+      case 5: return launch_lds_plain<5>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+      case 6: return launch_lds_plain<6>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+      case 7: return launch_lds_plain<7>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+      default: return launch_lds_plain<8>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+    }
+  }
   const bool small = M <= kQ4VectorMaxM && N < 8192 && K < 8192;
   if (M >= kQ4MfmaMinM && K % 256 == 0 && !small)
     return launch_mfma<false>(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream);
@@ -750,7 +782,7 @@ hipError_t launch_mmvq_q4_0(const uint8_t *w_qs, const uint16_t *w_d, int N, int
   // wide matrices staging them in LDS once per workgroup pays (measured on
   // MI355X: 4096 x 22016 10.8 -> 10.2 us, 4096 x 32000 15.0 -> 13.4 us); at
   // M = 1 and on narrow matrices the direct kernel is as fast or faster.
-  if (M == 2 && N >= 8192 && K <= kLdsMaxK)
+  if (M == 2 && N >= 8192 && lds_ok)
     return launch_lds<2, false>(w_qs, w_d, N, K, a_qs, a_d, a_s, nullptr, y, stream);
   switch (M) {
     case 1: return launch_m<1>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);

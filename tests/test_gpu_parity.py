@@ -166,6 +166,19 @@ def run_q4(w_qs, w_d, a_qs, a_d, a_s):
                                  # four waves sharing one activation chunk, ragged
                                  (30000, 1024)])
 def test_mmvq_q4_0_vs_oracle(M, N, K):
+    _check_q4_0(M, N, K)
+
+
+@pytest.mark.parametrize("M", [2, 3, 5, 8])
+@pytest.mark.parametrize("N,K", [(9000, 1376),      # M * K / 32 not a multiple of 8
+                                 (9000, 1280),      # ... a multiple of 8 for every M
+                                 (4000, 288), (4096, 4096), (10000, 12288), (2000, 12320)])
+def test_mmvq_q4_0_staged_activation_shapes(M, N, K):
+    # the shapes that decide between the LDS-staged and the other kernels
+    _check_q4_0(M, N, K)
+
+
+def _check_q4_0(M, N, K):
     w_qs, w_d = inputs.q4_0_weights(N, K, 7 * N + K)
     x = inputs.normal_f32(M, K, 3 * M + K)
     a_qs, a_d, a_s = oracle.quantize_q8_1(x)
