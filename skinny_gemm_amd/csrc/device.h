@@ -213,6 +213,54 @@ __device__ __forceinline__ void wg_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Binary16 activation rows staged in LDS for the vector kernels: rows [M][K]
+// as 16-byte pieces, P pieces per lane chunk; piece q of chunk c sits at
+// slot P c + (q ^ ((c / (16 / P)) % P)) of its row, so the 16 lanes of one
+// LDS read pass (consecutive chunks, same q) hit 16 distinct 16-byte bank
+// groups, and 16 consecutive pieces (one store pass) stay distinct too.
+template <int P>
+__device__ __forceinline__ int act_slot(int c, int q) {
+  return P * c + (q ^ ((c / (16 / P)) % P));
+}
+
+// First batch of the staging: A pieces per thread (of tot = M K / 8, piece
+// p = thread + NT a), issued before the weight loads so that waiting for
+// them does not wait for the weights; pieces past the end repeat the last.
+template <int A, int NT>
+__device__ __forceinline__ void act_issue(const uint16_t *x, int tot, uint4_t (&av)[A]) {
+#pragma unroll
+  for (int a = 0; a < A; ++a)
+    av[a] = load16(x + 8 * (size_t)min((int)threadIdx.x + NT * a, tot - 1));
+}
+
+// Stores the first batch into LDS (straight-line, so its wait covers only
+// the activation loads), then loads and stores any remaining pieces in
+// batches of A; np = K / 8 pieces per row.
+template <int P, int A, int NT>
+__device__ __forceinline__ void act_store_batch(int p0, int tot, int np, uint4_t *xs,
+                                                const uint4_t (&av)[A]) {
+#pragma unroll
+  for (int a = 0; a < A; ++a) {
+    const int p = p0 + (int)threadIdx.x + NT * a;
+    if (p < tot) {
+      const int m = p / np, pr = p - m * np;
+      xs[m * np + act_slot<P>(pr / P, pr % P)] = av[a];
+    }
+  }
+}
+
+template <int P, int A, int NT>
+__device__ __forceinline__ void act_stage(const uint16_t *x, int tot, int np, uint4_t *xs,
+                                          uint4_t (&av)[A]) {
+  act_store_batch<P, A, NT>(0, tot, np, xs, av);
+  for (int p0 = NT * A; p0 < tot; p0 += NT * A) {
+#pragma unroll
+    for (int a = 0; a < A; ++a)
+      av[a] = load16(x + 8 * (size_t)min(p0 + (int)threadIdx.x + NT * a, tot - 1));
+    act_store_batch<P, A, NT>(p0, tot, np, xs, av);
+  }
+}
+
 __device__ __forceinline__ half2_t h2_bcast(float f) {
   const _Float16 h = (_Float16)f;
   return half2_t{h, h};

@@ -447,6 +447,99 @@ static hipError_t launch_mfma(const uint8_t *w, const float *cs, int N, int K, c
   }
 }
 
+// Vector kernel with the activation rows staged in LDS (M <= 4, M K <= 80 K
+// elements).  The plain vector kernel reads each lane's activation bytes
+// through the vector memory path once per wave, M bytes per weight byte at
+// two rows per wave, and that path bounds it before HBM does.  Here a
+// workgroup of W waves loads the rows once (issued ahead of the first
+// weight loads), stores them as swizzled 16-byte pieces, one barrier, and
+// every lane reads its chunk's activations from LDS.  Each wave takes R
+// rows, one 16-element chunk per lane per round, the next round's weights
+// in flight under the current one's arithmetic.  Decode and dot order per
+// row are the plain kernel's.
+template <int M, int R, int W, int A>
+__global__ __launch_bounds__(64 * W) void gemv_fp8_lds_kernel(
+    const uint8_t *w, const float *cs, int N, int K, const uint16_t *x, uint16_t *y) {
+  extern __shared__ uint4_t xs[];
+  const int lane = threadIdx.x & 63;
+  const int n0 = (blockIdx.x * W + (threadIdx.x >> 6)) * R;
+  const int nc = K >> 4;                    // 16-element chunks per row
+  const int np = K >> 3;                    // 16-byte activation pieces per row
+  const int tot = M * np;
+  uint4_t av[A];
+  act_issue<A, 64 * W>(x, tot, av);
+
+  const uint8_t *wrow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) wrow[r] = w + (size_t)min(n0 + r, N - 1) * (size_t)K;
+  struct Round {
+    uint4_t wq[R];
+  };
+  auto load = [&](int c, Round &rd) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) rd.wq[r] = load16_nt(wrow[r] + 16 * c);
+  };
+  Round r0, r1;
+  load(min(lane, nc - 1), r0);
+  issue_fence();
+  act_stage<2, A, 64 * W>(x, tot, np, xs, av);
+  wg_barrier();
+  if (n0 >= N) return;
+
+  float acc[R][M];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+  auto compute = [&](int c, const Round &rd) {
+    uint4_t xv[M][2];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) xv[m][q] = xs[m * np + act_slot<2>(c, q)];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      // word i holds elements 4i..4i+3: pair (4i, 4i+1) and (4i+2, 4i+3)
+      uint32_t wh[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wh[2 * i + 0] = __builtin_bit_cast(uint32_t, e4m3x2_to_h2<false>(rd.wq[r][i]));
+        wh[2 * i + 1] = __builtin_bit_cast(uint32_t, e4m3x2_to_h2<true>(rd.wq[r][i]));
+      }
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float a = acc[r][m];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) a = dot2_f16(wh[p], xv[m][p >> 2][p & 3], a);
+        acc[r][m] = a;
+      }
+    }
+  };
+  // chunks c = lane, lane + 64, ...: the two round buffers alternate
+  for (int c = lane; c < nc; c += 2 * kWave) {
+    if (c + kWave < nc) load(c + kWave, r1);
+    issue_fence();
+    compute(c, r0);
+    if (c + kWave >= nc) break;
+    if (c + 2 * kWave < nc) load(c + 2 * kWave, r0);
+    issue_fence();
+    compute(c + kWave, r1);
+  }
+
+  constexpr int V = next_pow2_f(R * M);
+  float v[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) v[i] = (i < R * M) ? acc[i / M][i % M] : 0.0f;
+  const float total = wave_reduce_transpose<V>(v, lane);
+  constexpr int SHIFT = 6 - Log2<V>::value;
+  const int idx = lane >> SHIFT;
+  if ((lane & ((1 << SHIFT) - 1)) == 0 && idx < R * M) {
+    const int r = idx / M, m = idx % M;
+    const int n = n0 + r;
+    if (n < N) y[(size_t)m * N + n] = f32_to_f16_bits(total * cs[n]);
+  }
+}
+
 template <int M, int R, int U>
 static hipError_t launch_mru(const uint8_t *w, const float *cs, int N, int K, const uint16_t *x,
                              uint16_t *y, hipStream_t stream) {
@@ -476,6 +569,37 @@ static hipError_t launch_m(const uint8_t *w, const float *cs, int N, int K, cons
   }
 }
 
+// Staged-activation vector kernel (M <= 4): three rows per wave, eight
+// waves per workgroup (measured on MI355X over K 5120 and 17408, N 5120 to
+// 34816: 17408 x 5120 at M = 1 18.3 -> 16.0 us, 5120 x 34816 at M = 2 33.6
+// -> 28.3 us; at M = 3 and 4 on par with or ahead of the matrix cores).
+constexpr int kF8LdsMaxM = 4;
+constexpr int kF8LdsMaxMK = 80 * 1024;      // M K binary16 activations in LDS
+
+template <int M, int A>
+static hipError_t launch_lds_a(const uint8_t *w, const float *cs, int N, int K,
+                               const uint16_t *x, uint16_t *y, hipStream_t stream) {
+  constexpr int R = 3, W = 8;
+  const int lds = M * K * 2;
+  static const hipError_t lds_ok =
+      allow_lds((const void *)gemv_fp8_lds_kernel<M, R, W, A>, 2 * kF8LdsMaxMK);
+  if (lds_ok != hipSuccess) return lds_ok;
+  const int rows = R * W;
+  hipLaunchKernelGGL((gemv_fp8_lds_kernel<M, R, W, A>), dim3((N + rows - 1) / rows),
+                     dim3(64 * W), lds, stream, w, cs, N, K, x, y);
+  return hipGetLastError();
+}
+
+template <int M>
+static hipError_t launch_lds(const uint8_t *w, const float *cs, int N, int K,
+                             const uint16_t *x, uint16_t *y, hipStream_t stream) {
+  const int per_thread = (M * (K >> 3) + 511) / 512;   // first staging batch
+  if (per_thread <= 2) return launch_lds_a<M, 2>(w, cs, N, K, x, y, stream);
+  if (per_thread <= 4) return launch_lds_a<M, 4>(w, cs, N, K, x, y, stream);
+  if (per_thread <= 8) return launch_lds_a<M, 8>(w, cs, N, K, x, y, stream);
+  return launch_lds_a<M, 12>(w, cs, N, K, x, y, stream);
+}
+
 // Vector kernel for 1 <= M <= 8 rows.
 static hipError_t launch_vector(const uint8_t *w, const float *cs, int N, int K,
                                 const uint16_t *x, int M, uint16_t *y, hipStream_t stream) {
@@ -491,11 +615,21 @@ static hipError_t launch_vector(const uint8_t *w, const float *cs, int N, int K,
   }
 }
 
-// The matrix-core kernel takes every M >= 3 in one weight pass when K is a
-// whole number of 256-element chunks.  Otherwise the vector kernel serves
-// up to 8 rows per pass over the weights: rows 1..8, 9..16, ...
+// M <= 4 takes the staged-activation vector kernel while the rows fit in
+// LDS.  The matrix-core kernel takes every other M >= 3 in one weight pass
+// when K is a whole number of 256-element chunks.  Otherwise the plain
+// vector kernel serves up to 8 rows per pass over the weights: rows 1..8,
+// 9..16, ...
 hipError_t launch_gemv_fp8(const uint8_t *w, const float *cs, int N, int K, const uint16_t *x,
                            int M, uint16_t *y, hipStream_t stream) {
+  if (M <= kF8LdsMaxM && M * K <= kF8LdsMaxMK) {
+    switch (M) {
+      case 1: return launch_lds<1>(w, cs, N, K, x, y, stream);
+      case 2: return launch_lds<2>(w, cs, N, K, x, y, stream);
+      case 3: return launch_lds<3>(w, cs, N, K, x, y, stream);
+      default: return launch_lds<4>(w, cs, N, K, x, y, stream);
+    }
+  }
   if (M >= kFp8MfmaMinM && K % 256 == 0) return launch_mfma(w, cs, N, K, x, M, y, stream);
   for (int m0 = 0; m0 < M; m0 += 8) {
     const hipError_t e = launch_vector(w, cs, N, K, x + (size_t)m0 * K, min(8, M - m0),

@@ -129,6 +129,114 @@ __global__ __launch_bounds__(256) void gemv_nvfp4_kernel(
   }
 }
 
+// Vector kernel with the activation rows staged in LDS (M <= 2, M K <= 80 K
+// elements).  The plain vector kernel reads each lane's 64 activation bytes
+// per chunk through the vector memory path once per wave, 1.8 bytes per
+// weight byte at two rows per wave, and that path, not HBM, bounds it on
+// wide matrices.  Here a workgroup of W waves loads the rows once (issued
+// ahead of the first weight loads), stores them as swizzled 16-byte pieces,
+// one barrier, and every lane reads its chunk's activations from LDS.  Each
+// wave takes R rows, one 32-element chunk per lane per round, the next
+// round's weights in flight under the current one's arithmetic.  Decode,
+// group dots and flushes are the plain kernel's, in the same order per row.
+template <int M, int R, int W, int A>
+__global__ __launch_bounds__(64 * W) void gemv_nvfp4_lds_kernel(
+    const uint8_t *codes, const uint8_t *scales, float g, int N, int K, const uint16_t *x,
+    uint16_t *y) {
+  extern __shared__ uint4_t xs[];
+  const int lane = threadIdx.x & 63;
+  const int n0 = (blockIdx.x * W + (threadIdx.x >> 6)) * R;
+  const int nc = K >> 5;                    // 32-element chunks per row
+  const int np = K >> 3;                    // 16-byte activation pieces per row
+  const int tot = M * np;
+  uint4_t av[A];
+  act_issue<A, 64 * W>(x, tot, av);
+
+  const uint8_t *crow[R];
+  const uint16_t *srow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int n = min(n0 + r, N - 1);
+    crow[r] = codes + (size_t)n * (size_t)(K >> 1);
+    srow[r] = reinterpret_cast<const uint16_t *>(scales + (size_t)n * (size_t)(K >> 4));
+  }
+  struct Round {
+    uint4_t wq[R];
+    uint32_t sc[R];
+  };
+  auto load = [&](int c, Round &rd) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      rd.wq[r] = load16_nt(crow[r] + 16 * c);
+      rd.sc[r] = load_u16_nt(srow[r] + c);
+    }
+  };
+  Round r0, r1;
+  load(min(lane, nc - 1), r0);
+  issue_fence();
+  act_stage<4, A, 64 * W>(x, tot, np, xs, av);
+  wg_barrier();
+  if (n0 >= N) return;
+
+  float acc[R][M];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+  auto compute = [&](int c, const Round &rd) {
+    uint4_t xv[M][4];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xv[m][q] = xs[m * np + act_slot<4>(c, q)];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      uint32_t wh[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wh[4 * i + 0] = __builtin_bit_cast(uint32_t, e2m1x2_to_h2<0>(rd.wq[r][i]));
+        wh[4 * i + 1] = __builtin_bit_cast(uint32_t, e2m1x2_to_h2<1>(rd.wq[r][i]));
+        wh[4 * i + 2] = __builtin_bit_cast(uint32_t, e2m1x2_to_h2<2>(rd.wq[r][i]));
+        wh[4 * i + 3] = __builtin_bit_cast(uint32_t, e2m1x2_to_h2<3>(rd.wq[r][i]));
+      }
+      const float s0 = e4m3_to_f32<0>(rd.sc[r]) * g;
+      const float s1 = e4m3_to_f32<1>(rd.sc[r]) * g;
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+        for (int p = 0; p < 8; ++p) p0 = dot2_f16(wh[p], xv[m][p >> 2][p & 3], p0);
+#pragma unroll
+        for (int p = 8; p < 16; ++p) p1 = dot2_f16(wh[p], xv[m][p >> 2][p & 3], p1);
+        acc[r][m] = fmaf(p1, s1, fmaf(p0, s0, acc[r][m]));
+      }
+    }
+  };
+  // chunks c = lane, lane + 64, ...: the two round buffers alternate
+  for (int c = lane; c < nc; c += 2 * kWave) {
+    if (c + kWave < nc) load(c + kWave, r1);
+    issue_fence();
+    compute(c, r0);
+    if (c + kWave >= nc) break;
+    if (c + 2 * kWave < nc) load(c + 2 * kWave, r0);
+    issue_fence();
+    compute(c + kWave, r1);
+  }
+
+  constexpr int V = next_pow2_n(R * M);
+  float v[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) v[i] = (i < R * M) ? acc[i / M][i % M] : 0.0f;
+  const float total = wave_reduce_transpose<V>(v, lane);
+  constexpr int SHIFT = 6 - Log2<V>::value;
+  const int idx = lane >> SHIFT;
+  if ((lane & ((1 << SHIFT) - 1)) == 0 && idx < R * M) {
+    const int r = idx / M, m = idx % M;
+    const int n = n0 + r;
+    if (n < N) y[(size_t)m * N + n] = f32_to_f16_bits(total);
+  }
+}
+
 // One 128-K step of a 16-row tile: decode the lane's 16 code bytes with its
 // two group scales into four A operands and accumulate against the four B
 // operands xv.
@@ -443,6 +551,38 @@ static hipError_t launch_m(const uint8_t *codes, const uint8_t *scales, float g,
   }
 }
 
+// Staged-activation vector kernel (M <= 2): three rows per wave, four waves
+// per workgroup at M = 1 and eight at M = 2 (measured on MI355X over K 5120
+// and 17408, N 5120 to 34816: 5120 x 34816 at M = 1 24.7 -> 19.0 us, at M =
+// 2 28.3 -> 24.9 us against the matrix cores; 17408 x 5120 at M = 2 17.3 ->
+// 14.1 us).
+constexpr int kNvLdsMaxMK = 80 * 1024;      // M K binary16 activations in LDS
+
+template <int M, int W, int A>
+static hipError_t launch_lds_a(const uint8_t *codes, const uint8_t *scales, float g, int N,
+                               int K, const uint16_t *x, uint16_t *y, hipStream_t stream) {
+  constexpr int R = 3;
+  const int lds = M * K * 2;
+  static const hipError_t lds_ok =
+      allow_lds((const void *)gemv_nvfp4_lds_kernel<M, R, W, A>, 2 * kNvLdsMaxMK);
+  if (lds_ok != hipSuccess) return lds_ok;
+  const int rows = R * W;
+  hipLaunchKernelGGL((gemv_nvfp4_lds_kernel<M, R, W, A>), dim3((N + rows - 1) / rows),
+                     dim3(64 * W), lds, stream, codes, scales, g, N, K, x, y);
+  return hipGetLastError();
+}
+
+template <int M>
+static hipError_t launch_lds(const uint8_t *codes, const uint8_t *scales, float g, int N, int K,
+                             const uint16_t *x, uint16_t *y, hipStream_t stream) {
+  constexpr int W = M == 1 ? 4 : 8;
+  const int per_thread = (M * (K >> 3) + 64 * W - 1) / (64 * W);   // first staging batch
+  if (per_thread <= 2) return launch_lds_a<M, W, 2>(codes, scales, g, N, K, x, y, stream);
+  if (per_thread <= 4) return launch_lds_a<M, W, 4>(codes, scales, g, N, K, x, y, stream);
+  if (per_thread <= 8) return launch_lds_a<M, W, 8>(codes, scales, g, N, K, x, y, stream);
+  return launch_lds_a<M, W, 12>(codes, scales, g, N, K, x, y, stream);
+}
+
 // Vector kernel for 1 <= M <= 8 rows.
 static hipError_t launch_vector(const uint8_t *codes, const uint8_t *scales, float g, int N,
                                 int K, const uint16_t *x, int M, uint16_t *y,
@@ -459,16 +599,17 @@ static hipError_t launch_vector(const uint8_t *codes, const uint8_t *scales, flo
   }
 }
 
-// The matrix-core kernel takes every M >= 3 in one weight pass when K is a
-// whole number of 256-element chunks.  Otherwise the vector kernel serves
-// up to 8 rows per pass: rows 9..M take a second pass over the weights.
+// M <= 2 takes the staged-activation vector kernel while the rows fit in
+// LDS.  The matrix-core kernel takes every M >= 3 in one weight pass when K
+// is a whole number of 256-element chunks.  Otherwise the plain vector
+// kernel serves up to 8 rows per pass: rows 9..M take a second pass.
 hipError_t launch_gemv_nvfp4(const uint8_t *codes, const uint8_t *scales, float g, int N, int K,
                              const uint16_t *x, int M, uint16_t *y, hipStream_t stream) {
-  // M = 2 also goes to the matrix cores on wide or long matrices (measured
-  // on MI355X: 5120 x 10240 10.6 -> 9.2 us, 17408 x 5120 23.5 -> 17.3 us);
-  // 5120 x 5120 keeps the vector kernel (7.1 vs 7.6 us).
-  const bool mfma2 = M == 2 && ((N + 15) / 16 >= 512 || K >= 8192);
-  if ((M >= kNvfp4MfmaMinM || mfma2) && K % 256 == 0)
+  if (M <= 2 && M * K <= kNvLdsMaxMK) {
+    if (M == 1) return launch_lds<1>(codes, scales, g, N, K, x, y, stream);
+    return launch_lds<2>(codes, scales, g, N, K, x, y, stream);
+  }
+  if (M >= kNvfp4MfmaMinM && K % 256 == 0)
     return launch_mfma(codes, scales, g, N, K, x, M, y, stream);
   if (M <= 8) return launch_vector(codes, scales, g, N, K, x, M, y, stream);
   const hipError_t e = launch_vector(codes, scales, g, N, K, x, 8, y, stream);

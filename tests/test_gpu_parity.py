@@ -432,9 +432,11 @@ def test_gemv_nvfp4_every_code_and_scale_bit_exact():
         for m in range(8):
             x[m, base + m] = 1.0
         xb = x.view(np.uint16)
-        y = run_nvfp4(codes, scales, 1.0, xb)
-        _, want = oracle.gemv_nvfp4_w4a16(codes, scales, 1.0, xb)
-        assert np.array_equal(y, want), base
+        # M = 1 and 2: the staged-activation kernel; M = 8: the plain one
+        for M in (1, 2, 8):
+            y = run_nvfp4(codes, scales, 1.0, xb[:M])
+            _, want = oracle.gemv_nvfp4_w4a16(codes, scales, 1.0, xb[:M])
+            assert np.array_equal(y, want), (base, M)
 
 
 def test_gemv_nvfp4_outliers():
@@ -545,9 +547,11 @@ def test_gemv_fp8_every_code_bit_exact():
         x[m, m] = 1.0
         x[m, m + 8] = 1.0
     xb = x.view(np.uint16)
-    y = run_fp8(w, cs, xb)
-    _, want = oracle.gemv_fp8_w8a16(w, cs, xb)
-    assert np.array_equal(y, want)
+    # M <= 4: the staged-activation kernel; M = 8: the plain one
+    for M in (1, 2, 3, 4, 8):
+        y = run_fp8(w, cs, xb[:M])
+        _, want = oracle.gemv_fp8_w8a16(w, cs, xb[:M])
+        assert np.array_equal(y, want), M
 
 
 def test_gemv_fp8_sixteen_rows_bit_exact():
@@ -568,6 +572,27 @@ def test_gemv_fp8_sixteen_rows_bit_exact():
     _, want = oracle.gemv_fp8_w8a16(w, cs, xb)
     assert np.array_equal(y, want)
     assert np.count_nonzero(f16(want)) > 200
+
+
+@pytest.mark.parametrize("fmt,M,K", [
+    # activations staged in LDS up to M K = 80 K elements: at the limit the
+    # staging takes several batches per thread; just past it, the plain kernel
+    ("nvfp4", 1, 81920), ("nvfp4", 1, 81952), ("nvfp4", 2, 40960), ("nvfp4", 2, 40992),
+    ("fp8", 1, 81920), ("fp8", 3, 27296), ("fp8", 4, 20480), ("fp8", 4, 20496)])
+@pytest.mark.parametrize("N", [5, 37])
+def test_staged_activation_limits(fmt, M, K, N):
+    x = inputs.normal_f16_bits(M, K, 7 * M + N, std=0.25)
+    if fmt == "nvfp4":
+        codes, scales, g = inputs.nvfp4_weights(N, K, 11 * N + K)
+        y = run_nvfp4(codes, scales, g, x)
+        y_acc, _ = oracle.gemv_nvfp4_w4a16(codes, scales, g, x)
+        mag = nvfp4_mag(codes, scales, g, x)
+    else:
+        w, cs = inputs.fp8_weights(N, K, 13 * N + K)
+        y = run_fp8(w, cs, x)
+        y_acc, _ = oracle.gemv_fp8_w8a16(w, cs, x)
+        mag = fp8_mag(w, cs, x)
+    check_f16(y, y_acc, mag, K, "%s staged limit M=%d N=%d K=%d" % (fmt, M, N, K))
 
 
 # ------------------------------------------------------------------ full sizes (sampled rows)
