@@ -462,7 +462,8 @@ __global__ __launch_bounds__(64 * W) void gemv_fp8_lds_kernel(
     const uint8_t *w, const float *cs, int N, int K, const uint16_t *x, uint16_t *y) {
   extern __shared__ uint4_t xs[];
   const int lane = threadIdx.x & 63;
-  const int n0 = (blockIdx.x * W + (threadIdx.x >> 6)) * R;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // row addresses stay scalar
+  const int n0 = (blockIdx.x * W + wave) * R;
   const int nc = K >> 4;                    // 16-element chunks per row
   const int np = K >> 3;                    // 16-byte activation pieces per row
   const int tot = M * np;

@@ -145,7 +145,8 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_lds_kernel(
     uint16_t *y) {
   extern __shared__ uint4_t xs[];
   const int lane = threadIdx.x & 63;
-  const int n0 = (blockIdx.x * W + (threadIdx.x >> 6)) * R;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // row addresses stay scalar
+  const int n0 = (blockIdx.x * W + wave) * R;
   const int nc = K >> 5;                    // 32-element chunks per row
   const int np = K >> 3;                    // 16-byte activation pieces per row
   const int tot = M * np;
@@ -191,25 +192,32 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_lds_kernel(
       for (int q = 0; q < 4; ++q) xv[m][q] = xs[m * np + act_slot<4>(c, q)];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      uint32_t wh[16];
+      // the two 16-element groups in turn (words 0-1, then 2-3), each decoded
+      // just before its dots: fewer registers live, more waves resident
+      float p[2][M];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        wh[4 * i + 0] = __builtin_bit_cast(uint32_t, e2m1x2_to_h2<0>(rd.wq[r][i]));
-        wh[4 * i + 1] = __builtin_bit_cast(uint32_t, e2m1x2_to_h2<1>(rd.wq[r][i]));
-        wh[4 * i + 2] = __builtin_bit_cast(uint32_t, e2m1x2_to_h2<2>(rd.wq[r][i]));
-        wh[4 * i + 3] = __builtin_bit_cast(uint32_t, e2m1x2_to_h2<3>(rd.wq[r][i]));
+      for (int h = 0; h < 2; ++h) {
+        uint32_t wh[8];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const uint32_t w = rd.wq[r][2 * h + i];
+          wh[4 * i + 0] = __builtin_bit_cast(uint32_t, e2m1x2_to_h2<0>(w));
+          wh[4 * i + 1] = __builtin_bit_cast(uint32_t, e2m1x2_to_h2<1>(w));
+          wh[4 * i + 2] = __builtin_bit_cast(uint32_t, e2m1x2_to_h2<2>(w));
+          wh[4 * i + 3] = __builtin_bit_cast(uint32_t, e2m1x2_to_h2<3>(w));
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          float t = 0.0f;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) t = dot2_f16(wh[q], xv[m][2 * h + (q >> 2)][q & 3], t);
+          p[h][m] = t;
+        }
       }
       const float s0 = e4m3_to_f32<0>(rd.sc[r]) * g;
       const float s1 = e4m3_to_f32<1>(rd.sc[r]) * g;
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        float p0 = 0.0f, p1 = 0.0f;
-#pragma unroll
-        for (int p = 0; p < 8; ++p) p0 = dot2_f16(wh[p], xv[m][p >> 2][p & 3], p0);
-#pragma unroll
-        for (int p = 8; p < 16; ++p) p1 = dot2_f16(wh[p], xv[m][p >> 2][p & 3], p1);
-        acc[r][m] = fmaf(p1, s1, fmaf(p0, s0, acc[r][m]));
-      }
+      for (int m = 0; m < M; ++m) acc[r][m] = fmaf(p[1][m], s1, fmaf(p[0][m], s0, acc[r][m]));
     }
   };
   // chunks c = lane, lane + 64, ...: the two round buffers alternate
