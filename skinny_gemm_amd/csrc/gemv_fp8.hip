@@ -11,7 +11,9 @@
 // Mapping (one wave = R weight rows, full K): lane l takes 16-element
 // chunks c = l, l + 64, ...: one 128-bit weight load per row, the chunk's
 // activations (M x 32 B) loaded once and reused for all R rows, and a
-// transposing butterfly for the R*M partial sums at the end.
+// transposing butterfly for the R*M partial sums at the end.  At M <= 4 the
+// same mapping runs with the activation rows staged in LDS once per
+// workgroup (gemv_fp8_lds_kernel).
 // Bytes per call: N*K + 4*N weights and scales + 2*M*K + 2*M*N.
 #include "device.h"
 #include "launch.h"
@@ -551,7 +553,7 @@ static hipError_t launch_mru(const uint8_t *w, const float *cs, int N, int K, co
   return hipGetLastError();
 }
 
-// Vector kernel shape: two rows per wave measured best on MI355X at M <= 2
+// Plain vector kernel shape: two rows per wave measured best on MI355X at M <= 2
 // for every shape tried (K 4096 to 17408, N 4096 to 34816).  Each lane
 // loads up to U = 6 chunks of a row per round (one memory round trip per
 // round: 5.9 -> 6.2 TB/s on a 5120 x 34816 matrix), U fitted to the chunks

@@ -17,6 +17,8 @@
 //   * the chunk's binary16 activations (M x 64 B) are loaded once per lane
 //     and reused for all R rows;
 //   * a transposing butterfly reduces the R*M partial sums per lane.
+// At M <= 2 the same mapping runs with the activation rows staged in LDS
+// once per workgroup (gemv_nvfp4_lds_kernel); M >= 3 takes the matrix cores.
 // Bytes per call: N*K*(1/2 + 1/16) weights + 2*M*K activations + 2*M*N out.
 #include "device.h"
 #include "launch.h"
@@ -539,7 +541,7 @@ static hipError_t launch_mru(const uint8_t *codes, const uint8_t *scales, float 
   return hipGetLastError();
 }
 
-// Vector kernel shape: two rows per wave measured best on MI355X at M <= 2
+// Plain vector kernel shape: two rows per wave measured best on MI355X at M <= 2
 // for every shape tried (K 4096 to 17408, N 4096 to 34816).  A row of up to
 // 4 chunks per lane is loaded in one round (one memory round trip: 3.9 ->
 // 4.7 TB/s on a 5120 x 34816 matrix); longer rows keep the pipelined loop,
