@@ -355,7 +355,7 @@ static hipError_t launch_mfma_cfg(const uint8_t *w, const float *cs, int N, int 
                                   const uint16_t *x, int M, uint16_t *y, hipStream_t stream) {
   using C = f8::Cfg<T, WR, KS, S, MP>;
   if (K % (128 * S) != 0) return hipErrorInvalidValue;   // chunks must tile K
-  static const hipError_t lds_ok =
+  const hipError_t lds_ok =
       allow_lds((const void *)gemv_fp8_mfma_kernel<T, WR, KS, S, MP>, C::kLds);
   if (lds_ok != hipSuccess) return lds_ok;
   const int rows = C::kRows * WR;
@@ -584,7 +584,7 @@ static hipError_t launch_lds_a(const uint8_t *w, const float *cs, int N, int K,
                                const uint16_t *x, uint16_t *y, hipStream_t stream) {
   constexpr int R = 3, W = 8;
   const int lds = M * K * 2;
-  static const hipError_t lds_ok =
+  const hipError_t lds_ok =
       allow_lds((const void *)gemv_fp8_lds_kernel<M, R, W, A>, 2 * kF8LdsMaxMK);
   if (lds_ok != hipSuccess) return lds_ok;
   const int rows = R * W;

@@ -470,8 +470,7 @@ static hipError_t launch_mfma_cfg(const uint8_t *codes, const uint8_t *scales, f
                                   hipStream_t stream) {
   using C = nv::Cfg<T, WR, KS, S, MP>;
   if (K % (128 * S) != 0) return hipErrorInvalidValue;   // chunks must tile K
-  // workgroups above 64 KB of LDS must be allowed once per kernel
-  static const hipError_t lds_ok =
+  const hipError_t lds_ok =
       allow_lds((const void *)gemv_nvfp4_mfma_kernel<T, WR, KS, S, MP>, C::kLds);
   if (lds_ok != hipSuccess) return lds_ok;
   const int rows = C::kRows * WR;
@@ -573,7 +572,7 @@ static hipError_t launch_lds_a(const uint8_t *codes, const uint8_t *scales, floa
                                int K, const uint16_t *x, uint16_t *y, hipStream_t stream) {
   constexpr int R = 3;
   const int lds = M * K * 2;
-  static const hipError_t lds_ok =
+  const hipError_t lds_ok =
       allow_lds((const void *)gemv_nvfp4_lds_kernel<M, R, W, A>, 2 * kNvLdsMaxMK);
   if (lds_ok != hipSuccess) return lds_ok;
   const int rows = R * W;

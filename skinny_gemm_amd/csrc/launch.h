@@ -5,6 +5,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 namespace skinny {
 
 hipError_t launch_quantize_q8_1(const float *x, int M, int K, int8_t *qs,
@@ -38,10 +42,22 @@ hipError_t launch_gemv_fp8(const uint8_t *w, const float *cs, int N, int K,
                            const uint16_t *x, int M, uint16_t *y, hipStream_t stream);
 
 // Let a kernel use more than 64 KB of LDS per workgroup (gfx950 has 160 KB
-// per compute unit); a no-op at or below 64 KB.
+// per compute unit); a no-op at or below 64 KB.  The limit is raised once
+// per (device, kernel) and never lowered, so calls of any size, from any
+// thread, on any device, see a limit at least as large as they asked for.
 inline hipError_t allow_lds(const void *kernel, int bytes) {
   if (bytes <= 65536) return hipSuccess;
-  return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::map<std::pair<int, const void *>, int> granted;
+  std::lock_guard<std::mutex> lock(mu);
+  int &have = granted[{dev, kernel}];
+  if (bytes <= have) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) have = bytes;
+  return e;
 }
 
 }  // namespace skinny

@@ -456,7 +456,7 @@ static hipError_t launch_mfma_cfg(const uint8_t *w_qs, const uint16_t *w_d, int 
                                   int M, float *y, hipStream_t stream) {
   using C = q4::Cfg<T, WR, KS, S, MP>;
   if (K % (64 * S) != 0) return hipErrorInvalidValue;   // chunks must tile K
-  static const hipError_t lds_ok =
+  const hipError_t lds_ok =
       allow_lds((const void *)mmvq_q4_0_mfma_kernel<T, WR, KS, S, MP, D, KQ>, C::kLds);
   if (lds_ok != hipSuccess) return lds_ok;
   const int rows = C::kRows * WR;
