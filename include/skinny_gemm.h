@@ -21,8 +21,10 @@
  *   - Every pointer is a device pointer on the current HIP device; `stream`
  *     is a hipStream_t passed as void* (NULL = the default stream).
  *   - The caller allocates and owns every buffer.  The library allocates
- *     nothing, keeps no state between calls, and is safe to call from
- *     several host threads.  Outputs must not overlap inputs.
+ *     no device memory and keeps no data between calls (only, per device,
+ *     which kernels it has already allowed more than 64 KB of LDS), and is
+ *     safe to call from several host threads.  Outputs must not overlap
+ *     inputs.
  *   - A call validates its arguments on the host before any HIP call, then
  *     enqueues its kernel (several, for the split cases stated below) on
  *     `stream` and returns without synchronizing.
