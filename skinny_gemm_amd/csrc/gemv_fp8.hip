@@ -579,10 +579,9 @@ static hipError_t launch_m(const uint8_t *w, const float *cs, int N, int K, cons
 constexpr int kF8LdsMaxM = 4;
 constexpr int kF8LdsMaxMK = 80 * 1024;      // M K binary16 activations in LDS
 
-template <int M, int A>
+template <int M, int A, int R = 3, int W = 8>
 static hipError_t launch_lds_a(const uint8_t *w, const float *cs, int N, int K,
                                const uint16_t *x, uint16_t *y, hipStream_t stream) {
-  constexpr int R = 3, W = 8;
   const int lds = M * K * 2;
   const hipError_t lds_ok =
       allow_lds((const void *)gemv_fp8_lds_kernel<M, R, W, A>, 2 * kF8LdsMaxMK);

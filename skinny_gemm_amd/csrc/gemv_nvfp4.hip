@@ -567,10 +567,9 @@ static hipError_t launch_m(const uint8_t *codes, const uint8_t *scales, float g,
 // 14.1 us).
 constexpr int kNvLdsMaxMK = 80 * 1024;      // M K binary16 activations in LDS
 
-template <int M, int W, int A>
+template <int M, int W, int A, int R = 3>
 static hipError_t launch_lds_a(const uint8_t *codes, const uint8_t *scales, float g, int N,
                                int K, const uint16_t *x, uint16_t *y, hipStream_t stream) {
-  constexpr int R = 3;
   const int lds = M * K * 2;
   const hipError_t lds_ok =
       allow_lds((const void *)gemv_nvfp4_lds_kernel<M, R, W, A>, 2 * kNvLdsMaxMK);
