@@ -691,6 +691,66 @@ def test_repeat_runs_bit_identical_and_side_stream():
         assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
 
 
+def test_graph_replays_match_eager():
+    # every entry point, at M values that reach each kernel family, captured
+    # in one HIP graph; each replay (with eager work and synchronizations in
+    # between) must reproduce the eager bytes -- no memsets or host-side state
+    # may hide in a captured launch
+    import torch
+
+    import skinny_gemm_amd as sk
+
+    d = torch.device("cuda:0")
+    N, K = 1000, 4096                        # K % 256 == 0: matrix-core paths too
+    w_qs, w_d = inputs.q4_0_weights_torch(N, K, 21, d)
+    k_qs, k_hdr = inputs.q4_k_weights_torch(N, K, 22, d)
+    ql, qh, sc, dd = inputs.q6_k_weights_torch(N, K, 23, d)
+    codes, scales = inputs.nvfp4_weights_torch(N, K, 24, d)
+    w8, cs = inputs.fp8_weights_torch(N, K, 25, d)
+    xf = {M: inputs.normal_f32_torch(M, K, 30 + M, d) for M in (1, 2, 8)}
+    xh = {M: inputs.normal_f16_torch(M, K, 40 + M, d) for M in (1, 2, 4, 8, 32)}
+    q8 = {M: sk.quantize_act_q8_1(xf[M]) for M in (1, 2, 8)}
+    outs = []
+
+    def run():
+        outs.clear()
+        for M in (1, 2, 8):
+            sk.quantize_act_q8_1(xf[M], *q8[M])
+            outs.append(sk.mmvq_q4_0(w_qs, w_d, *q8[M]))
+            outs.append(sk.mmvq_q4_k(k_qs, k_hdr, *q8[M]))
+            outs.append(sk.mmvq_q6_k(ql, qh, sc, dd, q8[M][0], q8[M][1]))
+        for M in (1, 2):
+            outs.append(sk.mmvq_q4_0_f32act(w_qs, w_d, xf[M]))
+        for M in (1, 2, 4, 8):
+            outs.append(sk.gemv_nvfp4_w4a16(codes, scales, 1.0, xh[M]))
+        for M in (1, 2, 4, 8, 32):
+            outs.append(sk.gemv_fp8_w8a16(w8, cs, xh[M]))
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()                                # warm every path before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    graph_outs = list(outs)
+    torch.cuda.synchronize()
+    run()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    for _ in range(3):
+        for o in graph_outs:
+            o.view(torch.uint8).fill_(0xA5)
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (o, r) in enumerate(zip(graph_outs, ref)):
+            assert torch.equal(o.view(torch.uint8), r.view(torch.uint8)), i
+        run()                                # eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_largest_k_small_n():
     # K at the documented maximum, a handful of rows, ragged N
     M, N, K = 2, 5, 1 << 20
