@@ -179,12 +179,23 @@ struct Chunk {
 
 // (No __restrict__ on the inputs: the issue fence below must be able to
 // order their loads.)
+//
+// A grid with gridDim.y > 1 splits the activation rows into groups of MP:
+// workgroup row y takes rows [MP y, MP y + MP).  Workgroups past the last
+// tile (the launcher may round the grid's width up) exit at once.
 template <int T, int WR, int KS, int S, int MP>
 __global__ __launch_bounds__(64 * WR * KS) void gemv_fp8_mfma_kernel(
     const uint8_t *w, const float *cs, int N, int K, const uint16_t *x, int M, uint16_t *y) {
   using C = f8::Cfg<T, WR, KS, S, MP>;
   using R = f8::Chunk<T, S, C::kApw>;
   constexpr int MT = C::kMT;
+  if ((int)blockIdx.x * (C::kRows * WR) >= N) return;        // whole workgroup
+  {
+    const int m0 = (int)blockIdx.y * MP;
+    x += (size_t)m0 * K;
+    y += (size_t)m0 * N;
+    M = min(MP, M - m0);
+  }
   extern __shared__ uint4_t smem4[];
   uint8_t *smem = reinterpret_cast<uint8_t *>(smem4);
   const int lane = threadIdx.x & 63;
@@ -350,6 +361,10 @@ __global__ __launch_bounds__(64 * WR * KS) void gemv_fp8_mfma_kernel(
   }
 }
 
+// groups > 1: M > MP rows in groups of MP, one grid row per group.  The grid
+// width is then a multiple of 8, so the groups of one tile land on one XCD
+// (workgroups are dealt to the 8 XCDs in turn) and re-read its weights from
+// that XCD's L2.
 template <int T, int WR, int KS, int S, int MP>
 static hipError_t launch_mfma_cfg(const uint8_t *w, const float *cs, int N, int K,
                                   const uint16_t *x, int M, uint16_t *y, hipStream_t stream) {
@@ -359,8 +374,10 @@ static hipError_t launch_mfma_cfg(const uint8_t *w, const float *cs, int N, int 
       allow_lds((const void *)gemv_fp8_mfma_kernel<T, WR, KS, S, MP>, C::kLds);
   if (lds_ok != hipSuccess) return lds_ok;
   const int rows = C::kRows * WR;
-  const int blocks = (N + rows - 1) / rows;
-  hipLaunchKernelGGL((gemv_fp8_mfma_kernel<T, WR, KS, S, MP>), dim3(blocks),
+  const int groups = (M + MP - 1) / MP;
+  int blocks = (N + rows - 1) / rows;
+  if (groups > 1) blocks = (blocks + 7) / 8 * 8;
+  hipLaunchKernelGGL((gemv_fp8_mfma_kernel<T, WR, KS, S, MP>), dim3(blocks, groups),
                      dim3(64 * C::kWaves), C::kLds, stream, w, cs, N, K, x, M, y);
   return hipGetLastError();
 }
@@ -412,8 +429,9 @@ static hipError_t launch_mfma_wide(const uint8_t *w, const float *cs, int N, int
 // share it through LDS, and LDS then leaves room for a K split only with
 // short chunks.  Measured on MI355X at M = 32, 64, 96 over K 5120..17408, N
 // 5120..34816: wide matrices favour more sharing waves, narrow ones a K
-// split; narrow matrices at M >= 64 stay limited by their few workgroups
-// (0.6 TB/s on 17408 x 5120 at M = 96, against 1.6 on 5120 x 34816).
+// split.  (Narrow matrices, and mid-width ones above M = 48, now go to
+// launch_mfma_grouped: in one pass they were limited by their few
+// workgroups, 0.6 TB/s on 17408 x 5120 at M = 96.)
 template <int MP>
 static hipError_t launch_mfma_chunked_mp(const uint8_t *w, const float *cs, int N, int K,
                                          const uint16_t *x, int M, uint16_t *y,
@@ -435,11 +453,39 @@ static hipError_t launch_mfma_chunked_mp(const uint8_t *w, const float *cs, int 
 #undef SKINNY_F8
 }
 
+// 17 <= M <= 96 on narrow and mid-width matrices: the rows in groups of 16
+// or 32, one grid row per group (launch_mfma_cfg), so that a narrow matrix
+// still fills the chip; the groups of a tile re-read its weights from one
+// L2.  Measured on MI355X at M = 32, 48, 64, 96: 5120 x 5120 at M = 96 50.1
+// -> 24.1 us, 17408 x 5120 149.6 -> 68.4 us, 5120 x 10240 54.5 -> 35.8 us;
+// wide matrices keep one pass over all rows.
+static hipError_t launch_mfma_grouped(const uint8_t *w, const float *cs, int N, int K,
+                                      const uint16_t *x, int M, uint16_t *y,
+                                      hipStream_t stream) {
+  const int tiles = (N + 15) / 16;
+  const bool s4 = K % 512 == 0;
+  if (tiles < 512) {
+    if (M <= 32) {
+      if (s4) return launch_mfma_cfg<1, 1, 1, 4, 16>(w, cs, N, K, x, M, y, stream);
+      return launch_mfma_cfg<1, 1, 1, 2, 16>(w, cs, N, K, x, M, y, stream);
+    }
+    if (M <= 48) {
+      if (s4) return launch_mfma_cfg<2, 1, 2, 4, 16>(w, cs, N, K, x, M, y, stream);
+      return launch_mfma_cfg<2, 1, 2, 2, 16>(w, cs, N, K, x, M, y, stream);
+    }
+    return launch_mfma_cfg<1, 4, 2, 2, 32>(w, cs, N, K, x, M, y, stream);
+  }
+  return launch_mfma_cfg<1, 4, 1, 2, 32>(w, cs, N, K, x, M, y, stream);
+}
+
 static hipError_t launch_mfma(const uint8_t *w, const float *cs, int N, int K, const uint16_t *x,
                               int M, uint16_t *y, hipStream_t stream) {
   if (M <= 4) return launch_mfma_mp<4>(w, cs, N, K, x, M, y, stream);
   if (M <= 8) return launch_mfma_mp<8>(w, cs, N, K, x, M, y, stream);
   if (M <= 16) return launch_mfma_wide(w, cs, N, K, x, M, y, stream);
+  const int tiles = (N + 15) / 16;
+  if (tiles < 512 || (tiles < 1536 && M > 48))
+    return launch_mfma_grouped(w, cs, N, K, x, M, y, stream);
   switch ((M + 15) / 16) {
     case 2: return launch_mfma_chunked_mp<32>(w, cs, N, K, x, M, y, stream);
     case 3: return launch_mfma_chunked_mp<48>(w, cs, N, K, x, M, y, stream);

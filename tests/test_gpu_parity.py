@@ -501,11 +501,12 @@ def test_gemv_fp8_vs_oracle(M, N, K):
 
 @pytest.mark.parametrize("M", [17, 31, 48, 64, 80, 96])
 @pytest.mark.parametrize("N,K", [(4096 + 3, 272),     # K % 256 != 0: passes of 8 rows
-                                 (1030, 5120),        # narrow: K split (one-step chunks at M > 64)
+                                 (1030, 5120),        # narrow: activation rows in groups
                                  (3000, 1280),
-                                 (9000, 768),         # mid
+                                 (9000, 768),         # mid (row groups above M = 48)
                                  (24576 + 40, 256),   # wide: more waves share each chunk
-                                 (40, 768)])
+                                 (40, 768),
+                                 (600, 17408)])       # narrow, long: row groups of 16 / 32
 def test_gemv_fp8_chunked_vs_oracle(M, N, K):
     w, cs = inputs.fp8_weights(N, K, 13 * N + K)
     x = inputs.normal_f16_bits(M, K, 6 * M + K)
@@ -514,15 +515,17 @@ def test_gemv_fp8_chunked_vs_oracle(M, N, K):
     check_f16(y, y_acc, fp8_mag(w, cs, x), K, "fp8 M=%d N=%d K=%d" % (M, N, K))
 
 
-def test_gemv_fp8_ninety_six_rows_bit_exact():
-    # M = 96 on the chunked path: row n holds code n at element n; x row m is
-    # 1 at the elements k with k % 96 == m (so each output has at most one
-    # exact term) -- pins the mapping of all six column tiles
-    N, K = 256, 256
+@pytest.mark.parametrize("N", [256,             # narrow: three groups of 32 rows
+                               24576 + 256])    # wide: one pass, six column tiles
+def test_gemv_fp8_ninety_six_rows_bit_exact(N):
+    # M = 96 on the chunked path: row n holds code n % 256 at element n % 256;
+    # x row m is 1 at the elements k with k % 96 == m (so each output has at
+    # most one exact term) -- pins the mapping of all 96 activation rows
+    K = 256
     w = np.zeros((N, K), np.uint8)
     codes = np.arange(256)
     codes[[0x7F, 0xFF]] = 0x38
-    w[np.arange(N), np.arange(N)] = codes
+    w[np.arange(N), np.arange(N) % 256] = codes[np.arange(N) % 256]
     cs = np.ones(N, np.float32)
     x = np.zeros((96, K), np.float16)
     for m in range(96):
