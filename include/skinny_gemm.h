@@ -105,8 +105,8 @@ int quantize_act_q8_1(const float *x, int M, int K,
  * i.e. the -8 of every weight is applied once per block through the Q8_1
  * sum term.  Accumulated in float32, output float32.
  *
- *   w_qs 16-byte aligned; w_d, a_d, a_s 2-byte aligned; a_qs 16-byte
- *   aligned; y float32 [M][N] row-major, 4-byte aligned.
+ *   w_qs, w_d, a_qs, a_d, a_s 16-byte aligned (the scale arrays too are
+ *   read with 128-bit loads); y float32 [M][N] row-major, 4-byte aligned.
  *   0 <= M <= SKINNY_MAX_M_GEMV; K % 32 == 0.
  * Block sums are exact integers; the float result matches the definition
  * to float32 summation-order rounding.
@@ -152,8 +152,8 @@ int mmvq_q4_0_f32act(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
  * For each m, n:  y = sum_b d sc d8 isum_b - dmin m s8_b,
  * isum_b = sum_{i<32} q * q8 (exact int32); the min enters through the Q8_1
  * sum term s8.  Accumulated in float32.
- *   w_qs, w_hdr, a_qs 16-byte aligned; a_d, a_s 2-byte aligned; y float32
- *   [M][N], 4-byte aligned.  0 <= M <= SKINNY_MAX_M_GEMV; K % 256 == 0.
+ *   w_qs, w_hdr, a_qs, a_d, a_s 16-byte aligned; y float32 [M][N], 4-byte
+ *   aligned.  0 <= M <= SKINNY_MAX_M_GEMV; K % 256 == 0.
  */
 int mmvq_q4_k(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
               const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
@@ -192,7 +192,7 @@ int mmvq_q6_k(const uint8_t *w_ql, const uint8_t *w_qh, const int8_t *w_sc,
  *   w_codes  [N][K/2] bytes: element 2j of a row in the low nibble of byte
  *            j, element 2j+1 in the high nibble.  16-byte aligned.
  *   w_scales [N][K/16] OCP E4M3 ("FN") bytes, one per 16 elements.
- *            2-byte aligned.
+ *            16-byte aligned.
  *   global_scale  per-tensor float32 multiplier.
  *   x        binary16 [M][K] row-major, 16-byte aligned.
  *   y        binary16 [M][N] row-major, 2-byte aligned:

@@ -59,8 +59,9 @@ int mmvq_q4_0(const uint8_t *w_qs, const uint16_t *w_d, int N, int K, const int8
   if ((st = shape_status(N, K, 32))) return st;
   if (M == 0 || N == 0) return SKINNY_OK;
   if (!w_qs || !w_d || !a_qs || !a_d || !a_s || !y) return SKINNY_ERR_NULL;
-  if (!aligned(w_qs, 16) || !aligned(a_qs, 16) || !aligned(w_d, 2) || !aligned(a_d, 2) ||
-      !aligned(a_s, 2) || !aligned(y, 4))
+  // the scale arrays too are read with 128-bit loads on some paths
+  if (!aligned(w_qs, 16) || !aligned(a_qs, 16) || !aligned(w_d, 16) || !aligned(a_d, 16) ||
+      !aligned(a_s, 16) || !aligned(y, 4))
     return SKINNY_ERR_ALIGN;
   return launched(skinny::launch_mmvq_q4_0(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y,
                                            (hipStream_t)stream));
@@ -86,8 +87,8 @@ int mmvq_q4_k(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K, const int
   if ((st = shape_status(N, K, 256))) return st;
   if (M == 0 || N == 0) return SKINNY_OK;
   if (!w_qs || !w_hdr || !a_qs || !a_d || !a_s || !y) return SKINNY_ERR_NULL;
-  if (!aligned(w_qs, 16) || !aligned(w_hdr, 16) || !aligned(a_qs, 16) || !aligned(a_d, 2) ||
-      !aligned(a_s, 2) || !aligned(y, 4))
+  if (!aligned(w_qs, 16) || !aligned(w_hdr, 16) || !aligned(a_qs, 16) || !aligned(a_d, 16) ||
+      !aligned(a_s, 16) || !aligned(y, 4))
     return SKINNY_ERR_ALIGN;
   return launched(skinny::launch_mmvq_q4_k(w_qs, w_hdr, N, K, a_qs, a_d, a_s, M, y,
                                            (hipStream_t)stream));
@@ -115,7 +116,7 @@ int gemv_nvfp4_w4a16(const uint8_t *w_codes, const uint8_t *w_scales, float glob
   if ((st = shape_status(N, K, 32))) return st;
   if (M == 0 || N == 0) return SKINNY_OK;
   if (!w_codes || !w_scales || !x || !y) return SKINNY_ERR_NULL;
-  if (!aligned(w_codes, 16) || !aligned(w_scales, 2) || !aligned(x, 16) || !aligned(y, 2))
+  if (!aligned(w_codes, 16) || !aligned(w_scales, 16) || !aligned(x, 16) || !aligned(y, 2))
     return SKINNY_ERR_ALIGN;
   return launched(skinny::launch_gemv_nvfp4(w_codes, w_scales, global_scale, N, K, x, M, y,
                                             (hipStream_t)stream));

@@ -121,15 +121,16 @@ def test_gemv_null_pointers(L):
 
 
 def test_gemv_misaligned(L):
-    for kw, off in (("w", 8), ("aq", 4), ("wd", 1), ("ad", 1), ("as_", 1), ("y", 2)):
+    for kw, off in (("w", 8), ("aq", 4), ("wd", 8), ("ad", 8), ("as_", 2), ("y", 2)):
         assert q4(L, **{kw: A + off}) == -3, kw
-    for kw, off in (("c", 8), ("s", 1), ("x", 8), ("y", 1)):
+    for kw, off in (("c", 8), ("s", 8), ("x", 8), ("y", 1)):
         assert nv(L, **{kw: A + off}) == -3, kw
     for kw, off in (("w", 8), ("cs", 2), ("x", 8), ("y", 1)):
         assert f8(L, **{kw: A + off}) == -3, kw
     # the weaker requirements really are weaker
-    assert q4(L, wd=A + 2, y=0) == -1
-    assert nv(L, s=A + 2, y=0) == -1
+    assert q4(L, y=A + 4, w=0) == -1
+    assert nv(L, y=A + 2, c=0) == -1
+    assert f8(L, cs=A + 4, y=0) == -1
 
 
 def test_empty_calls_are_noops(L):
@@ -205,7 +206,7 @@ def test_k_quant_validation(L, fn):
 def test_k_quant_null_and_alignment(L):
     for kw in ("w", "h", "aq", "ad", "as_", "y"):
         assert q4k(L, **{kw: 0}) == -1, kw
-    for kw, off in (("w", 8), ("h", 8), ("aq", 8), ("ad", 1), ("as_", 1), ("y", 2)):
+    for kw, off in (("w", 8), ("h", 8), ("aq", 8), ("ad", 8), ("as_", 2), ("y", 2)):
         assert q4k(L, **{kw: A + off}) == -3, kw
     for kw in ("ql", "qh", "sc", "d", "aq", "ad", "y"):
         assert q6k(L, **{kw: 0}) == -1, kw
