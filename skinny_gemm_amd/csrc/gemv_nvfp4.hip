@@ -18,7 +18,9 @@
 //     and reused for all R rows;
 //   * a transposing butterfly reduces the R*M partial sums per lane.
 // At M <= 2 the same mapping runs with the activation rows staged in LDS
-// once per workgroup (gemv_nvfp4_lds_kernel); M >= 3 takes the matrix cores.
+// once per workgroup (gemv_nvfp4_lds_kernel, and gemv_nvfp4_flat_kernel,
+// which spreads a wave's rows evenly over its lanes); M >= 3 takes the
+// matrix cores.
 // Bytes per call: N*K*(1/2 + 1/16) weights + 2*M*K activations + 2*M*N out.
 #include "device.h"
 #include "launch.h"
@@ -245,6 +247,105 @@ __global__ __launch_bounds__(64 * W) void gemv_nvfp4_lds_kernel(
     const int n = n0 + r;
     if (n < N) y[(size_t)m * N + n] = f32_to_f16_bits(total);
   }
+}
+
+// Flat variant of the staged kernel for one activation row (M = 1) when a
+// row holds an odd number of half-waves of chunks (K = 3072 or 5120): the
+// round mapping above then leaves half the lanes idle in its last round.
+// A wave's R rows are adjacent in memory, one span of R * nc chunks (16 code
+// bytes and 2 scale bytes each), and lane l takes chunks f = l + 64 i of the
+// span, i < L = R nc / 64: every lane busy, all L loads issued before the
+// activation staging, one memory round trip.  Chunk f belongs to row f / nc
+// at position f % nc; since nc >= 64, stepping f by 64 wraps into the next
+// row at most once.  Decode, group dots and flushes are the staged kernel's,
+// one chunk at a time.
+template <int R, int L, int W, int A>
+__global__ __launch_bounds__(64 * W) void gemv_nvfp4_flat_kernel(
+    const uint8_t *codes, const uint8_t *scales, float g, int N, int K, const uint16_t *x,
+    uint16_t *y) {
+  extern __shared__ uint4_t xs[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // span address stays scalar
+  const int n0 = (blockIdx.x * W + wave) * R;
+  const int nc = K >> 5;                    // 32-element chunks per row
+  const int np = K >> 3;                    // 16-byte activation pieces
+  uint4_t av[A];
+  act_issue<A, 64 * W>(x, np, av);
+
+  // waves past N read row N - 1 and store nothing
+  const int nw = min(n0, N - 1);
+  const int span = min(R, N - nw) * nc;     // chunks of the rows that exist
+  const uint8_t *cspan = codes + (size_t)nw * (size_t)(K >> 1);
+  const uint16_t *sspan = reinterpret_cast<const uint16_t *>(scales + (size_t)nw * (size_t)(K >> 4));
+  uint4_t wq[L];
+  uint32_t sc[L];
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const int f = min(lane + kWave * i, span - 1);
+    wq[i] = load16_nt(cspan + 16 * (size_t)f);
+    sc[i] = load_u16_nt(sspan + f);
+  }
+  issue_fence();
+  act_stage<4, A, 64 * W>(x, np, np, xs, av);
+  wg_barrier();
+  if (n0 >= N) return;
+
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+  int c = lane, row = 0;                    // position and row of chunk i
+  uint4_t xn[4];                            // its activations, read one chunk ahead
+#pragma unroll
+  for (int q = 0; q < 4; ++q) xn[q] = xs[act_slot<4>(c, q)];
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    __builtin_amdgcn_sched_barrier(0);      // one chunk at a time: few registers live
+    uint4_t xv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xv[q] = xn[q];
+    const int ri = row;
+    const bool live = lane + kWave * i < span;
+    if (i + 1 < L) {
+      c += kWave;
+      if (c >= nc) { c -= nc; ++row; }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xn[q] = xs[act_slot<4>(c, q)];
+    }
+    float p[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t wh[8];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t w = wq[i][2 * h + j];
+        wh[4 * j + 0] = __builtin_bit_cast(uint32_t, e2m1x2_to_h2<0>(w));
+        wh[4 * j + 1] = __builtin_bit_cast(uint32_t, e2m1x2_to_h2<1>(w));
+        wh[4 * j + 2] = __builtin_bit_cast(uint32_t, e2m1x2_to_h2<2>(w));
+        wh[4 * j + 3] = __builtin_bit_cast(uint32_t, e2m1x2_to_h2<3>(w));
+      }
+      float t = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) t = dot2_f16(wh[q], xv[2 * h + (q >> 2)][q & 3], t);
+      p[h] = t;
+    }
+    const float s0 = e4m3_to_f32<0>(sc[i]) * g;
+    const float s1 = e4m3_to_f32<1>(sc[i]) * g;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float a = fmaf(p[1], s1, fmaf(p[0], s0, acc[r]));
+      acc[r] = (live && ri == r) ? a : acc[r];
+    }
+  }
+
+  constexpr int V = next_pow2_n(R);
+  float v[V];
+#pragma unroll
+  for (int k = 0; k < V; ++k) v[k] = k < R ? acc[k] : 0.0f;
+  const float total = wave_reduce_transpose<V>(v, lane);
+  constexpr int SHIFT = 6 - Log2<V>::value;
+  const int r = lane >> SHIFT;
+  if ((lane & ((1 << SHIFT) - 1)) == 0 && r < R && n0 + r < N)
+    y[n0 + r] = f32_to_f16_bits(total);
 }
 
 // One 128-K step of a 16-row tile: decode the lane's 16 code bytes with its
@@ -591,6 +692,41 @@ static hipError_t launch_lds(const uint8_t *codes, const uint8_t *scales, float 
   return launch_lds_a<M, W, 12>(codes, scales, g, N, K, x, y, stream);
 }
 
+// Flat kernel (M = 1, nc = K / 32 in {96, 160}): two rows per wave, L = nc / 32
+// chunks per lane; four waves per workgroup, eight on wide matrices
+// (measured on MI355X at M = 1: 5120 x 10240 8.2 -> 7.3 us with four waves,
+// 5120 x 34816 18.2 -> 17.9 us with eight; 5120 x 5120 is as fast on the
+// round mapping and keeps it).
+template <int L, int W>
+static hipError_t launch_flat_lw(const uint8_t *codes, const uint8_t *scales, float g, int N,
+                                 int K, const uint16_t *x, uint16_t *y, hipStream_t stream) {
+  constexpr int R = 2;
+  const int rows = R * W;
+  const int lds = 2 * K;
+  if ((K >> 3) <= 2 * 64 * W)
+    hipLaunchKernelGGL((gemv_nvfp4_flat_kernel<R, L, W, 2>), dim3((N + rows - 1) / rows),
+                       dim3(64 * W), lds, stream, codes, scales, g, N, K, x, y);
+  else
+    hipLaunchKernelGGL((gemv_nvfp4_flat_kernel<R, L, W, 4>), dim3((N + rows - 1) / rows),
+                       dim3(64 * W), lds, stream, codes, scales, g, N, K, x, y);
+  return hipGetLastError();
+}
+
+static bool flat_fits(int N, int K) {
+  const int nc = K >> 5;
+  return N >= 8192 && (nc == 96 || nc == 160);
+}
+
+static hipError_t launch_flat(const uint8_t *codes, const uint8_t *scales, float g, int N, int K,
+                              const uint16_t *x, uint16_t *y, hipStream_t stream) {
+  const bool wide = N >= 16384;
+  if ((K >> 5) == 96)
+    return wide ? launch_flat_lw<3, 8>(codes, scales, g, N, K, x, y, stream)
+                : launch_flat_lw<3, 4>(codes, scales, g, N, K, x, y, stream);
+  return wide ? launch_flat_lw<5, 8>(codes, scales, g, N, K, x, y, stream)
+              : launch_flat_lw<5, 4>(codes, scales, g, N, K, x, y, stream);
+}
+
 // Vector kernel for 1 <= M <= 8 rows.
 static hipError_t launch_vector(const uint8_t *codes, const uint8_t *scales, float g, int N,
                                 int K, const uint16_t *x, int M, uint16_t *y,
@@ -608,12 +744,14 @@ static hipError_t launch_vector(const uint8_t *codes, const uint8_t *scales, flo
 }
 
 // M <= 2 takes the staged-activation vector kernel while the rows fit in
-// LDS.  The matrix-core kernel takes every M >= 3 in one weight pass when K
-// is a whole number of 256-element chunks.  Otherwise the plain vector
-// kernel serves up to 8 rows per pass: rows 9..M take a second pass.
+// LDS (its flat variant at M = 1 on wide matrices with K = 3072 or 5120).
+// The matrix-core kernel takes every M >= 3 in one weight pass when K is a
+// whole number of 256-element chunks.  Otherwise the plain vector kernel
+// serves up to 8 rows per pass: rows 9..M take a second pass.
 hipError_t launch_gemv_nvfp4(const uint8_t *codes, const uint8_t *scales, float g, int N, int K,
                              const uint16_t *x, int M, uint16_t *y, hipStream_t stream) {
   if (M <= 2 && M * K <= kNvLdsMaxMK) {
+    if (M == 1 && flat_fits(N, K)) return launch_flat(codes, scales, g, N, K, x, y, stream);
     if (M == 1) return launch_lds<1>(codes, scales, g, N, K, x, y, stream);
     return launch_lds<2>(codes, scales, g, N, K, x, y, stream);
   }

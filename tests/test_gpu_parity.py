@@ -439,6 +439,48 @@ def test_gemv_nvfp4_every_code_and_scale_bit_exact():
             assert np.array_equal(y, want), (base, M)
 
 
+@pytest.mark.parametrize("N,K", [(8192, 5120), (8193, 5120), (16385, 5120), (8195, 3072),
+                                 (16384, 3072)])
+def test_gemv_nvfp4_flat_vs_oracle(N, K):
+    # M = 1 with K / 32 an odd multiple of 32 chunks on wide matrices: the
+    # flat mapping (two adjacent rows spread evenly over a wave's lanes); an
+    # odd N leaves the last wave one row
+    codes, scales, g = inputs.nvfp4_weights(N, K, 3 * N + K)
+    x = inputs.normal_f16_bits(1, K, N + 1)
+    y = run_nvfp4(codes, scales, g, x)
+    y_acc, _ = oracle.gemv_nvfp4_w4a16(codes, scales, g, x)
+    check_f16(y, y_acc, nvfp4_mag(codes, scales, g, x), K, "nvfp4 flat N=%d K=%d" % (N, K))
+
+
+def test_gemv_nvfp4_flat_bit_exact():
+    # flat mapping, exact: row n holds the 16 E2M1 codes (twice) in chunk
+    # n % nc only, under group scales n % 256 and its mirror (NaN codes
+    # replaced by 1.0); x holds one 1.0 per chunk at element (base + 5 c) %
+    # 32, so y[n] is one code times one scale, exact in binary16 -- a chunk
+    # credited to the wrong row, lane or position shows as a wrong bit
+    N, K = 8193, 3072
+    nc = K // 32
+    pattern = np.array([c0 | (c1 << 4) for c0, c1 in zip(range(0, 16, 2), range(1, 16, 2))] +
+                       [0x12, 0x34, 0x56, 0x70, 0x89, 0xAB, 0xCD, 0xEF], np.uint8)
+    codes = np.zeros((N, K // 2), np.uint8)
+    scales = np.full((N, K // 16), 0x38, np.uint8)
+    for n in range(N):
+        c = n % nc
+        codes[n, 16 * c:16 * c + 16] = pattern
+        scales[n, 2 * c] = n % 256
+        scales[n, 2 * c + 1] = 255 - n % 256
+    scales[(scales & 0x7F) == 0x7F] = 0x38
+    for base in (0, 11, 22):
+        x = np.zeros((1, K), np.float16)
+        for c in range(nc):
+            x[0, 32 * c + (base + 5 * c) % 32] = 1.0
+        xb = x.view(np.uint16)
+        y = run_nvfp4(codes, scales, 1.0, xb)
+        _, want = oracle.gemv_nvfp4_w4a16(codes, scales, 1.0, xb)
+        assert np.array_equal(y, want), base
+        assert np.count_nonzero(f16(want)) > N // 2
+
+
 def test_gemv_nvfp4_outliers():
     # activation outliers of +-2e4: any binary16 partial sum would overflow
     M, N, K = 4, 512, 5120
