@@ -3,7 +3,8 @@
 Argument marshalling only: each function checks tensor dtypes, shapes,
 device and contiguity, allocates outputs that were not supplied (torch is
 used for device memory and streams, nothing else), and calls the C entry of
-the same name on the current stream.  Every step of the computation runs in
+the same name with the tensors' device current, on that device's current
+stream unless a stream is given.  Every step of the computation runs in
 the library's HIP kernels.  A missing library raises immediately; there is
 no fallback.
 """
@@ -90,11 +91,23 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream):
+def _run(fn: str, tensors, stream, *args) -> None:
+    """Call C entry `fn` with `args` and the stream appended, with the
+    tensors' device current (the library launches on, and sizes its LDS
+    limits for, the current device).  Every tensor must be on that one
+    device; `stream` defaults to its current stream and must belong to it."""
     torch = _torch()
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+    device = tensors[0].device
+    for t in tensors[1:]:
+        if t.device != device:
+            raise ValueError("%s: tensors on %s and %s; all must be on one device"
+                             % (fn, device, t.device))
+    with torch.cuda.device(device):
+        if stream is None:
+            stream = torch.cuda.current_stream(device)
+        elif stream.device != device:
+            raise ValueError("%s: stream on %s, tensors on %s" % (fn, stream.device, device))
+        _check(fn, getattr(lib(), fn)(*args, ctypes.c_void_p(stream.cuda_stream)))
 
 
 def _req(t, name, dtypes, shape=None):
@@ -131,8 +144,7 @@ def quantize_act_q8_1(x, qs=None, d=None, s=None, stream=None):
     _req(qs, "qs", (torch.int8,), (M, K))
     _req(d, "d", _f16_bits_dtypes(), (M, K // 32))
     _req(s, "s", _f16_bits_dtypes(), (M, K // 32))
-    _check("quantize_act_q8_1",
-           lib().quantize_act_q8_1(_ptr(x), M, K, _ptr(qs), _ptr(d), _ptr(s), _stream(stream)))
+    _run("quantize_act_q8_1", (x, qs, d, s), stream, _ptr(x), M, K, _ptr(qs), _ptr(d), _ptr(s))
     return qs, d, s
 
 
@@ -151,8 +163,8 @@ def mmvq_q4_0(w_qs, w_d, a_qs, a_d, a_s, y=None, stream=None):
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=w_qs.device)
     _req(y, "y", (torch.float32,), (M, N))
-    _check("mmvq_q4_0", lib().mmvq_q4_0(_ptr(w_qs), _ptr(w_d), N, K, _ptr(a_qs), _ptr(a_d),
-                                         _ptr(a_s), M, _ptr(y), _stream(stream)))
+    _run("mmvq_q4_0", (w_qs, w_d, a_qs, a_d, a_s, y), stream, _ptr(w_qs), _ptr(w_d), N, K,
+         _ptr(a_qs), _ptr(a_d), _ptr(a_s), M, _ptr(y))
     return y
 
 
@@ -170,8 +182,8 @@ def mmvq_q4_0_f32act(w_qs, w_d, x, y=None, stream=None):
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=w_qs.device)
     _req(y, "y", (torch.float32,), (M, N))
-    _check("mmvq_q4_0_f32act", lib().mmvq_q4_0_f32act(_ptr(w_qs), _ptr(w_d), N, K, _ptr(x), M,
-                                                       _ptr(y), _stream(stream)))
+    _run("mmvq_q4_0_f32act", (w_qs, w_d, x, y), stream, _ptr(w_qs), _ptr(w_d), N, K, _ptr(x), M,
+         _ptr(y))
     return y
 
 
@@ -191,8 +203,8 @@ def mmvq_q4_k(w_qs, w_hdr, a_qs, a_d, a_s, y=None, stream=None):
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=w_qs.device)
     _req(y, "y", (torch.float32,), (M, N))
-    _check("mmvq_q4_k", lib().mmvq_q4_k(_ptr(w_qs), _ptr(w_hdr), N, K, _ptr(a_qs), _ptr(a_d),
-                                         _ptr(a_s), M, _ptr(y), _stream(stream)))
+    _run("mmvq_q4_k", (w_qs, w_hdr, a_qs, a_d, a_s, y), stream, _ptr(w_qs), _ptr(w_hdr), N, K,
+         _ptr(a_qs), _ptr(a_d), _ptr(a_s), M, _ptr(y))
     return y
 
 
@@ -213,8 +225,8 @@ def mmvq_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d, y=None, stream=None):
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=w_ql.device)
     _req(y, "y", (torch.float32,), (M, N))
-    _check("mmvq_q6_k", lib().mmvq_q6_k(_ptr(w_ql), _ptr(w_qh), _ptr(w_sc), _ptr(w_d), N, K,
-                                         _ptr(a_qs), _ptr(a_d), M, _ptr(y), _stream(stream)))
+    _run("mmvq_q6_k", (w_ql, w_qh, w_sc, w_d, a_qs, a_d, y), stream, _ptr(w_ql), _ptr(w_qh),
+         _ptr(w_sc), _ptr(w_d), N, K, _ptr(a_qs), _ptr(a_d), M, _ptr(y))
     return y
 
 
@@ -232,9 +244,8 @@ def gemv_nvfp4_w4a16(w_codes, w_scales, global_scale, x, y=None, stream=None):
     if y is None:
         y = torch.empty((M, N), dtype=torch.float16, device=x.device)
     _req(y, "y", _f16_bits_dtypes(), (M, N))
-    _check("gemv_nvfp4_w4a16",
-           lib().gemv_nvfp4_w4a16(_ptr(w_codes), _ptr(w_scales), float(global_scale), N, K,
-                                  _ptr(x), M, _ptr(y), _stream(stream)))
+    _run("gemv_nvfp4_w4a16", (w_codes, w_scales, x, y), stream, _ptr(w_codes), _ptr(w_scales),
+         float(global_scale), N, K, _ptr(x), M, _ptr(y))
     return y
 
 
@@ -251,6 +262,6 @@ def gemv_fp8_w8a16(w, channel_scale, x, y=None, stream=None):
     if y is None:
         y = torch.empty((M, N), dtype=torch.float16, device=x.device)
     _req(y, "y", _f16_bits_dtypes(), (M, N))
-    _check("gemv_fp8_w8a16", lib().gemv_fp8_w8a16(_ptr(w), _ptr(channel_scale), N, K, _ptr(x), M,
-                                                   _ptr(y), _stream(stream)))
+    _run("gemv_fp8_w8a16", (w, channel_scale, x, y), stream, _ptr(w), _ptr(channel_scale), N, K,
+         _ptr(x), M, _ptr(y))
     return y

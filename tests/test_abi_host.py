@@ -168,6 +168,21 @@ def test_binding_raises_without_gpu_tensors():
         skinny_gemm_amd.quantize_act_q8_1(torch.zeros((1, 32), dtype=torch.float64))
 
 
+def test_binding_rejects_tensors_on_two_devices():
+    # the check runs before any device context or library call, so stand-ins
+    # that only carry a device are enough
+    import types
+
+    import torch
+
+    from skinny_gemm_amd import _lib
+
+    a = types.SimpleNamespace(device=torch.device("cuda", 0))
+    b = types.SimpleNamespace(device=torch.device("cuda", 1))
+    with pytest.raises(ValueError, match="one device"):
+        _lib._run("mmvq_q4_0", (a, a, b), None)
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     from skinny_gemm_amd import _lib
 
