@@ -640,6 +640,76 @@ def test_staged_activation_limits(fmt, M, K, N):
     check_f16(y, y_acc, mag, K, "%s staged limit M=%d N=%d K=%d" % (fmt, M, N, K))
 
 
+# ------------------------------------------------------------------ seeded random shapes
+
+def random_shapes(seed, count, kmult, kmax, max_m, nk_max=1.6e7, mnk_max=1e8):
+    """(M, N, K) drawn log-uniformly over the valid range of an entry point:
+    N in [1, 40000], K a multiple of kmult up to kmax, M in [1, max_m], sized
+    so that the oracle finishes quickly.  The hand-picked shapes above pin
+    the routing boundaries they name; these reach the combinations between."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    while len(out) < count:
+        K = max(kmult, int(np.exp(rng.uniform(np.log(kmult), np.log(kmax)))) // kmult * kmult)
+        if K >= 256 and rng.uniform() < 0.5:
+            K = K // 256 * 256               # half of them tile the matrix-core chunks
+        M = int(rng.integers(1, max_m + 1))
+        n_max = min(40000.0, nk_max / K, mnk_max / (M * K))
+        if n_max < 1:
+            continue
+        N = int(np.exp(rng.uniform(0.0, np.log(n_max))))
+        out.append((M, max(N, 1), K))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", random_shapes(101, 64, 32, 16384, 8))
+def test_mmvq_q4_0_random_shapes(M, N, K):
+    _check_q4_0(M, N, K)
+
+
+@pytest.mark.parametrize("M,N,K", random_shapes(102, 24, 32, 12288, 2))
+def test_mmvq_q4_0_f32act_random_shapes(M, N, K):
+    w_qs, w_d = inputs.q4_0_weights(N, K, 5 * N + K)
+    x = inputs.normal_f32(M, K, 7 * M + K)
+    y = run_q4_f32act(w_qs, w_d, x)
+    a_qs, a_d, a_s = oracle.quantize_q8_1(x)
+    ref = oracle.mmvq_q4_0(w_qs, w_d, a_qs, a_d, a_s)
+    check_f32(y, ref, q4_mag(w_qs, w_d, a_qs, a_d, a_s), K,
+              "q4_0 f32act M=%d N=%d K=%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M,N,K", random_shapes(103, 64, 32, 20480, 16))
+def test_gemv_nvfp4_random_shapes(M, N, K):
+    codes, scales, g = inputs.nvfp4_weights(N, K, 9 * N + K)
+    x = inputs.normal_f16_bits(M, K, 5 * M + K)
+    y = run_nvfp4(codes, scales, g, x)
+    y_acc, _ = oracle.gemv_nvfp4_w4a16(codes, scales, g, x)
+    check_f16(y, y_acc, nvfp4_mag(codes, scales, g, x), K,
+              "nvfp4 M=%d N=%d K=%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M,N,K", random_shapes(104, 64, 16, 20480, 96))
+def test_gemv_fp8_random_shapes(M, N, K):
+    w, cs = inputs.fp8_weights(N, K, 13 * N + K)
+    x = inputs.normal_f16_bits(M, K, 3 * M + K)
+    y = run_fp8(w, cs, x)
+    y_acc, _ = oracle.gemv_fp8_w8a16(w, cs, x)
+    check_f16(y, y_acc, fp8_mag(w, cs, x), K, "fp8 M=%d N=%d K=%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M,N,K", random_shapes(105, 32, 256, 16384, 8))
+def test_k_quants_random_shapes(M, N, K):
+    w_qs, w_hdr = inputs.q4_k_weights(N, K, 3 * N + K)
+    w_ql, w_qh, w_sc, w_d = inputs.q6_k_weights(N, K, 5 * N + K)
+    x = inputs.normal_f32(M, K, 11 * M + K)
+    a_qs, a_d, a_s = oracle.quantize_q8_1(x)
+    check_f32(run_q4_k(w_qs, w_hdr, a_qs, a_d, a_s), oracle.mmvq_q4_k(w_qs, w_hdr, a_qs, a_d, a_s),
+              q4_k_mag(w_qs, w_hdr, a_qs, a_d, a_s), K, "q4_k M=%d N=%d K=%d" % (M, N, K))
+    check_f32(run_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d),
+              oracle.mmvq_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d),
+              q6_k_mag(w_ql, w_qh, w_sc, w_d, a_qs, a_d), K, "q6_k M=%d N=%d K=%d" % (M, N, K))
+
+
 # ------------------------------------------------------------------ full sizes (sampled rows)
 
 LLAMA_Q4 = [(12288, 4096), (4096, 4096), (22016, 4096), (4096, 11008), (32000, 4096)]
