@@ -478,7 +478,9 @@ __global__ __launch_bounds__(64 * WR * KS) void gemv_nvfp4_mfma_kernel(
   auto load = [&](int c, R &rg) {
 #pragma unroll
     for (int q = 0; q < C::kCi; ++q) rg.c[q] = load16_nt(csrc[q] + (size_t)c * (64 * S));
-    rg.s = load16_nt(ssrc + (size_t)c * (8 * S));
+    // a chunk takes 8 S bytes of each row's scales, part of a 128-byte line:
+    // the default cache policy keeps the rest of the line for the next chunks
+    rg.s = load16(ssrc + (size_t)c * (8 * S));
 #pragma unroll
     for (int u = 0; u < C::kApw; ++u) rg.a[u] = load16(asrc[u] + (size_t)c * (128 * S));
     issue_fence();   // keep each chunk's loads together and ahead of later work
