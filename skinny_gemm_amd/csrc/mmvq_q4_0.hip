@@ -300,9 +300,7 @@ __global__ __launch_bounds__(64 * WR * KS) void mmvq_q4_0_mfma_kernel(
   auto load = [&](int c, R &rg) {
 #pragma unroll
     for (int q = 0; q < C::kCi; ++q) rg.c[q] = load16_nt(csrc[q] + (size_t)c * C::kCB);
-    // a chunk takes 4 S bytes of each row's scales, part of a 128-byte line:
-    // the default cache policy keeps the rest of the line for the next chunks
-    rg.ws = load16(wssrc + (size_t)c * (4 * S));
+    rg.ws = load16_nt(wssrc + (size_t)c * (4 * S));
 #pragma unroll
     for (int u = 0; u < C::kApw; ++u)
       rg.a[u] = load16(asrc[u] + (size_t)c * (apiece[u] < C::kAi ? 64 * S : 4 * S));
