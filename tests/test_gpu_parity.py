@@ -806,6 +806,59 @@ def test_repeat_runs_bit_identical_and_side_stream():
         assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
 
 
+def test_concurrent_host_threads_on_their_own_streams():
+    # four host threads call the library at once, each on its own stream and
+    # at its own M (so through different kernel families); every thread's
+    # results must equal the same calls made alone
+    import threading
+
+    import torch
+
+    import skinny_gemm_amd as sk
+
+    d = torch.device("cuda:0")
+    N, K = 3000, 4096
+    w_qs, w_d = inputs.q4_0_weights_torch(N, K, 31, d)
+    codes, scales = inputs.nvfp4_weights_torch(N, K, 32, d)
+    w8, cs = inputs.fp8_weights_torch(N, K, 33, d)
+    xs = {M: (inputs.normal_f32_torch(M, K, 40 + M, d), inputs.normal_f16_torch(M, K, 50 + M, d))
+          for M in (1, 2, 8, 16)}
+
+    def work(M):
+        xf, xh = xs[M]
+        out = []
+        if M <= 8:
+            qs, dd, ss = sk.quantize_act_q8_1(xf)
+            out.append(sk.mmvq_q4_0(w_qs, w_d, qs, dd, ss))
+        out.append(sk.gemv_nvfp4_w4a16(codes, scales, 1.0, xh))
+        out.append(sk.gemv_fp8_w8a16(w8, cs, xh))
+        return out
+
+    alone = {M: [host(t).view(np.uint8).copy() for t in work(M)] for M in xs}
+    got, errors = {}, []
+
+    def run(M):
+        try:
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                res = [work(M) for _ in range(5)]
+            stream.synchronize()
+            got[M] = [[t.cpu().numpy().view(np.uint8) for t in r] for r in res]
+        except Exception as e:          # reported below, on the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=run, args=(M,)) for M in xs]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for M in xs:
+        for r in got[M]:
+            for u, v in zip(r, alone[M]):
+                assert np.array_equal(u, v), M
+
+
 def test_graph_replays_match_eager():
     # every entry point, at M values that reach each kernel family, captured
     # in one HIP graph; each replay (with eager work and synchronizations in
