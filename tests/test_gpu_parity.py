@@ -875,6 +875,8 @@ def test_graph_replays_match_eager():
     ql, qh, sc, dd = inputs.q6_k_weights_torch(N, K, 23, d)
     codes, scales = inputs.nvfp4_weights_torch(N, K, 24, d)
     w8, cs = inputs.fp8_weights_torch(N, K, 25, d)
+    fc, fs = inputs.nvfp4_weights_torch(8192, 5120, 26, d)   # the flat NVFP4 mapping (M = 1)
+    fx = inputs.normal_f16_torch(1, 5120, 27, d)
     xf = {M: inputs.normal_f32_torch(M, K, 30 + M, d) for M in (1, 2, 8)}
     xh = {M: inputs.normal_f16_torch(M, K, 40 + M, d) for M in (1, 2, 4, 8, 32)}
     q8 = {M: sk.quantize_act_q8_1(xf[M]) for M in (1, 2, 8)}
@@ -891,6 +893,7 @@ def test_graph_replays_match_eager():
             outs.append(sk.mmvq_q4_0_f32act(w_qs, w_d, xf[M]))
         for M in (1, 2, 4, 8):
             outs.append(sk.gemv_nvfp4_w4a16(codes, scales, 1.0, xh[M]))
+        outs.append(sk.gemv_nvfp4_w4a16(fc, fs, 1.0, fx))
         for M in (1, 2, 4, 8, 32):
             outs.append(sk.gemv_fp8_w8a16(w8, cs, xh[M]))
 
