@@ -11,9 +11,9 @@
 // Mapping (one wave = R weight rows, full K): lane l takes 16-element
 // chunks c = l, l + 64, ...: one 128-bit weight load per row, the chunk's
 // activations (M x 32 B) loaded once and reused for all R rows, and a
-// transposing butterfly for the R*M partial sums at the end.  At M <= 4 the
-// same mapping runs with the activation rows staged in LDS once per
-// workgroup (gemv_fp8_lds_kernel).
+// transposing butterfly for the R*M partial sums at the end.  At M <= 5
+// (and M = 6 on narrow matrices) the same mapping runs with the activation
+// rows staged in LDS once per workgroup (gemv_fp8_lds_kernel).
 // Bytes per call: N*K + 4*N weights and scales + 2*M*K + 2*M*N.
 #include "device.h"
 #include "launch.h"
@@ -495,7 +495,7 @@ static hipError_t launch_mfma(const uint8_t *w, const float *cs, int N, int K, c
   }
 }
 
-// Vector kernel with the activation rows staged in LDS (M <= 4, M K <= 80 K
+// Vector kernel with the activation rows staged in LDS (M <= 6, M K <= 80 K
 // elements).  The plain vector kernel reads each lane's activation bytes
 // through the vector memory path once per wave, M bytes per weight byte at
 // two rows per wave, and that path bounds it before HBM does.  Here a
@@ -618,11 +618,15 @@ static hipError_t launch_m(const uint8_t *w, const float *cs, int N, int K, cons
   }
 }
 
-// Staged-activation vector kernel (M <= 4): three rows per wave, eight
-// waves per workgroup (measured on MI355X over K 5120 and 17408, N 5120 to
-// 34816: 17408 x 5120 at M = 1 18.3 -> 16.0 us, 5120 x 34816 at M = 2 33.6
-// -> 28.3 us; at M = 3 and 4 on par with or ahead of the matrix cores).
-constexpr int kF8LdsMaxM = 4;
+// Staged-activation vector kernel (M <= 5, and M = 6 on narrow matrices):
+// three rows per wave, eight waves per workgroup (measured on MI355X over K
+// 5120 and 17408, N 5120 to 34816: 17408 x 5120 at M = 1 18.3 -> 16.0 us,
+// 5120 x 34816 at M = 2 33.6 -> 28.3 us; at M = 3 and 4 on par with or ahead
+// of the matrix cores; at M = 5 5120 x 5120 9.9 -> 8.4 us, 5120 x 10240 13.5
+// -> 12.9 us, 5120 x 34816 37.0 -> 36.3 us; at M = 6 only 5120 x 5120 gains,
+// 9.8 -> 8.4 us, and at M = 8 none).
+constexpr int kF8LdsMaxM = 6;
+constexpr int kF8LdsNarrowN = 8192;         // M = 6: staged only up to this N
 constexpr int kF8LdsMaxMK = 80 * 1024;      // M K binary16 activations in LDS
 
 template <int M, int A, int R = 3, int W = 8>
@@ -663,19 +667,22 @@ static hipError_t launch_vector(const uint8_t *w, const float *cs, int N, int K,
   }
 }
 
-// M <= 4 takes the staged-activation vector kernel while the rows fit in
-// LDS.  The matrix-core kernel takes every other M >= 3 in one weight pass
+// M <= 5 (M = 6 on narrow matrices) takes the staged-activation vector
+// kernel while the rows fit in LDS.  The matrix-core kernel takes every
+// other M >= 3 in one weight pass
 // when K is a whole number of 256-element chunks.  Otherwise the plain
 // vector kernel serves up to 8 rows per pass over the weights: rows 1..8,
 // 9..16, ...
 hipError_t launch_gemv_fp8(const uint8_t *w, const float *cs, int N, int K, const uint16_t *x,
                            int M, uint16_t *y, hipStream_t stream) {
-  if (M <= kF8LdsMaxM && M * K <= kF8LdsMaxMK) {
+  if (M <= kF8LdsMaxM && M * K <= kF8LdsMaxMK && (M < 6 || N <= kF8LdsNarrowN)) {
     switch (M) {
       case 1: return launch_lds<1>(w, cs, N, K, x, y, stream);
       case 2: return launch_lds<2>(w, cs, N, K, x, y, stream);
       case 3: return launch_lds<3>(w, cs, N, K, x, y, stream);
-      default: return launch_lds<4>(w, cs, N, K, x, y, stream);
+      case 4: return launch_lds<4>(w, cs, N, K, x, y, stream);
+      case 5: return launch_lds<5>(w, cs, N, K, x, y, stream);
+      default: return launch_lds<6>(w, cs, N, K, x, y, stream);
     }
   }
   if (M >= kFp8MfmaMinM && K % 256 == 0) return launch_mfma(w, cs, N, K, x, M, y, stream);

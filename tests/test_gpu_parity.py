@@ -592,8 +592,8 @@ def test_gemv_fp8_every_code_bit_exact():
         x[m, m] = 1.0
         x[m, m + 8] = 1.0
     xb = x.view(np.uint16)
-    # M <= 4: the staged-activation kernel; M = 8: the plain one
-    for M in (1, 2, 3, 4, 8):
+    # M <= 6: the staged-activation kernel; M = 8: the plain one
+    for M in (1, 2, 3, 4, 5, 6, 8):
         y = run_fp8(w, cs, xb[:M])
         _, want = oracle.gemv_fp8_w8a16(w, cs, xb[:M])
         assert np.array_equal(y, want), M
@@ -623,7 +623,8 @@ def test_gemv_fp8_sixteen_rows_bit_exact():
     # activations staged in LDS up to M K = 80 K elements: at the limit the
     # staging takes several batches per thread; just past it, the plain kernel
     ("nvfp4", 1, 81920), ("nvfp4", 1, 81952), ("nvfp4", 2, 40960), ("nvfp4", 2, 40992),
-    ("fp8", 1, 81920), ("fp8", 3, 27296), ("fp8", 4, 20480), ("fp8", 4, 20496)])
+    ("fp8", 1, 81920), ("fp8", 3, 27296), ("fp8", 4, 20480), ("fp8", 4, 20496),
+    ("fp8", 5, 16384), ("fp8", 5, 16400), ("fp8", 6, 13648), ("fp8", 6, 13664)])
 @pytest.mark.parametrize("N", [5, 37])
 def test_staged_activation_limits(fmt, M, K, N):
     x = inputs.normal_f16_bits(M, K, 7 * M + N, std=0.25)
