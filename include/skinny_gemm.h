@@ -175,8 +175,9 @@ int mmvq_q4_k(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
  * For each m, n:  y = sum_b d d8_b (sc_2b isum_lo + sc_2b+1 isum_hi), the
  * isums over the two 16-element halves of block b with codes q - 32 (exact
  * integers; the Q8_1 sum term is not used).  Accumulated in float32.
- *   w_ql, a_qs 16-byte aligned; w_qh 8-byte aligned; w_sc, w_d, a_d
- *   2-byte aligned; y float32 [M][N], 4-byte aligned.
+ *   w_ql, a_qs, a_d 16-byte aligned (a_d is read with 128-bit loads on
+ *   some paths); w_qh 8-byte aligned; w_sc, w_d 2-byte aligned; y float32
+ *   [M][N], 4-byte aligned.
  *   0 <= M <= SKINNY_MAX_M_GEMV; K % 256 == 0.
  */
 int mmvq_q6_k(const uint8_t *w_ql, const uint8_t *w_qh, const int8_t *w_sc,

@@ -103,7 +103,7 @@ int mmvq_q6_k(const uint8_t *w_ql, const uint8_t *w_qh, const int8_t *w_sc, cons
   if (M == 0 || N == 0) return SKINNY_OK;
   if (!w_ql || !w_qh || !w_sc || !w_d || !a_qs || !a_d || !y) return SKINNY_ERR_NULL;
   if (!aligned(w_ql, 16) || !aligned(w_qh, 8) || !aligned(w_sc, 2) || !aligned(w_d, 2) ||
-      !aligned(a_qs, 16) || !aligned(a_d, 2) || !aligned(y, 4))
+      !aligned(a_qs, 16) || !aligned(a_d, 16) || !aligned(y, 4))
     return SKINNY_ERR_ALIGN;
   return launched(skinny::launch_mmvq_q6_k(w_ql, w_qh, w_sc, w_d, N, K, a_qs, a_d, M, y,
                                            (hipStream_t)stream));

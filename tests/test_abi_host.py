@@ -225,7 +225,7 @@ def test_k_quant_null_and_alignment(L):
         assert q4k(L, **{kw: A + off}) == -3, kw
     for kw in ("ql", "qh", "sc", "d", "aq", "ad", "y"):
         assert q6k(L, **{kw: 0}) == -1, kw
-    for kw, off in (("ql", 8), ("qh", 4), ("sc", 1), ("d", 1), ("aq", 8), ("ad", 1), ("y", 2)):
+    for kw, off in (("ql", 8), ("qh", 4), ("sc", 1), ("d", 1), ("aq", 8), ("ad", 8), ("y", 2)):
         assert q6k(L, **{kw: A + off}) == -3, kw
     # the weaker requirements really are weaker
     assert q6k(L, qh=A + 8, y=0) == -1
