@@ -263,6 +263,139 @@ __global__ __launch_bounds__(256) void mmvq_q6_k_kernel(
   kq_store<R, M>(acc, lane, n0, N, y);
 }
 
+// Q4_K with the Q8_1 activation rows staged in LDS once per workgroup
+// (M >= 3, matrices up to N = 16383): codes int8 [M][K], then d8 and s8 as
+// float [M][K/32] each.  The mapping, header sharing and per-block
+// arithmetic are mmvq_q4_k_kernel's; as in the staged Q6_K kernel below,
+// activations are loaded once per workgroup (issued first, first batch
+// stored while the first weight round is in flight, one barrier) and the
+// rounds of one block per lane alternate two register buffers.
+template <int M, int R, int W, int A>
+__global__ __launch_bounds__(64 * W) void mmvq_q4_k_lds_kernel(
+    const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K, const int8_t *a_qs,
+    const uint16_t *a_d, const uint16_t *a_s, float *y) {
+  extern __shared__ uint4_t smem4[];
+  int8_t *lq = reinterpret_cast<int8_t *>(smem4);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // row addresses stay scalar
+  const int nb = K >> 5;
+  float *ld8 = reinterpret_cast<float *>(lq + M * K);
+  float *ls8 = ld8 + M * nb;
+  const int n0 = (blockIdx.x * W + wave) * R;
+  // 16-byte pieces: codes (M K / 16), d8 (M nb / 8), s8 (M nb / 8)
+  const int ncode = M * K / 16, nd = M * nb / 8, npieces = ncode + 2 * nd;
+  auto piece = [&](int p) {
+    return p < ncode ? reinterpret_cast<const uint8_t *>(a_qs) + 16 * (size_t)p
+         : p < ncode + nd ? reinterpret_cast<const uint8_t *>(a_d) + 16 * (size_t)(p - ncode)
+                          : reinterpret_cast<const uint8_t *>(a_s) + 16 * (size_t)(p - ncode - nd);
+  };
+  uint4_t av[A];
+#pragma unroll
+  for (int a = 0; a < A; ++a) av[a] = load16(piece(min(tid + a * W * kWave, npieces - 1)));
+  issue_fence();
+
+  const int nw = min(n0, N - 1);            // waves past N read row N - 1 and store nothing
+  const uint8_t *wrow[R];
+  const uint8_t *hrow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int n = min(nw + r, N - 1);
+    wrow[r] = w_qs + (size_t)n * (size_t)(K >> 1);
+    hrow[r] = w_hdr + (size_t)n * (size_t)(K >> 8) * 16;
+  }
+  const int j = lane & 7;                   // sub-block of the lane's blocks
+  const int s_sh = 8 * (j & 3);
+  const int h_sh = 8 * (j >> 1) + 4 * (j & 1);
+  const int hq = (lane & 3) == 0 ? 0 : (lane & 3) == 1 ? 1 + (j >> 2) : 3;   // dword loaded
+  struct Round {
+    uint4_t wq[R];
+    uint32_t hw[R];
+  };
+  auto load = [&](int b, Round &rd) {
+    b = min(b, nb - 1);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      rd.wq[r] = load16_nt(wrow[r] + 16 * b);
+      rd.hw[r] = __builtin_nontemporal_load(
+          reinterpret_cast<const uint32_t *>(hrow[r] + 16 * (b >> 3)) + hq);
+    }
+  };
+  Round r0, r1;
+  load(lane, r0);
+  issue_fence();
+  auto store = [&](int p0) {
+#pragma unroll
+    for (int a = 0; a < A; ++a) {
+      const int p = p0 + tid + a * W * kWave;
+      if (p < ncode) {
+        *reinterpret_cast<uint4_t *>(lq + 16 * p) = av[a];
+      } else if (p < npieces) {
+        float *dst = p < ncode + nd ? ld8 + 8 * (p - ncode) : ls8 + 8 * (p - ncode - nd);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          dst[e] = f16_bits_to_f32((uint16_t)(av[a][e >> 1] >> (16 * (e & 1))));
+      }
+    }
+  };
+  store(0);                                 // straight-line: waits only for the activations
+  for (int p0 = A * W * kWave; p0 < npieces; p0 += A * W * kWave) {
+#pragma unroll
+    for (int a = 0; a < A; ++a) av[a] = load16(piece(min(p0 + tid + a * W * kWave, npieces - 1)));
+    store(p0);
+  }
+  wg_barrier();
+  if (n0 >= N) return;
+
+  float acc[R][M];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+  auto compute = [&](int b, const Round &rd) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t h0 = quad_lane<0>(rd.hw[r]);
+      const uint32_t pb = quad_lane<1>(rd.hw[r]) >> s_sh;
+      const uint32_t h3 = quad_lane<2>(rd.hw[r]);
+      const uint32_t sc = pb & 63u;
+      const uint32_t mn = ((pb >> 6) & 3u) | (((h3 >> h_sh) & 15u) << 2);
+      const float dsc = f16_bits_to_f32((uint16_t)(h0 & 0xFFFFu)) * (float)sc;
+      const float dmm = f16_bits_to_f32((uint16_t)(h0 >> 16)) * (float)mn;
+      uint32_t lo[4], hi[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo[i] = rd.wq[r][i] & 0x0F0F0F0Fu;
+        hi[i] = (rd.wq[r][i] >> 4) & 0x0F0F0F0Fu;
+      }
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const uint4_t aq0 = *reinterpret_cast<const uint4_t *>(lq + (size_t)m * K + 32 * b);
+        const uint4_t aq1 = *reinterpret_cast<const uint4_t *>(lq + (size_t)m * K + 32 * b + 16);
+        int32_t isum = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          isum = dot4_i8(lo[i], aq0[i], isum);
+          isum = dot4_i8(hi[i], aq1[i], isum);
+        }
+        const float t = fmaf(dsc * ld8[m * nb + b], (float)isum, -(dmm * ls8[m * nb + b]));
+        acc[r][m] = acc[r][m] + t;
+      }
+    }
+  };
+  // blocks b = lane, lane + 64, ...: the two round buffers alternate (nb is a
+  // multiple of 8, so a quad enters and leaves the loop together)
+  for (int b = lane; b < nb; b += 2 * kWave) {
+    if (b + kWave < nb) load(b + kWave, r1);
+    issue_fence();
+    compute(b, r0);
+    if (b + kWave >= nb) break;
+    if (b + 2 * kWave < nb) load(b + 2 * kWave, r0);
+    issue_fence();
+    compute(b + kWave, r1);
+  }
+  kq_store<R, M>(acc, lane, n0, N, y);
+}
+
 // Q6_K with the Q8_1 activation rows staged in LDS once per workgroup
 // (3 <= M <= 8): codes int8 [M][K] then d8 float [M][K/32].  The plain
 // kernel re-reads each lane's activation blocks from L2 for every R rows,
@@ -469,15 +602,69 @@ static hipError_t launch_q6k_m(const uint8_t *w_ql, const uint8_t *w_qh, const i
 #undef SKINNY_Q6K
 }
 
-// From M = 5 the Q4_0 matrix-core kernel takes Q4_K (its header array has
-// the geometry of the Q4_0 block scales), except mid-width short matrices.
-// Measured on MI355X over the Qwen3-8B projections at M = 8: 4096 x 24576
-// 2.5 -> 3.5, 12288 x 4096 1.9 -> 2.3, 4096 x 4096 1.46 -> 1.54 TB/s on the
-// matrix cores, while 4096 x 6144 (384 tiles) and every shape at M = 4 keep
-// the vector kernel.
+// Routing.  From M = 3 matrices below N = 16384 take the staged kernel (when
+// the activation rows fit in LDS).  Wider ones take, from M = 5, the Q4_0
+// matrix-core kernel (its header array has the geometry of the Q4_0 block
+// scales; 4096 x 24576 at M = 8 2.5 -> 3.5 TB/s there), and below that the
+// plain vector kernel.  Shapes the staged kernel cannot hold keep the
+// earlier rule: the matrix cores from M = 5 except mid-width short matrices.
+// Staged Q4_K (3 <= M <= 8, N < 16384): three rows per wave on mid-width
+// matrices, two otherwise, eight waves per workgroup (measured on MI355X over
+// the Qwen3-8B projections at M = 3..8: 4096 x 4096 at M = 5 5.9 -> 4.9 us,
+// 12288 x 4096 at M = 4 10.3 -> 8.9 us, 4096 x 6144 at M = 8 8.1 -> 7.3 us;
+// 4096 x 24576 is faster on the other kernels from M = 4 and keeps them).
+constexpr int kQ4kLdsMaxN = 16383;
+
+static int q4k_lds_bytes(int M, int K) { return M * K + 8 * M * (K >> 5); }
+
+template <int M, int R, int A>
+static hipError_t launch_q4k_lds_a(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
+                                   const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
+                                   float *y, hipStream_t stream) {
+  constexpr int W = 8;
+  const int lds = q4k_lds_bytes(M, K);
+  const hipError_t lds_ok = allow_lds((const void *)mmvq_q4_k_lds_kernel<M, R, W, A>, lds);
+  if (lds_ok != hipSuccess) return lds_ok;
+  const int rows = R * W;
+  hipLaunchKernelGGL((mmvq_q4_k_lds_kernel<M, R, W, A>), dim3((N + rows - 1) / rows),
+                     dim3(64 * W), lds, stream, w_qs, w_hdr, N, K, a_qs, a_d, a_s, y);
+  return hipGetLastError();
+}
+
+template <int M, int R>
+static hipError_t launch_q4k_lds_r(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
+                                   const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
+                                   float *y, hipStream_t stream) {
+  const int pieces = M * K / 16 + 2 * (M * (K >> 5) / 8);
+  const int per_thread = (pieces + 511) / 512;   // first staging batch
+#define SKINNY_Q4L(A) \
+  return launch_q4k_lds_a<M, R, A>(w_qs, w_hdr, N, K, a_qs, a_d, a_s, y, stream)
+  if (per_thread <= 4) SKINNY_Q4L(4);
+  if (per_thread <= 8) SKINNY_Q4L(8);
+  SKINNY_Q4L(16);
+#undef SKINNY_Q4L
+}
+
+template <int M>
+static hipError_t launch_q4k_lds(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
+                                 const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
+                                 float *y, hipStream_t stream) {
+  if (N > 4096) return launch_q4k_lds_r<M, 3>(w_qs, w_hdr, N, K, a_qs, a_d, a_s, y, stream);
+  return launch_q4k_lds_r<M, 2>(w_qs, w_hdr, N, K, a_qs, a_d, a_s, y, stream);
+}
+
 hipError_t launch_mmvq_q4_k(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
                             const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s, int M,
                             float *y, hipStream_t stream) {
+  if (M >= 3 && N <= kQ4kLdsMaxN && q4k_lds_bytes(M, K) <= 160 * 1024) {
+    switch (M) {
+#define SKINNY_Q4L(MM) \
+  case MM: return launch_q4k_lds<MM>(w_qs, w_hdr, N, K, a_qs, a_d, a_s, y, stream);
+      SKINNY_Q4L(3) SKINNY_Q4L(4) SKINNY_Q4L(5) SKINNY_Q4L(6) SKINNY_Q4L(7)
+#undef SKINNY_Q4L
+      default: return launch_q4k_lds<8>(w_qs, w_hdr, N, K, a_qs, a_d, a_s, y, stream);
+    }
+  }
   const int tiles = (N + 15) / 16;
   if (M >= 5 && (tiles >= 512 || tiles <= 256 || K >= 8192))
     return launch_mmvq_q4_k_mfma(w_qs, w_hdr, N, K, a_qs, a_d, a_s, M, y, stream);
