@@ -675,6 +675,173 @@ __global__ __launch_bounds__(64 * W) void mmvq_q4_0_lds_kernel(
   }
 }
 
+// Staged kernel in rounds (3 <= M <= 8, narrow matrices): the activation
+// rows are staged in LDS as above (codes int8 [M][K] | d8 float | 8 s8
+// float), but each lane then walks its blocks b = lane, lane + 64, ... one
+// per round, two register buffers alternating, so a wave holds two blocks
+// per row in flight instead of its whole share of K; the per-block dot and
+// epilogue are the plain kernel's.
+template <int M, int R, int W, int A>
+__global__ __launch_bounds__(64 * W) void mmvq_q4_0_lds_rounds_kernel(
+    const uint8_t *w_qs, const uint16_t *w_d, int N, int K, const int8_t *a_qs,
+    const uint16_t *a_d, const uint16_t *a_s, float *y) {
+  extern __shared__ uint4_t smem4[];
+  int8_t *lq = reinterpret_cast<int8_t *>(smem4);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // row addresses stay scalar
+  const int nb = K >> 5;
+  float *ld8 = reinterpret_cast<float *>(lq + M * K);
+  float *ls8 = ld8 + M * nb;
+  const int n0 = (blockIdx.x * W + wave) * R;
+  // 16-byte pieces: codes (M K / 16), d (M nb / 8), s (M nb / 8)
+  const int ncode = M * K / 16, nd = M * nb / 8, npieces = ncode + 2 * nd;
+  auto piece = [&](int p) {
+    return p < ncode ? reinterpret_cast<const uint8_t *>(a_qs) + 16 * (size_t)p
+         : p < ncode + nd ? reinterpret_cast<const uint8_t *>(a_d) + 16 * (size_t)(p - ncode)
+                          : reinterpret_cast<const uint8_t *>(a_s) + 16 * (size_t)(p - ncode - nd);
+  };
+  uint4_t av[A];
+#pragma unroll
+  for (int a = 0; a < A; ++a) av[a] = load16(piece(min(tid + a * W * kWave, npieces - 1)));
+  issue_fence();
+
+  const int nw = min(n0, N - 1);            // waves past N read row N - 1 and store nothing
+  const uint8_t *wrow[R];
+  const uint16_t *drow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int n = min(nw + r, N - 1);
+    wrow[r] = w_qs + (size_t)n * (size_t)(K >> 1);
+    drow[r] = w_d + (size_t)n * (size_t)nb;
+  }
+  struct Round {
+    uint4_t wq[R];
+    uint16_t d4[R];
+  };
+  auto load = [&](int b, Round &rd) {
+    b = min(b, nb - 1);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      rd.wq[r] = load16_nt(wrow[r] + 16 * b);
+      rd.d4[r] = load_u16_nt(drow[r] + b);
+    }
+  };
+  Round r0, r1;
+  load(lane, r0);
+  issue_fence();
+  auto store = [&](int p0) {
+#pragma unroll
+    for (int a = 0; a < A; ++a) {
+      const int p = p0 + tid + a * W * kWave;
+      if (p < ncode) {
+        *reinterpret_cast<uint4_t *>(lq + 16 * p) = av[a];
+      } else if (p < npieces) {
+        const bool isd = p < ncode + nd;
+        float *dst = isd ? ld8 + 8 * (p - ncode) : ls8 + 8 * (p - ncode - nd);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = f16_bits_to_f32((uint16_t)(av[a][e >> 1] >> (16 * (e & 1))));
+          dst[e] = isd ? v : 8.0f * v;
+        }
+      }
+    }
+  };
+  store(0);                                 // straight-line: waits only for the activations
+  for (int p0 = A * W * kWave; p0 < npieces; p0 += A * W * kWave) {
+#pragma unroll
+    for (int a = 0; a < A; ++a) av[a] = load16(piece(min(p0 + tid + a * W * kWave, npieces - 1)));
+    store(p0);
+  }
+  wg_barrier();
+  if (n0 >= N) return;
+
+  float acc[R][M];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+  auto compute = [&](int b, const Round &rd) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      uint32_t lo[4], hi[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo[i] = rd.wq[r][i] & 0x0F0F0F0Fu;
+        hi[i] = (rd.wq[r][i] >> 4) & 0x0F0F0F0Fu;
+      }
+      const float d4 = f16_bits_to_f32(rd.d4[r]);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const uint4_t aq0 = *reinterpret_cast<const uint4_t *>(lq + (size_t)m * K + 32 * b);
+        const uint4_t aq1 = *reinterpret_cast<const uint4_t *>(lq + (size_t)m * K + 32 * b + 16);
+        int32_t isum = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          isum = dot4_i8(lo[i], aq0[i], isum);
+          isum = dot4_i8(hi[i], aq1[i], isum);
+        }
+        const float t = fmaf(ld8[m * nb + b], (float)isum, -ls8[m * nb + b]);
+        acc[r][m] = fmaf(d4, t, acc[r][m]);
+      }
+    }
+  };
+  for (int b = lane; b < nb; b += 2 * kWave) {
+    if (b + kWave < nb) load(b + kWave, r1);
+    issue_fence();
+    compute(b, r0);
+    if (b + kWave >= nb) break;
+    if (b + 2 * kWave < nb) load(b + 2 * kWave, r0);
+    issue_fence();
+    compute(b + kWave, r1);
+  }
+
+  constexpr int V = next_pow2(R * M);
+  float v[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) v[i] = (i < R * M) ? acc[i / M][i % M] : 0.0f;
+  const float total = wave_reduce_transpose<V>(v, lane);
+  constexpr int SHIFT = 6 - Log2<V>::value;
+  const int idx = lane >> SHIFT;
+  if ((lane & ((1 << SHIFT) - 1)) == 0 && idx < R * M) {
+    const int r = idx / M, m = idx % M;
+    const int n = n0 + r;
+    if (n < N) y[(size_t)m * N + n] = total;
+  }
+}
+
+template <int M, int A>
+static hipError_t launch_lds_rounds_a(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
+                                      const int8_t *a_qs, const uint16_t *a_d,
+                                      const uint16_t *a_s, float *y, hipStream_t stream) {
+  constexpr int R = 2, W = 8;
+  const int lds = M * K + 8 * M * (K >> 5);
+  const hipError_t lds_ok = allow_lds((const void *)mmvq_q4_0_lds_rounds_kernel<M, R, W, A>, lds);
+  if (lds_ok != hipSuccess) return lds_ok;
+  const int rows = R * W;
+  hipLaunchKernelGGL((mmvq_q4_0_lds_rounds_kernel<M, R, W, A>), dim3((N + rows - 1) / rows),
+                     dim3(64 * W), lds, stream, w_qs, w_d, N, K, a_qs, a_d, a_s, y);
+  return hipGetLastError();
+}
+
+// Two rows per wave, eight waves (measured on MI355X over the Llama-2-7B
+// shapes: 11008 x 4096 at M = 4 9.4 -> 8.5 us, at M = 8 11.8 -> 11.2 us on the
+// matrix cores; 4096 x 4096 at M = 6 5.25 -> 4.8 us; wider matrices lose
+// from M = 6 and keep the other kernels).
+constexpr int kQ4RoundsMaxN = 4096;
+
+static int lds_rounds_bytes(int M, int K) { return M * K + 8 * M * (K >> 5); }
+
+template <int M>
+static hipError_t launch_lds_rounds(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
+                                    const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
+                                    float *y, hipStream_t stream) {
+  const int pieces = M * K / 16 + 2 * (M * (K >> 5) / 8);
+  const int per_thread = (pieces + 511) / 512;   // first staging batch
+  if (per_thread <= 4) return launch_lds_rounds_a<M, 4>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+  if (per_thread <= 8) return launch_lds_rounds_a<M, 8>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+  return launch_lds_rounds_a<M, 16>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+}
+
 template <int M, int U, bool FUSED, int W = 8>
 static hipError_t launch_lds_u(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                                const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
@@ -756,13 +923,27 @@ static hipError_t launch_lds_plain(const uint8_t *w_qs, const uint16_t *w_d, int
 hipError_t launch_mmvq_q4_0(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                             const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
                             int M, float *y, hipStream_t stream) {
-  // M = 3..5, and narrow matrices at M = 6..8: the activation rows staged in
-  // LDS once per workgroup beat the matrix cores (measured on MI355X over the
-  // Llama-2-7B shapes: 4096 x 22016 at M = 3 15.0 -> 10.8 us, at M = 4 15.2
-  // -> 12.9 us, at M = 5 14.2 -> 13.1 us; 4096 x 4096 at M = 8 6.3 -> 5.5
-  // us; wider M on wider matrices stays on the matrix cores).
+  // M = 3..5 on wider matrices: the activation rows staged in LDS once per
+  // workgroup beat the matrix cores (measured on MI355X over the Llama-2-7B
+  // shapes: 4096 x 22016 at M = 3 15.0 -> 10.8 us, at M = 4 15.2 -> 12.9 us,
+  // at M = 5 14.2 -> 13.1 us; wider M on wider matrices stays on the matrix
+  // cores).  Narrow matrices took the same kernel at M = 6..8 (4096 x 4096 at
+  // M = 8 6.3 -> 5.5 us) before the staged kernel in rounds above.
   // The plain staging copies the Q8_1 scales in 16-byte pieces of 8, so it
   // needs M * K / 32 to be a multiple of 8.
+  // narrow matrices from M = 3: the staged kernel in rounds (M nb / 8 whole
+  // 16-byte pieces of scales)
+  if (M >= 3 && N <= kQ4RoundsMaxN && (M * (K >> 5)) % 8 == 0 &&
+      lds_rounds_bytes(M, K) <= 160 * 1024) {
+    switch (M) {
+      case 3: return launch_lds_rounds<3>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+      case 4: return launch_lds_rounds<4>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+      case 5: return launch_lds_rounds<5>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+      case 6: return launch_lds_rounds<6>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+      case 7: return launch_lds_rounds<7>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+      default: return launch_lds_rounds<8>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+    }
+  }
   const bool lds_ok = K <= kLdsMaxK && (M * (K >> 5)) % 8 == 0;
   const bool narrow = N <= 4096 && K <= 4096;
   if (M >= 3 && lds_ok && (M <= 5 || narrow)) {
