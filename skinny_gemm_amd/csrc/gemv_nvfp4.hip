@@ -683,6 +683,11 @@ static hipError_t launch_lds_a(const uint8_t *codes, const uint8_t *scales, floa
   return hipGetLastError();
 }
 
+// At M = 3 it also beats the matrix cores on matrices up to N = 5120
+// (5120 x 5120 7.6 -> 6.8 us, 17408 x 5120 17.2 -> 16.4 us; wider matrices
+// and M = 4 stay on the matrix cores).
+constexpr int kNvLdsM3MaxN = 5120;
+
 template <int M>
 static hipError_t launch_lds(const uint8_t *codes, const uint8_t *scales, float g, int N, int K,
                              const uint16_t *x, uint16_t *y, hipStream_t stream) {
@@ -746,12 +751,15 @@ static hipError_t launch_vector(const uint8_t *codes, const uint8_t *scales, flo
 }
 
 // M <= 2 takes the staged-activation vector kernel while the rows fit in
-// LDS (its flat variant at M = 1 on wide matrices with K = 3072 or 5120).
+// LDS (its flat variant at M = 1 on wide matrices with K = 3072 or 5120),
+// and so does M = 3 on matrices up to N = 5120.
 // The matrix-core kernel takes every M >= 3 in one weight pass when K is a
 // whole number of 256-element chunks.  Otherwise the plain vector kernel
 // serves up to 8 rows per pass: rows 9..M take a second pass.
 hipError_t launch_gemv_nvfp4(const uint8_t *codes, const uint8_t *scales, float g, int N, int K,
                              const uint16_t *x, int M, uint16_t *y, hipStream_t stream) {
+  if (M == 3 && N <= kNvLdsM3MaxN && M * K <= kNvLdsMaxMK)
+    return launch_lds<3>(codes, scales, g, N, K, x, y, stream);
   if (M <= 2 && M * K <= kNvLdsMaxMK) {
     if (M == 1 && flat_fits(N, K)) return launch_flat(codes, scales, g, N, K, x, y, stream);
     if (M == 1) return launch_lds<1>(codes, scales, g, N, K, x, y, stream);

@@ -432,8 +432,8 @@ def test_gemv_nvfp4_every_code_and_scale_bit_exact():
         for m in range(8):
             x[m, base + m] = 1.0
         xb = x.view(np.uint16)
-        # M = 1 and 2: the staged-activation kernel; M = 8: the plain one
-        for M in (1, 2, 8):
+        # M = 1, 2 and 3: the staged-activation kernel; M = 8: the plain one
+        for M in (1, 2, 3, 8):
             y = run_nvfp4(codes, scales, 1.0, xb[:M])
             _, want = oracle.gemv_nvfp4_w4a16(codes, scales, 1.0, xb[:M])
             assert np.array_equal(y, want), (base, M)
@@ -623,6 +623,7 @@ def test_gemv_fp8_sixteen_rows_bit_exact():
     # activations staged in LDS up to M K = 80 K elements: at the limit the
     # staging takes several batches per thread; just past it, the plain kernel
     ("nvfp4", 1, 81920), ("nvfp4", 1, 81952), ("nvfp4", 2, 40960), ("nvfp4", 2, 40992),
+    ("nvfp4", 3, 27296), ("nvfp4", 3, 27328),
     ("fp8", 1, 81920), ("fp8", 3, 27296), ("fp8", 4, 20480), ("fp8", 4, 20496),
     ("fp8", 5, 16384), ("fp8", 5, 16400), ("fp8", 6, 13648), ("fp8", 6, 13664)])
 @pytest.mark.parametrize("N", [5, 37])
