@@ -909,30 +909,22 @@ static hipError_t launch_m(const uint8_t *w_qs, const uint16_t *w_d, int N, int 
   }
 }
 
-// Plain LDS-staged vector kernel for 3 <= M <= 8: four waves per workgroup
-// on narrow matrices, eight otherwise.
+// Plain LDS-staged vector kernel for 3 <= M <= 5 on matrices wider than
+// N = 4096 (narrower ones take the staged kernel in rounds): eight waves per
+// workgroup.
 template <int M>
 static hipError_t launch_lds_plain(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                                    const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
                                    float *y, hipStream_t stream) {
-  if (N <= 4096 && K <= 4096)
-    return launch_lds<M, false, 4>(w_qs, w_d, N, K, a_qs, a_d, a_s, nullptr, y, stream);
   return launch_lds<M, false, 8>(w_qs, w_d, N, K, a_qs, a_d, a_s, nullptr, y, stream);
 }
 
 hipError_t launch_mmvq_q4_0(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                             const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
                             int M, float *y, hipStream_t stream) {
-  // M = 3..5 on wider matrices: the activation rows staged in LDS once per
-  // workgroup beat the matrix cores (measured on MI355X over the Llama-2-7B
-  // shapes: 4096 x 22016 at M = 3 15.0 -> 10.8 us, at M = 4 15.2 -> 12.9 us,
-  // at M = 5 14.2 -> 13.1 us; wider M on wider matrices stays on the matrix
-  // cores).  Narrow matrices took the same kernel at M = 6..8 (4096 x 4096 at
-  // M = 8 6.3 -> 5.5 us) before the staged kernel in rounds above.
-  // The plain staging copies the Q8_1 scales in 16-byte pieces of 8, so it
-  // needs M * K / 32 to be a multiple of 8.
-  // narrow matrices from M = 3: the staged kernel in rounds (M nb / 8 whole
-  // 16-byte pieces of scales)
+  // Narrow matrices from M = 3: the staged kernel in rounds.  Both staged
+  // kernels copy the Q8_1 scales in 16-byte pieces of 8, so they need
+  // M * K / 32 to be a multiple of 8.
   if (M >= 3 && N <= kQ4RoundsMaxN && (M * (K >> 5)) % 8 == 0 &&
       lds_rounds_bytes(M, K) <= 160 * 1024) {
     switch (M) {
@@ -944,16 +936,17 @@ hipError_t launch_mmvq_q4_0(const uint8_t *w_qs, const uint16_t *w_d, int N, int
       default: return launch_lds_rounds<8>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
     }
   }
+  // M = 3..5 on wider matrices: the activation rows staged in LDS once per
+  // workgroup beat the matrix cores (measured on MI355X over the Llama-2-7B
+  // shapes: 4096 x 22016 at M = 3 15.0 -> 10.8 us, at M = 4 15.2 -> 12.9 us,
+  // at M = 5 14.2 -> 13.1 us); from M = 6 wider matrices take the matrix
+  // cores.
   const bool lds_ok = K <= kLdsMaxK && (M * (K >> 5)) % 8 == 0;
-  const bool narrow = N <= 4096 && K <= 4096;
-  if (M >= 3 && lds_ok && (M <= 5 || narrow)) {
+  if (M >= 3 && M <= 5 && lds_ok) {
     switch (M) {
       case 3: return launch_lds_plain<3>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
       case 4: return launch_lds_plain<4>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
-      case 5: return launch_lds_plain<5>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
-      case 6: return launch_lds_plain<6>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
-      case 7: return launch_lds_plain<7>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
-      default: return launch_lds_plain<8>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+      default: return launch_lds_plain<5>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
     }
   }
   const bool small = M <= kQ4VectorMaxM && N < 8192 && K < 8192;
