@@ -53,15 +53,20 @@ extern "C" {
 #define SKINNY_ERR_M           -4  /* M outside the entry point's range             */
 #define SKINNY_ERR_LAUNCH      -5  /* the HIP launch reported an error              */
 
-/* Limits: 1 <= K <= SKINNY_MAX_K, 0 <= N <= SKINNY_MAX_N. */
+/* Limits: 1 <= K <= SKINNY_MAX_K, 0 <= N <= SKINNY_MAX_N.  No kernel gives an
+ * output row more than 32 threads, so N <= 2^24 keeps every grid near 2^29
+ * work-items, well inside the 2^32 that one dispatch can hold. */
 #define SKINNY_MAX_K  (1 << 20)
-#define SKINNY_MAX_N  (1 << 28)
+#define SKINNY_MAX_N  (1 << 24)
 #define SKINNY_MAX_M_GEMV   8    /* mmvq_q4_0, mmvq_q4_k, mmvq_q6_k */
 /* gemv_nvfp4_w4a16: two 8-row verification tiles. */
 #define SKINNY_MAX_M_F16ACT 16
 /* gemv_fp8_w8a16: also the "chunked" band up to 96 rows. */
 #define SKINNY_MAX_M_FP8    96
 #define SKINNY_MAX_M_QUANT  65536
+/* quantize_act_q8_1: one thread per 8 elements, so M * K <= 2^32 keeps its grid
+ * at 2^29 threads. */
+#define SKINNY_MAX_MK_QUANT (1LL << 32)
 /* mmvq_q4_0_f32act: decode widths only, one row of K in LDS per workgroup. */
 #define SKINNY_MAX_M_F32ACT 2
 #define SKINNY_MAX_K_F32ACT 12288
@@ -84,7 +89,8 @@ const char *skinny_status_string(int status);
  *   qs  int8    [M][K] row-major, 16-byte aligned.
  *   d   binary16 [M][K/32], 2-byte aligned.
  *   s   binary16 [M][K/32], 2-byte aligned.
- *   0 <= M <= SKINNY_MAX_M_QUANT; K % 32 == 0.
+ *   0 <= M <= SKINNY_MAX_M_QUANT; K % 32 == 0; M * K <= SKINNY_MAX_MK_QUANT
+ *   (else SKINNY_ERR_SHAPE).
  * Results are bit-exact (one correct answer per input).  NaN or infinite
  * inputs give unspecified codes.
  */

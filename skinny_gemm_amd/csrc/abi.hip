@@ -45,6 +45,7 @@ int quantize_act_q8_1(const float *x, int M, int K, int8_t *qs, uint16_t *d, uin
                       void *stream) {
   if (M < 0 || M > SKINNY_MAX_M_QUANT) return SKINNY_ERR_M;
   if (K <= 0 || K > SKINNY_MAX_K || (K % 32) != 0) return SKINNY_ERR_SHAPE;
+  if ((long long)M * K > SKINNY_MAX_MK_QUANT) return SKINNY_ERR_SHAPE;
   if (M == 0) return SKINNY_OK;
   if (!x || !qs || !d || !s) return SKINNY_ERR_NULL;
   if (!aligned(x, 16) || !aligned(qs, 16) || !aligned(d, 2) || !aligned(s, 2))

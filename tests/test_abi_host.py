@@ -100,7 +100,10 @@ def test_gemv_rejects_bad_shapes(L, fn, kmult):
     assert fn(L, K=kmult + kmult // 2) == -2
     assert fn(L, K=(1 << 20) + kmult) == -2
     assert fn(L, N=-1) == -2
-    assert fn(L, N=(1 << 28) + 1) == -2
+    assert fn(L, N=(1 << 24) + 1) == -2
+    assert fn(L, N=1 << 28) == -2
+    # the largest N passes shape validation
+    assert fn(L, N=1 << 24, y=0) == -1
     # the largest K passes shape validation (stopped here by a NULL pointer)
     assert fn(L, K=1 << 20, y=0) == -1
 
@@ -149,6 +152,11 @@ def test_quantize_validation(L):
     assert qa(L, K=0) == -2
     assert qa(L, M=-1) == -4
     assert qa(L, M=65537) == -4
+    # M * K is capped at 2^32 elements (the grid has one thread per 8)
+    assert qa(L, M=65536, K=1 << 20) == -2
+    assert qa(L, M=4097, K=1 << 20) == -2
+    assert qa(L, M=4096, K=1 << 20, x=0) == -1
+    assert qa(L, M=65536, K=65536, x=0) == -1
     assert qa(L, x=0) == -1
     assert qa(L, s=0) == -1
     assert qa(L, x=A + 4) == -3
