@@ -688,15 +688,30 @@ static hipError_t launch_lds_a(const uint8_t *codes, const uint8_t *scales, floa
 // and M = 4 stay on the matrix cores).
 constexpr int kNvLdsM3MaxN = 5120;
 
+// One activation row on a small matrix (N and K up to 8192) takes two rows
+// per wave: more, smaller workgroups.  Measured at M = 1: 4096 x 4096 4.0 ->
+// 3.65 us, 8192 x 4096 5.9 -> 5.4 us, 5120 x 5120 5.0 -> 4.9 us; rows of
+// K = 17408 lose with it (11.0 -> 11.8 us).
+constexpr int kNvSmallMaxNK = 8192;
+
+template <int M, int R>
+static hipError_t launch_lds_r(const uint8_t *codes, const uint8_t *scales, float g, int N,
+                               int K, const uint16_t *x, uint16_t *y, hipStream_t stream) {
+  constexpr int W = M == 1 ? 4 : 8;
+  const int per_thread = (M * (K >> 3) + 64 * W - 1) / (64 * W);   // first staging batch
+  if (per_thread <= 2) return launch_lds_a<M, W, 2, R>(codes, scales, g, N, K, x, y, stream);
+  if (per_thread <= 4) return launch_lds_a<M, W, 4, R>(codes, scales, g, N, K, x, y, stream);
+  if (per_thread <= 8) return launch_lds_a<M, W, 8, R>(codes, scales, g, N, K, x, y, stream);
+  return launch_lds_a<M, W, 12, R>(codes, scales, g, N, K, x, y, stream);
+}
+
 template <int M>
 static hipError_t launch_lds(const uint8_t *codes, const uint8_t *scales, float g, int N, int K,
                              const uint16_t *x, uint16_t *y, hipStream_t stream) {
-  constexpr int W = M == 1 ? 4 : 8;
-  const int per_thread = (M * (K >> 3) + 64 * W - 1) / (64 * W);   // first staging batch
-  if (per_thread <= 2) return launch_lds_a<M, W, 2>(codes, scales, g, N, K, x, y, stream);
-  if (per_thread <= 4) return launch_lds_a<M, W, 4>(codes, scales, g, N, K, x, y, stream);
-  if (per_thread <= 8) return launch_lds_a<M, W, 8>(codes, scales, g, N, K, x, y, stream);
-  return launch_lds_a<M, W, 12>(codes, scales, g, N, K, x, y, stream);
+  if constexpr (M == 1)
+    if (N <= kNvSmallMaxNK && K <= kNvSmallMaxNK)
+      return launch_lds_r<M, 2>(codes, scales, g, N, K, x, y, stream);
+  return launch_lds_r<M, 3>(codes, scales, g, N, K, x, y, stream);
 }
 
 // Flat kernel (M = 1, nc = K / 32 in {96, 160}): two rows per wave, L = nc / 32
