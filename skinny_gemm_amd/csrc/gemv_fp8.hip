@@ -658,13 +658,21 @@ static hipError_t launch_lds_rw(const uint8_t *w, const float *cs, int N, int K,
 // at M = 1: 2048 x 5120 5.3 -> 4.3 us, 4096 x 4096 5.35 -> 4.85 us, 4096 x
 // 8192 7.8 -> 7.4 us; rows of K = 17408 lose with it (16.0 -> 16.6 us).
 constexpr int kF8SmallMaxNK = 8192;
+// At M = 2 the same shape wins only on matrices of up to 2^24 weights
+// (5120 x 2048 5.7 -> 4.6 us, 4096 x 4096 5.6 -> 5.0 us; 5120 x 5120 and
+// larger lose with it).
+constexpr long long kF8SmallMaxWeights = 1LL << 24;
 
 template <int M>
 static hipError_t launch_lds(const uint8_t *w, const float *cs, int N, int K,
                              const uint16_t *x, uint16_t *y, hipStream_t stream) {
-  if constexpr (M == 1)
+  if constexpr (M == 1) {
     if (N <= kF8SmallMaxNK && K <= kF8SmallMaxNK)
       return launch_lds_rw<M, 2, 4>(w, cs, N, K, x, y, stream);
+  } else if constexpr (M == 2) {
+    if ((long long)N * K <= kF8SmallMaxWeights)
+      return launch_lds_rw<M, 2, 4>(w, cs, N, K, x, y, stream);
+  }
   return launch_lds_rw<M, 3, 8>(w, cs, N, K, x, y, stream);
 }
 

@@ -694,11 +694,14 @@ constexpr int kNvLdsM3MaxN = 5120;
 // 3.65 us, 8192 x 4096 5.9 -> 5.4 us, 5120 x 5120 5.0 -> 4.9 us; rows of
 // K = 17408 lose with it (11.0 -> 11.8 us).
 constexpr int kNvSmallMaxNK = 8192;
+// At M = 2 the same shape wins only on matrices of up to 2^24 weights
+// (5120 x 2048 5.4 -> 4.0 us, 4096 x 4096 4.6 -> 4.1 us; 5120 x 5120 and
+// larger lose with it).
+constexpr long long kSmallMaxWeights = 1LL << 24;
 
-template <int M, int R>
+template <int M, int R, int W>
 static hipError_t launch_lds_r(const uint8_t *codes, const uint8_t *scales, float g, int N,
                                int K, const uint16_t *x, uint16_t *y, hipStream_t stream) {
-  constexpr int W = M == 1 ? 4 : 8;
   const int per_thread = (M * (K >> 3) + 64 * W - 1) / (64 * W);   // first staging batch
   if (per_thread <= 2) return launch_lds_a<M, W, 2, R>(codes, scales, g, N, K, x, y, stream);
   if (per_thread <= 4) return launch_lds_a<M, W, 4, R>(codes, scales, g, N, K, x, y, stream);
@@ -709,10 +712,15 @@ static hipError_t launch_lds_r(const uint8_t *codes, const uint8_t *scales, floa
 template <int M>
 static hipError_t launch_lds(const uint8_t *codes, const uint8_t *scales, float g, int N, int K,
                              const uint16_t *x, uint16_t *y, hipStream_t stream) {
-  if constexpr (M == 1)
+  if constexpr (M == 1) {
     if (N <= kNvSmallMaxNK && K <= kNvSmallMaxNK)
-      return launch_lds_r<M, 2>(codes, scales, g, N, K, x, y, stream);
-  return launch_lds_r<M, 3>(codes, scales, g, N, K, x, y, stream);
+      return launch_lds_r<M, 2, 4>(codes, scales, g, N, K, x, y, stream);
+    return launch_lds_r<M, 3, 4>(codes, scales, g, N, K, x, y, stream);
+  } else {
+    if (M == 2 && (long long)N * K <= kSmallMaxWeights)
+      return launch_lds_r<M, 2, 4>(codes, scales, g, N, K, x, y, stream);
+    return launch_lds_r<M, 3, 8>(codes, scales, g, N, K, x, y, stream);
+  }
 }
 
 // Flat kernel (M = 1, nc = K / 32 in {96, 160}): two rows per wave, L = nc / 32

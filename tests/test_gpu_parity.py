@@ -541,21 +541,22 @@ def test_gemv_fp8_vs_oracle(M, N, K):
     check_f16(y, y_acc, fp8_mag(w, cs, x), K, "fp8 M=%d N=%d K=%d" % (M, N, K))
 
 
+@pytest.mark.parametrize("M", [1, 2])
 @pytest.mark.parametrize("N,K", [(8192, 8192), (8193, 8192), (8192, 8224), (2048 + 5, 5120),
-                                 (8, 32)])
-def test_single_row_small_matrix_route_vs_oracle(N, K):
-    # one activation row on a matrix with N and K up to 8192 takes two weight
-    # rows per wave in both binary16 formats; one step past either bound
-    # takes three
-    x = inputs.normal_f16_bits(1, K, 7 + K)
+                                 (4096, 4096), (4097, 4096), (8, 32)])
+def test_small_matrix_route_vs_oracle(M, N, K):
+    # one activation row on a matrix with N and K up to 8192, or two on one of
+    # up to 2^24 weights, takes two weight rows per wave in both binary16
+    # formats; one step past a bound takes three
+    x = inputs.normal_f16_bits(M, K, 7 + K)
     codes, scales, _ = inputs.nvfp4_weights(N, K, 11 * N + K)
     y = run_nvfp4(codes, scales, 0.75, x)
     y_acc, _ = oracle.gemv_nvfp4_w4a16(codes, scales, 0.75, x)
-    check_f16(y, y_acc, nvfp4_mag(codes, scales, 0.75, x), K, "nvfp4 N=%d K=%d" % (N, K))
+    check_f16(y, y_acc, nvfp4_mag(codes, scales, 0.75, x), K, "nvfp4 M=%d N=%d K=%d" % (M, N, K))
     w, cs = inputs.fp8_weights(N, K, 13 * N + K)
     y = run_fp8(w, cs, x)
     y_acc, _ = oracle.gemv_fp8_w8a16(w, cs, x)
-    check_f16(y, y_acc, fp8_mag(w, cs, x), K, "fp8 N=%d K=%d" % (N, K))
+    check_f16(y, y_acc, fp8_mag(w, cs, x), K, "fp8 M=%d N=%d K=%d" % (M, N, K))
 
 
 @pytest.mark.parametrize("M", [17, 31, 48, 64, 80, 96])
