@@ -187,26 +187,71 @@ def _check_q4_0(M, N, K):
     check_f32(y, ref, q4_mag(w_qs, w_d, a_qs, a_d, a_s), K, "q4_0 M=%d N=%d K=%d" % (M, N, K))
 
 
-@pytest.mark.parametrize("M", [1, 4, 8])
-def test_mmvq_q4_0_integer_gate_bit_exact(M):
-    # unit Q8_1 scales and unit weight scales: every term is an integer below
-    # 2^24, so the result is exact in any summation order
-    N, K = 1031, 4096
-    x = inputs.q8_1_unit_scale_source(M, K, 90 + M)
+# (M, N, K) of the exact-integer gate, one or more per dispatch route of
+# mmvq_q4_0 (the route each reaches is named).  With unit scales every block
+# term isum - 8 s8 = sum (code - 8) q8 is an integer, and the sum of their
+# magnitudes is checked below 2^24, so every partial sum in any order is an
+# exact float32 integer and y must equal the oracle bit for bit.
+Q4_GATE = [
+    (1, 1031, 4096),      # vector kernel, one round of two blocks per lane
+    (1, 25000, 4096),     # vector kernel, many workgroups
+    (1, 300, 11008),      # vector kernel, six blocks per lane
+    (2, 1031, 4096),      # vector kernel at M = 2
+    (2, 9000, 4096),      # plain staged-activation kernel (M = 2, N >= 8192)
+    (3, 1031, 4096), (4, 1031, 4096), (6, 1031, 4096), (8, 1031, 4096),
+                          # staged kernel in rounds (M >= 3, N <= 4096)
+    (3, 9000, 4096), (4, 25000, 4096), (5, 9000, 4096),
+                          # plain staged-activation kernel (M = 3..5, wider)
+    (6, 5000, 4096), (8, 5000, 4096),
+                          # matrix cores, eight K slices, chunks of 4 steps
+    (6, 9000, 4096), (7, 9000, 4096), (8, 9000, 4096),
+                          # matrix cores, two K slices, chunks of 8 steps
+    (6, 25000, 4096), (8, 25000, 4096),
+                          # matrix cores, two waves share each activation chunk
+    (7, 30000, 4096), (8, 30000, 4096),
+                          # matrix cores, four waves share each activation chunk
+    (8, 25000, 3840),     # matrix cores, shared chunks of 4 steps (K % 512 == 256)
+    (3, 5000, 12800), (4, 9000, 12800),
+                          # matrix cores with 4 padded activation rows (K past the
+                          # staged kernels' limit)
+]
+
+
+@pytest.mark.parametrize("M,N,K", Q4_GATE)
+def test_mmvq_q4_0_integer_gate_bit_exact(M, N, K):
+    x = inputs.q8_1_unit_scale_source(M, K, 90 + M + K)
     import skinny_gemm_amd as sk
 
     qs, d, s = sk.quantize_act_q8_1(dev(x))            # quantized on the device
-    w_qs, _ = inputs.q4_0_weights(N, K, 91)
+    w_qs, _ = inputs.q4_0_weights(N, K, 91 + N)
     w_d = np.full((N, K // 32), 0x3C00, np.uint16)
     y = host(sk.mmvq_q4_0(dev(w_qs), dev(w_d), qs, d, s))
     a_qs, a_d, a_s = oracle.quantize_q8_1(x)
+    assert np.all(a_d == 0x3C00)                       # d8 = 1 in every block
+    # |code - 8| <= 8, so the block terms' magnitudes sum to at most 8 sum |q8|
+    assert 8 * np.abs(a_qs.astype(np.int64)).sum(axis=1).max() < 2 ** 24
     exact = oracle.mmvq_q4_0(w_qs, w_d, a_qs, a_d, a_s)
     assert np.array_equal(exact, np.rint(exact))
-    assert np.array_equal(y.astype(np.float64), exact)
+    assert np.array_equal(y.astype(np.float64), exact), "M=%d N=%d K=%d" % (M, N, K)
     # every code 8: all weights zero
     w8 = np.full((N, K // 2), 0x88, np.uint8)
     y8 = host(sk.mmvq_q4_0(dev(w8), dev(w_d), qs, d, s))
     assert np.all(y8 == 0.0)
+
+
+@pytest.mark.parametrize("M,N", [(1, 1031), (1, 25000), (2, 9000)])
+def test_mmvq_q4_0_f32act_integer_gate_bit_exact(M, N):
+    # the fused entry point on integer activations and unit weight scales:
+    # exact, equal to the oracle chain bit for bit
+    K = 4096
+    x = inputs.q8_1_unit_scale_source(M, K, 190 + M)
+    w_qs, _ = inputs.q4_0_weights(N, K, 191 + N)
+    w_d = np.full((N, K // 32), 0x3C00, np.uint16)
+    y = run_q4_f32act(w_qs, w_d, x)
+    a_qs, a_d, a_s = oracle.quantize_q8_1(x)
+    assert 8 * np.abs(a_qs.astype(np.int64)).sum(axis=1).max() < 2 ** 24
+    exact = oracle.mmvq_q4_0(w_qs, w_d, a_qs, a_d, a_s)
+    assert np.array_equal(y.astype(np.float64), exact)
 
 
 def test_q4_0_pipeline_device_quantize():
@@ -346,29 +391,67 @@ def test_mmvq_q6_k_vs_oracle(M, N, K):
               "q6_k M=%d N=%d K=%d" % (M, N, K))
 
 
+def _q4_k_gate_weights(N, K, s, sc_mask):
+    # d = dmin = 1, sub-block scales sc & sc_mask, mins in {0, 4}
+    w_qs, w_hdr = inputs.q4_k_weights(N, K, s)
+    w_hdr[:, :, 0:2] = np.array([0x3C00], np.uint16).view(np.uint8)
+    w_hdr[:, :, 2:4] = np.array([0x3C00], np.uint16).view(np.uint8)
+    w_hdr[:, :, 4:12] &= sc_mask
+    w_hdr[:, :, 12:16] &= 0x11
+    return w_qs, w_hdr
+
+
+def _q4_k_gate_bound(w_qs, w_hdr, a_qs, a_s):
+    # sum over blocks of |sc isum - m s8| <= sum_k sc q |q8| + sum_b m |s8|
+    _, _, sc, mn = q4_k_fields(w_hdr)
+    W = unpack_q4_0(w_qs) * np.repeat(sc, 32, axis=1)
+    return (np.abs(a_qs.astype(np.float64)) @ W.T.astype(np.float64)
+            + np.abs(f16(a_s)) @ mn.T.astype(np.float64)).max()
+
+
+# (M, N, K, sc_mask) of the Q4_K exact-integer gate, one or more per route
+Q4K_GATE = [
+    (1, 300, 4096, 7), (2, 300, 4096, 7),       # vector kernel
+    (3, 300, 4096, 7), (8, 300, 4096, 7),       # staged-activation kernel (N < 16384)
+    (4, 16393, 4096, 7),                        # vector kernel (M < 5, wide)
+    (5, 16393, 4096, 7), (8, 16393, 4096, 7),   # matrix cores, two waves share activations
+    (8, 28805, 4096, 7),                        # matrix cores, four waves share activations
+    (8, 5000, 16640, 3),                        # matrix cores, eight K slices (activations
+                                                # past the staged kernel's LDS)
+    (8, 9000, 16640, 3),                        # matrix cores, two K slices
+]
+
+
+@pytest.mark.parametrize("M,N,K,sc_mask", Q4K_GATE)
+def test_q4_k_integer_gate_bit_exact(M, N, K, sc_mask):
+    # unit d and dmin, small scales and mins, integer activations (d8 = 1,
+    # s8 = sum q8 exactly): every block term is an integer and their
+    # magnitudes sum below 2^24, so any summation order gives the exact result
+    x = inputs.q8_1_unit_scale_source(M, K, 70 + M + K)
+    a_qs, a_d, a_s = oracle.quantize_q8_1(x)
+    assert np.all(a_d == 0x3C00)
+    w_qs, w_hdr = _q4_k_gate_weights(N, K, 71 + N, sc_mask)
+    assert _q4_k_gate_bound(w_qs, w_hdr, a_qs, a_s) < 2 ** 24
+    y = run_q4_k(w_qs, w_hdr, a_qs, a_d, a_s)
+    ref = oracle.mmvq_q4_k(w_qs, w_hdr, a_qs, a_d, a_s)
+    assert np.array_equal(ref, np.round(ref))
+    assert np.array_equal(y.astype(np.float64), ref), "M=%d N=%d K=%d" % (M, N, K)
+
+
 @pytest.mark.parametrize("M", [1, 4, 8])
-def test_k_quant_integer_gate_bit_exact(M):
-    # unit scales and integer activations (d8 = 1, s8 = sum q8 exactly):
-    # every term is an integer below 2^24, so any summation order gives the
-    # exact result
+def test_q6_k_integer_gate_bit_exact(M):
+    # unit d, scales in -2..2, integer activations: exact in any order
     N, K = 300, 4096
     x = inputs.q8_1_unit_scale_source(M, K, 70 + M)
     a_qs, a_d, a_s = oracle.quantize_q8_1(x)
-    w_qs, w_hdr = inputs.q4_k_weights(N, K, 71)
-    w_hdr[:, :, 0:2] = np.array([0x3C00], np.uint16).view(np.uint8)       # d = 1
-    w_hdr[:, :, 2:4] = np.array([0x3C00], np.uint16).view(np.uint8)       # dmin = 1
-    w_hdr[:, :, 4:12] &= 0x07                                              # sc <= 7, m low bits 0
-    w_hdr[:, :, 12:16] &= 0x11                                             # m in {0, 4}
-    y = run_q4_k(w_qs, w_hdr, a_qs, a_d, a_s)
-    ref = oracle.mmvq_q4_k(w_qs, w_hdr, a_qs, a_d, a_s)
-    assert np.all(np.abs(ref) < 2 ** 24) and np.array_equal(ref, np.round(ref))
-    assert np.array_equal(y.astype(np.float64), ref)
     w_ql, w_qh, w_sc, _ = inputs.q6_k_weights(N, K, 72)
     w_sc = (w_sc.astype(np.int64) % 5 - 2).astype(np.int8)                # sc in -2..2
     w_d = np.full((N, K // 256), 0x3C00, np.uint16)
+    # |q - 32| <= 32 and |sc| <= 2: the block terms sum to at most 64 sum |q8|
+    assert 64 * np.abs(a_qs.astype(np.int64)).sum(axis=1).max() < 2 ** 24
     y6 = run_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d)
     ref6 = oracle.mmvq_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d)
-    assert np.all(np.abs(ref6) < 2 ** 24) and np.array_equal(ref6, np.round(ref6))
+    assert np.array_equal(ref6, np.round(ref6))
     assert np.array_equal(y6.astype(np.float64), ref6)
 
 
@@ -481,12 +564,27 @@ def test_gemv_nvfp4_flat_bit_exact():
         assert np.count_nonzero(f16(want)) > N // 2
 
 
-def test_gemv_nvfp4_outliers():
+# (M, N, K) of the outlier test, one per route of gemv_nvfp4_w4a16
+NV_OUTLIER = [
+    (1, 512, 5120),       # staged activations, two rows per wave (small matrix)
+    (1, 512, 17408),      # staged activations, three rows per wave
+    (1, 8192, 5120),      # flat mapping
+    (2, 512, 5120),       # staged activations at M = 2
+    (2, 512, 40992),      # plain vector kernel (activations past the LDS limit)
+    (3, 512, 5120),       # staged activations at M = 3
+    (4, 512, 5120),       # matrix cores, 4 padded activation rows
+    (8, 512, 5120),       # matrix cores, 8 padded activation rows
+    (8, 512, 5152),       # plain vector kernel (K % 256 != 0)
+    (16, 512, 5120),      # matrix cores, 16 activation rows
+]
+
+
+@pytest.mark.parametrize("M,N,K", NV_OUTLIER)
+def test_gemv_nvfp4_outliers(M, N, K):
     # activation outliers of +-2e4: any binary16 partial sum would overflow
-    M, N, K = 4, 512, 5120
-    codes, scales, _ = inputs.nvfp4_weights(N, K, 61)
-    x = inputs.normal_f16_bits(M, K, 62).view(np.float16).copy()
-    rng = np.random.Generator(np.random.PCG64(63))
+    codes, scales, _ = inputs.nvfp4_weights(N, K, 61 + K)
+    x = inputs.normal_f16_bits(M, K, 62 + M).view(np.float16).copy()
+    rng = np.random.Generator(np.random.PCG64(63 + M))
     idx = rng.integers(0, K, size=(M, 24))
     for m in range(M):
         x[m, idx[m]] = np.float16(2.0e4) * np.where(rng.integers(0, 2, 24) == 0, -1, 1)
@@ -494,7 +592,8 @@ def test_gemv_nvfp4_outliers():
     y = run_nvfp4(codes, scales, 1.0, xb)
     y_acc, _ = oracle.gemv_nvfp4_w4a16(codes, scales, 1.0, xb)
     assert np.all(np.isfinite(y_acc))
-    check_f16(y, y_acc, nvfp4_mag(codes, scales, 1.0, xb), K, "nvfp4 outliers")
+    check_f16(y, y_acc, nvfp4_mag(codes, scales, 1.0, xb), K, "nvfp4 outliers M=%d N=%d K=%d" % (
+        M, N, K))
 
 
 def test_gemv_nvfp4_sixteen_rows_bit_exact():
