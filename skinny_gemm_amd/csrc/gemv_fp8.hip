@@ -620,7 +620,8 @@ static hipError_t launch_m(const uint8_t *w, const float *cs, int N, int K, cons
 
 // Staged-activation vector kernel (M <= 5, and M = 6 on narrow matrices):
 // three rows per wave, eight waves per workgroup (two rows and four waves on
-// small matrices at M = 1, below; measured on MI355X over K
+// small matrices: at M = 1 with N and K up to 8192, at M = 2 up to 2^24
+// weights, below; measured on MI355X over K
 // 5120 and 17408, N 5120 to 34816: 17408 x 5120 at M = 1 18.3 -> 16.0 us,
 // 5120 x 34816 at M = 2 33.6 -> 28.3 us; at M = 3 and 4 on par with or ahead
 // of the matrix cores; at M = 5 5120 x 5120 9.9 -> 8.4 us, 5120 x 10240 13.5

@@ -663,12 +663,13 @@ static hipError_t launch_m(const uint8_t *codes, const uint8_t *scales, float g,
   }
 }
 
-// Staged-activation vector kernel (M <= 2): three rows per wave (two on
-// small matrices at M = 1, below), four waves per workgroup at M = 1 and
-// eight at M = 2 (measured on MI355X over K 5120
-// and 17408, N 5120 to 34816: 5120 x 34816 at M = 1 24.7 -> 19.0 us, at M =
-// 2 28.3 -> 24.9 us against the matrix cores; 17408 x 5120 at M = 2 17.3 ->
-// 14.1 us).
+// Staged-activation vector kernel (M <= 2, and M = 3 up to N = 5120): three
+// rows per wave, four waves per workgroup at M = 1 and eight at M = 2 and 3
+// (measured on MI355X over K 5120 and 17408, N 5120 to 34816: 5120 x 34816 at
+// M = 1 24.7 -> 19.0 us, at M = 2 28.3 -> 24.9 us against the matrix cores;
+// 17408 x 5120 at M = 2 17.3 -> 14.1 us).  Small matrices take two rows and
+// four waves instead: at M = 1 with N and K up to 8192, at M = 2 up to 2^24
+// weights (below).
 constexpr int kNvLdsMaxMK = 80 * 1024;      // M K binary16 activations in LDS
 
 template <int M, int W, int A, int R = 3>
