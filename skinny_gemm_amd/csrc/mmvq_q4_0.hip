@@ -825,9 +825,13 @@ static hipError_t launch_lds_rounds_a(const uint8_t *w_qs, const uint16_t *w_d, 
 
 // Two rows per wave, eight waves (measured on MI355X over the Llama-2-7B
 // shapes: 11008 x 4096 at M = 4 9.4 -> 8.5 us, at M = 8 11.8 -> 11.2 us on the
-// matrix cores; 4096 x 4096 at M = 6 5.25 -> 4.8 us; wider matrices lose
-// from M = 6 and keep the other kernels).
-constexpr int kQ4RoundsMaxN = 4096;
+// matrix cores; 4096 x 4096 at M = 6 5.25 -> 4.8 us).  It keeps the lead up
+// to N = 6144 (at M = 8 4096 x 6144 10.4 -> 8.5 us and 5120 x 5120
+// 12.5 -> 10.9 us against the matrix cores; at M = 4 13824 x 5120, past the
+// plain staged kernel's K limit, 19.9 -> 13.3 us); from N = 8192 (512
+// workgroups) the matrix cores are faster at M = 8 (8192 x 8192 13.1
+// against 15.4 us).
+constexpr int kQ4RoundsMaxN = 6144;
 
 static int lds_rounds_bytes(int M, int K) { return M * K + 8 * M * (K >> 5); }
 
@@ -889,15 +893,17 @@ static hipError_t launch_mru(const uint8_t *w_qs, const uint16_t *w_d, int N, in
 // Vector kernel shape: two rows per wave (a handful of 128-bit weight loads
 // in flight per lane, many waves) measured best on MI355X at M <= 4 on
 // every Llama-2-7B shape.  At M <= 2 each lane loads all of its blocks of a
-// row in one round (U = blocks per lane, up to 6 = K 12288) -- long rows
-// are otherwise bound by successive memory round trips (7.8 -> 6.3 us for
-// an 11008 x 4096 matrix).
+// row in one round (U = blocks per lane, up to 8 = K 16384; longer rows take
+// rounds of 8) -- long rows are otherwise bound by successive memory round
+// trips (7.8 -> 6.3 us for an 11008 x 4096 matrix; with U = 8, 14336 x 4096
+// 9.7 -> 7.7 us and 13824 x 5120 11.9 -> 9.8 us at M = 1).
 template <int M>
 static hipError_t launch_m(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                            const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
                            float *y, hipStream_t stream) {
   if constexpr (M <= 2) {
     const int per_lane = ((K >> 5) + kWave - 1) / kWave;
+    if (per_lane > 6) return launch_mru<M, 2, 8>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
     if (per_lane > 4) return launch_mru<M, 2, 6>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
     if (per_lane > 3) return launch_mru<M, 2, 4>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
     if (per_lane > 2) return launch_mru<M, 2, 3>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
@@ -910,7 +916,7 @@ static hipError_t launch_m(const uint8_t *w_qs, const uint16_t *w_d, int N, int 
 }
 
 // Plain LDS-staged vector kernel for 3 <= M <= 5 on matrices wider than
-// N = 4096 (narrower ones take the staged kernel in rounds): eight waves per
+// N = 6144 (narrower ones take the staged kernel in rounds): eight waves per
 // workgroup.
 template <int M>
 static hipError_t launch_lds_plain(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
@@ -922,7 +928,7 @@ static hipError_t launch_lds_plain(const uint8_t *w_qs, const uint16_t *w_d, int
 hipError_t launch_mmvq_q4_0(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                             const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
                             int M, float *y, hipStream_t stream) {
-  // Narrow matrices from M = 3: the staged kernel in rounds.  Both staged
+  // Narrow matrices (N <= 6144) from M = 3: the staged kernel in rounds.  Both staged
   // kernels copy the Q8_1 scales in 16-byte pieces of 8, so they need
   // M * K / 32 to be a multiple of 8.
   if (M >= 3 && N <= kQ4RoundsMaxN && (M * (K >> 5)) % 8 == 0 &&

@@ -164,7 +164,11 @@ def run_q4(w_qs, w_d, a_qs, a_d, a_s):
                                  # one empty slice
                                  (25000, 768), (9000, 1280), (40, 768), (700, 8192),
                                  # four waves sharing one activation chunk, ragged
-                                 (30000, 1024)])
+                                 (30000, 1024),
+                                 # narrow matrix-core route past the staged kernels'
+                                 # N and K limits (eight K slices), and the staged
+                                 # kernel in rounds at N = 6144
+                                 (7000, 12800), (6144, 2048)])
 def test_mmvq_q4_0_vs_oracle(M, N, K):
     _check_q4_0(M, N, K)
 
@@ -196,13 +200,18 @@ Q4_GATE = [
     (1, 1031, 4096),      # vector kernel, one round of two blocks per lane
     (1, 25000, 4096),     # vector kernel, many workgroups
     (1, 300, 11008),      # vector kernel, six blocks per lane
+    (1, 1031, 13824),     # vector kernel, one round of eight blocks per lane
+    (1, 300, 20480),      # vector kernel, rounds of eight blocks per lane
     (2, 1031, 4096),      # vector kernel at M = 2
+    (2, 300, 16384),      # vector kernel at M = 2, eight blocks per lane
     (2, 9000, 4096),      # plain staged-activation kernel (M = 2, N >= 8192)
     (3, 1031, 4096), (4, 1031, 4096), (6, 1031, 4096), (8, 1031, 4096),
-                          # staged kernel in rounds (M >= 3, N <= 4096)
+    (5, 6000, 4096), (8, 6144, 4096),
+                          # staged kernel in rounds (M >= 3, N <= 6144)
+    (4, 5120, 13824),     # staged kernel in rounds past the plain staged kernel's K
     (3, 9000, 4096), (4, 25000, 4096), (5, 9000, 4096),
                           # plain staged-activation kernel (M = 3..5, wider)
-    (6, 5000, 4096), (8, 5000, 4096),
+    (6, 7000, 4096), (8, 7000, 4096),
                           # matrix cores, eight K slices, chunks of 4 steps
     (6, 9000, 4096), (7, 9000, 4096), (8, 9000, 4096),
                           # matrix cores, two K slices, chunks of 8 steps
@@ -211,9 +220,10 @@ Q4_GATE = [
     (7, 30000, 4096), (8, 30000, 4096),
                           # matrix cores, four waves share each activation chunk
     (8, 25000, 3840),     # matrix cores, shared chunks of 4 steps (K % 512 == 256)
-    (3, 5000, 12800), (4, 9000, 12800),
+    (3, 9000, 12800), (4, 9000, 12800),
                           # matrix cores with 4 padded activation rows (K past the
-                          # staged kernels' limit)
+                          # plain staged kernel's limit)
+    (3, 5000, 12800),     # staged kernel in rounds at the same K
 ]
 
 
@@ -412,6 +422,7 @@ def _q4_k_gate_bound(w_qs, w_hdr, a_qs, a_s):
 # (M, N, K, sc_mask) of the Q4_K exact-integer gate, one or more per route
 Q4K_GATE = [
     (1, 300, 4096, 7), (2, 300, 4096, 7),       # vector kernel
+    (1, 1031, 13824, 3), (2, 300, 16384, 3),    # vector kernel, eight blocks per lane
     (3, 300, 4096, 7), (8, 300, 4096, 7),       # staged-activation kernel (N < 16384)
     (4, 16393, 4096, 7),                        # vector kernel (M < 5, wide)
     (5, 16393, 4096, 7), (8, 16393, 4096, 7),   # matrix cores, two waves share activations
@@ -438,17 +449,20 @@ def test_q4_k_integer_gate_bit_exact(M, N, K, sc_mask):
     assert np.array_equal(y.astype(np.float64), ref), "M=%d N=%d K=%d" % (M, N, K)
 
 
-@pytest.mark.parametrize("M", [1, 4, 8])
-def test_q6_k_integer_gate_bit_exact(M):
-    # unit d, scales in -2..2, integer activations: exact in any order
-    N, K = 300, 4096
-    x = inputs.q8_1_unit_scale_source(M, K, 70 + M)
+@pytest.mark.parametrize("M,N,K,sc_max", [
+    (1, 300, 4096, 2), (4, 300, 4096, 2), (8, 300, 4096, 2),
+    (1, 1031, 13824, 1), (2, 300, 13824, 1),    # vector kernel, eight blocks per lane
+])
+def test_q6_k_integer_gate_bit_exact(M, N, K, sc_max):
+    # unit d, scales in -sc_max..sc_max, integer activations: exact in any order
+    x = inputs.q8_1_unit_scale_source(M, K, 70 + M + K)
     a_qs, a_d, a_s = oracle.quantize_q8_1(x)
     w_ql, w_qh, w_sc, _ = inputs.q6_k_weights(N, K, 72)
-    w_sc = (w_sc.astype(np.int64) % 5 - 2).astype(np.int8)                # sc in -2..2
+    w_sc = (w_sc.astype(np.int64) % (2 * sc_max + 1) - sc_max).astype(np.int8)
     w_d = np.full((N, K // 256), 0x3C00, np.uint16)
-    # |q - 32| <= 32 and |sc| <= 2: the block terms sum to at most 64 sum |q8|
-    assert 64 * np.abs(a_qs.astype(np.int64)).sum(axis=1).max() < 2 ** 24
+    # |q - 32| <= 32 and |sc| <= sc_max: the block terms sum to at most
+    # 32 sc_max sum |q8|
+    assert 32 * sc_max * np.abs(a_qs.astype(np.int64)).sum(axis=1).max() < 2 ** 24
     y6 = run_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d)
     ref6 = oracle.mmvq_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d)
     assert np.array_equal(ref6, np.round(ref6))
