@@ -558,7 +558,7 @@ static hipError_t launch_q6k_mru(const uint8_t *w_ql, const uint8_t *w_qh, const
 // Launch shapes measured on MI355X over the Qwen3-8B projections (K 4096 and
 // 12288, N 4096 to 24576) at M = 1, 2, 4, 8.  At M <= 2 a lane takes its
 // whole share of a row in one round up to 8 blocks (K <= 16384; longer rows
-// take rounds of 8), two rows per wave, four on wide matrices.  Wider M takes one or two blocks per
+// take rounds of 6), two rows per wave, four on wide matrices.  Wider M takes one or two blocks per
 // round (the activation registers grow with M) and four rows per wave on
 // wide matrices (Q4_K at M = 4 on 12288 x 4096: 11.6 -> 10.1 us with two).
 template <int M>
@@ -573,7 +573,7 @@ static hipError_t launch_q4k_m(const uint8_t *w_qs, const uint8_t *w_hdr, int N,
       SKINNY_Q4K(2, 2);
     }
     if (per_lane <= 4) SKINNY_Q4K(2, 4);
-    if (per_lane <= 6) SKINNY_Q4K(2, 6);
+    if (per_lane <= 6 || per_lane > 8) SKINNY_Q4K(2, 6);
     SKINNY_Q4K(2, 8);
   } else {
     if (N >= 16384) SKINNY_Q4K(4, 1);
@@ -595,7 +595,7 @@ static hipError_t launch_q6k_m(const uint8_t *w_ql, const uint8_t *w_qh, const i
       SKINNY_Q6K(2, 2);
     }
     if (per_lane <= 4) SKINNY_Q6K(2, 4);
-    if (per_lane <= 6) SKINNY_Q6K(2, 6);
+    if (per_lane <= 6 || per_lane > 8) SKINNY_Q6K(2, 6);
     SKINNY_Q6K(2, 8);
   } else {
     if (N >= 16384) SKINNY_Q6K(4, 1);

@@ -37,14 +37,25 @@ constexpr int next_pow2(int v) { return v <= 1 ? 1 : 2 * next_pow2((v + 1) / 2);
 
 // (No __restrict__ on the inputs: the issue fence below must be able to
 // keep a round's loads ahead of its arithmetic.)
-template <int M, int R, int U, bool NT>
+//
+// KS > 1 splits K: the KS waves w, w + 1, .. of a group take the same R rows
+// and consecutive slices of ceil(nb / KS) blocks, and the group's first wave
+// adds the others' reduced sums (in slice order, so results repeat bit for
+// bit) and stores.  Long rows then take one memory round per wave instead
+// of several.
+template <int M, int R, int U, bool NT, int KS = 1>
 __global__ __launch_bounds__(256) void mmvq_q4_0_kernel(
     const uint8_t *w_qs, const uint16_t *w_d, int N, int K, const int8_t *a_qs,
     const uint16_t *a_d, const uint16_t *a_s, float *y) {
+  static_assert(KS == 1 || KS == 2 || KS == 4, "K slices per row group");
   const int lane = threadIdx.x & 63;
-  const int n0 = (blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6)) * R;
-  if (n0 >= N) return;
+  const int wave = threadIdx.x >> 6;
+  const int ks = wave % KS;
+  const int n0 = (blockIdx.x * (4 / KS) + wave / KS) * R;
+  if (KS == 1 && n0 >= N) return;   // with KS > 1 every wave meets the barrier below
   const int nb = K >> 5;
+  const int nbs = (nb + KS - 1) / KS;
+  const int bb = ks * nbs, be = min(nb, bb + nbs);   // this wave's blocks [bb, be)
 
   const uint8_t *wrow[R];
   const uint16_t *drow[R];
@@ -62,16 +73,16 @@ __global__ __launch_bounds__(256) void mmvq_q4_0_kernel(
     for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
 
   // U blocks per lane per round, all loaded before any is used, so a row of
-  // up to 64 U blocks costs one memory round trip.  Blocks past the row end
-  // load block nb - 1 again and are not accumulated.
-  for (int b0 = lane; b0 < nb; b0 += U * kWave) {
+  // up to 64 U blocks costs one memory round trip.  Blocks past the slice
+  // end load block be - 1 again and are not accumulated.
+  for (int b0 = bb + lane; b0 < be; b0 += U * kWave) {
     uint4_t wq[U][R];
     uint16_t d4h[U][R];
     uint4_t aq0[U][M], aq1[U][M];
     uint16_t d8h[U][M], s8h[U][M];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int b = min(b0 + u * kWave, nb - 1);
+      const int b = min(b0 + u * kWave, be - 1);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         wq[u][r] = NT ? load16_nt(wrow[r] + 16 * b) : load16(wrow[r] + 16 * b);
@@ -89,7 +100,7 @@ __global__ __launch_bounds__(256) void mmvq_q4_0_kernel(
     issue_all();
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const bool live = b0 + u * kWave < nb;
+      const bool live = b0 + u * kWave < be;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         // low nibbles = codes 0..15 of the block, high nibbles = codes 16..31
@@ -121,7 +132,15 @@ __global__ __launch_bounds__(256) void mmvq_q4_0_kernel(
   float v[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) v[i] = (i < R * M) ? acc[i / M][i % M] : 0.0f;
-  const float total = wave_reduce_transpose<V>(v, lane);
+  float total = wave_reduce_transpose<V>(v, lane);
+  if constexpr (KS > 1) {
+    __shared__ float part[4][kWave];
+    part[wave][lane] = total;
+    wg_barrier();
+    if (ks != 0) return;
+#pragma unroll
+    for (int v2 = 1; v2 < KS; ++v2) total += part[wave + v2][lane];
+  }
   constexpr int SHIFT = 6 - Log2<V>::value;
   const int idx = lane >> SHIFT;
   if ((lane & ((1 << SHIFT) - 1)) == 0 && idx < R * M) {
@@ -879,13 +898,14 @@ static hipError_t launch_lds(const uint8_t *w_qs, const uint16_t *w_d, int N, in
 #undef SKINNY_LDS
 }
 
-template <int M, int R, int U>
+template <int M, int R, int U, int KS = 1>
 static hipError_t launch_mru(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                              const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
                              float *y, hipStream_t stream) {
-  const int waves = (N + R - 1) / R;
-  const int blocks = (waves + 3) / 4;
-  hipLaunchKernelGGL((mmvq_q4_0_kernel<M, R, U, true>), dim3(blocks), dim3(256), 0, stream,
+  const int groups = (N + R - 1) / R;                 // row groups of KS waves each
+  const int per_block = 4 / KS;
+  const int blocks = (groups + per_block - 1) / per_block;
+  hipLaunchKernelGGL((mmvq_q4_0_kernel<M, R, U, true, KS>), dim3(blocks), dim3(256), 0, stream,
                      w_qs, w_d, N, K, a_qs, a_d, a_s, y);
   return hipGetLastError();
 }
@@ -893,16 +913,22 @@ static hipError_t launch_mru(const uint8_t *w_qs, const uint16_t *w_d, int N, in
 // Vector kernel shape: two rows per wave (a handful of 128-bit weight loads
 // in flight per lane, many waves) measured best on MI355X at M <= 4 on
 // every Llama-2-7B shape.  At M <= 2 each lane loads all of its blocks of a
-// row in one round (U = blocks per lane, up to 8 = K 16384; longer rows take
-// rounds of 8) -- long rows are otherwise bound by successive memory round
-// trips (7.8 -> 6.3 us for an 11008 x 4096 matrix; with U = 8, 14336 x 4096
-// 9.7 -> 7.7 us and 13824 x 5120 11.9 -> 9.8 us at M = 1).
+// row in one round (U = blocks per lane, up to 8 = K 16384) -- long rows are
+// otherwise bound by successive memory round trips (7.8 -> 6.3 us for an
+// 11008 x 4096 matrix; with U = 8, 14336 x 4096 9.7 -> 7.7 us and
+// 13824 x 5120 11.9 -> 9.8 us at M = 1).  Up to 12 blocks per lane (K 24576)
+// two waves split each row, one round of up to 6 blocks each (17408 x 5120
+// 12.8 -> 11.2 us at M = 1, 16.1 -> 14.6 at M = 2); longer rows take rounds
+// of 6, which measured as fast as a split or rounds of 8 there (28672 x 4096
+// and 40960 x 2048).
 template <int M>
 static hipError_t launch_m(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                            const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
                            float *y, hipStream_t stream) {
   if constexpr (M <= 2) {
     const int per_lane = ((K >> 5) + kWave - 1) / kWave;
+    if (per_lane > 12) return launch_mru<M, 2, 6>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+    if (per_lane > 8) return launch_mru<M, 2, 6, 2>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
     if (per_lane > 6) return launch_mru<M, 2, 8>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
     if (per_lane > 4) return launch_mru<M, 2, 6>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
     if (per_lane > 3) return launch_mru<M, 2, 4>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);

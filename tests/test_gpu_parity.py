@@ -168,7 +168,10 @@ def run_q4(w_qs, w_d, a_qs, a_d, a_s):
                                  # narrow matrix-core route past the staged kernels'
                                  # N and K limits (eight K slices), and the staged
                                  # kernel in rounds at N = 6144
-                                 (7000, 12800), (6144, 2048)])
+                                 (7000, 12800), (6144, 2048),
+                                 # long rows at M <= 2: K split over two waves,
+                                 # rounds of six
+                                 (333, 20480), (97, 40960)])
 def test_mmvq_q4_0_vs_oracle(M, N, K):
     _check_q4_0(M, N, K)
 
@@ -201,7 +204,9 @@ Q4_GATE = [
     (1, 25000, 4096),     # vector kernel, many workgroups
     (1, 300, 11008),      # vector kernel, six blocks per lane
     (1, 1031, 13824),     # vector kernel, one round of eight blocks per lane
-    (1, 300, 20480),      # vector kernel, rounds of eight blocks per lane
+    (1, 300, 20480),      # vector kernel, K split over two waves (six blocks each)
+    (1, 1031, 28672),     # vector kernel, rounds of six blocks per lane
+    (2, 301, 17408),      # vector kernel at M = 2, K split over two waves
     (2, 1031, 4096),      # vector kernel at M = 2
     (2, 300, 16384),      # vector kernel at M = 2, eight blocks per lane
     (2, 9000, 4096),      # plain staged-activation kernel (M = 2, N >= 8192)
@@ -373,6 +378,7 @@ def run_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d):
 
 
 KQ_SHAPES = [(1, 256), (4096 + 37, 256), (4099, 1280), (257, 12288), (1000, 4096), (63, 16384),
+             (301, 13824), (77, 20480),   # one round of eight blocks per lane; rounds of six
              (16384 + 9, 512),   # four-row vector shapes; two waves share activations (M >= 3)
              (28800 + 5, 512)]   # four waves share activations (Q4_K, M >= 3)
 
@@ -423,6 +429,7 @@ def _q4_k_gate_bound(w_qs, w_hdr, a_qs, a_s):
 Q4K_GATE = [
     (1, 300, 4096, 7), (2, 300, 4096, 7),       # vector kernel
     (1, 1031, 13824, 3), (2, 300, 16384, 3),    # vector kernel, eight blocks per lane
+    (1, 300, 20480, 3),                         # vector kernel, rounds of six blocks
     (3, 300, 4096, 7), (8, 300, 4096, 7),       # staged-activation kernel (N < 16384)
     (4, 16393, 4096, 7),                        # vector kernel (M < 5, wide)
     (5, 16393, 4096, 7), (8, 16393, 4096, 7),   # matrix cores, two waves share activations
