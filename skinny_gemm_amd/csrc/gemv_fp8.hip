@@ -383,7 +383,11 @@ static hipError_t launch_mfma_cfg(const uint8_t *w, const float *cs, int N, int 
 }
 
 // Tiles per wave, K split and chunk length, measured on MI355X at M = 3, 4
-// and 8 over K 5120..17408, N 5120..34816.
+// and 8 over K 5120..17408, N 5120..34816.  Up to 256 tiles (N <= 4096) one
+// tile per wave with a four-way K split (eight-way of 2-step chunks when
+// K % 512 != 0) keeps enough waves streaming (measured at M = 8 over K
+// 2048..16384, N 1024..4096: 14336 x 4096 19.3 -> 14.6 us, 8192 x 2048
+// 12.4 -> 8.7 us, 11008 x 4096 18.6 -> 13.0 us).
 template <int MP>
 static hipError_t launch_mfma_mp(const uint8_t *w, const float *cs, int N, int K,
                                  const uint16_t *x, int M, uint16_t *y, hipStream_t stream) {
@@ -397,6 +401,10 @@ static hipError_t launch_mfma_mp(const uint8_t *w, const float *cs, int N, int K
   if (tiles >= 512) {
     if (s4) SKINNY_F8(1, 1, 4);
     SKINNY_F8(1, 1, 2);
+  }
+  if (tiles <= 256) {
+    if (s4) SKINNY_F8(1, 4, 4);
+    SKINNY_F8(1, 8, 2);
   }
   if (s4 && K >= 8192 && M > 4) SKINNY_F8(2, 4, 4);
   if (s4) SKINNY_F8(1, 2, 4);
@@ -630,6 +638,13 @@ static hipError_t launch_m(const uint8_t *w, const float *cs, int N, int K, cons
 constexpr int kF8LdsMaxM = 6;
 constexpr int kF8LdsNarrowN = 8192;         // M = 6: staged only up to this N
 constexpr int kF8LdsMaxMK = 80 * 1024;      // M K binary16 activations in LDS
+// Narrow matrices (N <= 4096) with rows of K >= 8192 take the matrix cores'
+// narrow table from M = 3 (measured on MI355X: 14336 x 4096 at M = 4
+// 15.6 -> 12.7 us, 12288 x 1024 at M = 5 14.5 -> 9.9 us, 8192 x 2048 at M = 3
+// 8.2 -> 7.3 us); shorter rows stay staged (4096 x 4096 at M = 3..5 and
+// 2048 x 2048 5-8% faster staged).
+constexpr int kF8NarrowN = 4096;
+constexpr int kF8NarrowMinK = 8192;
 
 template <int M, int A, int R = 3, int W = 8>
 static hipError_t launch_lds_a(const uint8_t *w, const float *cs, int N, int K,
@@ -692,15 +707,16 @@ static hipError_t launch_vector(const uint8_t *w, const float *cs, int N, int K,
   }
 }
 
-// M <= 5 (M = 6 on narrow matrices) takes the staged-activation vector
-// kernel while the rows fit in LDS.  The matrix-core kernel takes every
-// other M >= 3 in one weight pass
-// when K is a whole number of 256-element chunks.  Otherwise the plain
-// vector kernel serves up to 8 rows per pass over the weights: rows 1..8,
-// 9..16, ...
+// M <= 5 (M = 6 up to N = 8192) takes the staged-activation vector kernel
+// while the rows fit in LDS, except, from M = 3, matrices of at most 4096
+// rows with K >= 8192.  The matrix-core kernel takes every other M >= 3 in
+// one weight pass when K is a whole number of 256-element chunks.
+// Otherwise the plain vector kernel serves up to 8 rows per pass over the
+// weights: rows 1..8, 9..16, ...
 hipError_t launch_gemv_fp8(const uint8_t *w, const float *cs, int N, int K, const uint16_t *x,
                            int M, uint16_t *y, hipStream_t stream) {
-  if (M <= kF8LdsMaxM && M * K <= kF8LdsMaxMK && (M < 6 || N <= kF8LdsNarrowN)) {
+  const bool narrow_long = M >= 3 && N <= kF8NarrowN && K >= kF8NarrowMinK && K % 256 == 0;
+  if (M <= kF8LdsMaxM && M * K <= kF8LdsMaxMK && (M < 6 || N <= kF8LdsNarrowN) && !narrow_long) {
     switch (M) {
       case 1: return launch_lds<1>(w, cs, N, K, x, y, stream);
       case 2: return launch_lds<2>(w, cs, N, K, x, y, stream);

@@ -586,7 +586,12 @@ static hipError_t launch_mfma_cfg(const uint8_t *codes, const uint8_t *scales, f
 // Tiles per wave, K split and chunk length, measured on MI355X at M = 4 and
 // 8 over K 5120..17408, N 5120..34816: wide matrices want two tiles per
 // wave and no split; mid-width ones one tile; narrow ones (few tiles, long
-// K) a four-way split to keep enough waves streaming.
+// K) a four-way split to keep enough waves streaming.  Up to 256 tiles
+// (N <= 4096) one tile per wave with the four-way split keeps twice the
+// waves (measured at M = 4 and 8 over K 2048..16384, N 1024..4096:
+// 14336 x 4096 at M = 4 14.7 -> 10.2 us, 8192 x 2048 9.9 -> 6.8 us,
+// 4096 x 4096 6.7 -> 5.3 us; K % 512 != 0 an eight-way split of 2-step
+// chunks, 11008 x 4096 12.5 -> 9.0 us).
 template <int MP>
 static hipError_t launch_mfma_mp(const uint8_t *codes, const uint8_t *scales, float g, int N,
                                  int K, const uint16_t *x, int M, uint16_t *y,
@@ -601,6 +606,10 @@ static hipError_t launch_mfma_mp(const uint8_t *codes, const uint8_t *scales, fl
   if (tiles >= 512) {
     if (s4) { if (M <= 4) SKINNY_NV(1, 2, 4); SKINNY_NV(1, 1, 4); }
     SKINNY_NV(1, 1, 2);
+  }
+  if (tiles <= 256) {
+    if (s4) SKINNY_NV(1, 4, 4);
+    SKINNY_NV(1, 8, 2);
   }
   if (s4 && K >= 8192) SKINNY_NV(2, 4, 4);
   SKINNY_NV(2, 4, 2);
@@ -685,10 +694,14 @@ static hipError_t launch_lds_a(const uint8_t *codes, const uint8_t *scales, floa
   return hipGetLastError();
 }
 
-// At M = 3 it also beats the matrix cores on matrices up to N = 5120
-// (5120 x 5120 7.6 -> 6.8 us, 17408 x 5120 17.2 -> 16.4 us; wider matrices
-// and M = 4 stay on the matrix cores).
+// At M = 3 it also beats the matrix cores on matrices from N = 4097 up to
+// N = 5120 (5120 x 5120 7.6 -> 6.8 us, 17408 x 5120 17.2 -> 16.4 us; wider
+// matrices and M = 4 stay on the matrix cores).  Up to N = 4096 the matrix
+// cores' narrow table (one tile per wave, K split) is as fast or faster
+// (14336 x 4096 12.5 -> 9.9 us, 8192 x 2048 7.6 -> 6.7 us; 4096 x 4096 and
+// 2048 x 2048 equal).
 constexpr int kNvLdsM3MaxN = 5120;
+constexpr int kNvNarrowN = 4096;
 
 // One activation row on a small matrix (N and K up to 8192) takes two rows
 // per wave: more, smaller workgroups.  Measured at M = 1: 4096 x 4096 4.0 ->
@@ -783,7 +796,7 @@ static hipError_t launch_vector(const uint8_t *codes, const uint8_t *scales, flo
 // serves up to 8 rows per pass: rows 9..M take a second pass.
 hipError_t launch_gemv_nvfp4(const uint8_t *codes, const uint8_t *scales, float g, int N, int K,
                              const uint16_t *x, int M, uint16_t *y, hipStream_t stream) {
-  if (M == 3 && N <= kNvLdsM3MaxN && M * K <= kNvLdsMaxMK)
+  if (M == 3 && N <= kNvLdsM3MaxN && M * K <= kNvLdsMaxMK && (N > kNvNarrowN || K % 256 != 0))
     return launch_lds<3>(codes, scales, g, N, K, x, y, stream);
   if (M <= 2 && M * K <= kNvLdsMaxMK) {
     if (M == 1 && flat_fits(N, K)) return launch_flat(codes, scales, g, N, K, x, y, stream);

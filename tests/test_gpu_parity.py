@@ -508,7 +508,10 @@ def run_nvfp4(codes, scales, g, x):
                                    # matrix-core paths: wide / mid / narrow, chunk of 2
                                    # steps (K % 512 == 256), ragged tiles, K slices
                                    # of unequal length and one empty slice
-                                   (25000, 768, 1.0), (9000, 1280, 1.0), (40, 768, 1.0)])
+                                   (25000, 768, 1.0), (9000, 1280, 1.0), (40, 768, 1.0),
+                                   # narrow (<= 256 tiles): eight K slices of 2-step
+                                   # chunks, the last one short
+                                   (2000, 11008, 1.0)])
 def test_gemv_nvfp4_vs_oracle(M, N, K, g):
     codes, scales, _ = inputs.nvfp4_weights(N, K, 5 * N + K)
     x = inputs.normal_f16_bits(M, K, 2 * M + K)
@@ -652,7 +655,7 @@ def run_fp8(w, cs, x):
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8, 9, 12, 16])
 @pytest.mark.parametrize("N,K", [(1, 16), (4096 + 3, 272), (1030, 5120), (129, 17408),
                                  # matrix-core paths, as for NVFP4
-                                 (25000, 768), (9000, 1280), (40, 768)])
+                                 (25000, 768), (9000, 1280), (40, 768), (2000, 11008)])
 def test_gemv_fp8_vs_oracle(M, N, K):
     w, cs = inputs.fp8_weights(N, K, 3 * N + K)
     x = inputs.normal_f16_bits(M, K, 4 * M + K)
