@@ -487,10 +487,17 @@ static hipError_t launch_mfma_cfg(const uint8_t *w_qs, const uint16_t *w_d, int 
 }
 
 // One tile per wave throughout.  Wide matrices share each activation chunk
-// between two (>= 1024 tiles) or four (>= 1800 tiles) waves; narrower ones
-// split K instead so that enough waves stream (measured on MI355X at M = 4
-// and 8 over the Llama-2-7B shapes: 2000 tiles four-way sharing, 1376 tiles
-// two-way, 768 tiles a two-way K split, 256 tiles an eight-way split).
+// between two (>= 1100 tiles) or four (>= 1800 tiles) waves; narrower ones
+// split K instead so that enough waves stream, and from 800 tiles both.
+// Measured on MI355X at M = 6 and 8 over every configuration, with weights
+// rotating over > 2 GiB: 2000 tiles (4096 x 32000) four-way sharing, 1376
+// and 1536 two-way, 864-1024 tiles two-way sharing with a two-way split
+// (4096 x 16384 at M = 8 12.8 -> 11.4 us, 5120 x 13824 15.3 -> 13.3 us), 512
+// to 768 a two-way split; below 512 tiles a two-way split of 8-step chunks
+// on rows up to K = 8191 (7168 x 7168 at M = 8 15.7 -> 11.8 us, 5120 x 5120
+// 12.4 -> 9.3 us), two tiles per wave with a four-way split on longer rows
+// (13824 x 5120 23.9 -> 17.6 us), four-way below 256 tiles; chunks of 4
+// steps (K % 512 == 256) keep the eight-way split there.
 template <int MP, bool KQ>
 static hipError_t launch_mfma_mp(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                                  const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
@@ -503,13 +510,22 @@ static hipError_t launch_mfma_mp(const uint8_t *w_qs, const uint16_t *w_d, int N
     if (s8) SKINNY_Q4(1, 4, 1, 8);
     SKINNY_Q4(1, 4, 1, 4);
   }
-  if (tiles >= 1024) {
+  if (tiles >= 1100) {
     if (s8) SKINNY_Q4(1, 2, 1, 8);
     SKINNY_Q4(1, 2, 1, 4);
+  }
+  if (tiles >= 800) {
+    if (s8) SKINNY_Q4(1, 2, 2, 8);
+    SKINNY_Q4(1, 2, 2, 4);
   }
   if (tiles >= 512) {
     if (s8) SKINNY_Q4(1, 1, 2, 8);
     SKINNY_Q4(1, 1, 2, 4);
+  }
+  if (s8) {
+    if (tiles < 256) SKINNY_Q4(1, 1, 4, 8);
+    if (K >= 8192) SKINNY_Q4(2, 1, 4, 8);
+    SKINNY_Q4(1, 1, 2, 8);
   }
   SKINNY_Q4(1, 1, 8, 4);
 #undef SKINNY_Q4
@@ -844,13 +860,19 @@ static hipError_t launch_lds_rounds_a(const uint8_t *w_qs, const uint16_t *w_d, 
 
 // Two rows per wave, eight waves (measured on MI355X over the Llama-2-7B
 // shapes: 11008 x 4096 at M = 4 9.4 -> 8.5 us, at M = 8 11.8 -> 11.2 us on the
-// matrix cores; 4096 x 4096 at M = 6 5.25 -> 4.8 us).  It keeps the lead up
-// to N = 6144 (at M = 8 4096 x 6144 10.4 -> 8.5 us and 5120 x 5120
-// 12.5 -> 10.9 us against the matrix cores; at M = 4 13824 x 5120, past the
-// plain staged kernel's K limit, 19.9 -> 13.3 us); from N = 8192 (512
-// workgroups) the matrix cores are faster at M = 8 (8192 x 8192 13.1
-// against 15.4 us).
-constexpr int kQ4RoundsMaxN = 6144;
+// matrix cores; 4096 x 4096 at M = 6 5.25 -> 4.8 us).  At M <= 6 it keeps
+// the lead up to N = 8192 (7168 x 7168 at M = 6 14.6 -> 10.8 us, 2048 x 8192
+// at M = 4 5.3 -> 4.4 us; at M = 4 13824 x 5120, past the plain staged
+// kernel's K limit, 19.9 -> 13.3 us); at M = 7 and 8 only up to N = 4096,
+// as the matrix cores' narrow table is faster above (5120 x 5120 at M = 8
+// 10.8 against 9.3 us).
+constexpr int kQ4RoundsMaxN = 8192;
+constexpr int kQ4RoundsMaxNWide = 4096;   // at M >= 7
+constexpr int kQ4RoundsWideM = 7;
+// Up to N = 2048 and K = 8192 the vector kernel is the fastest at M <= 4
+// (a handful of staged workgroups cannot fill the chip: 8192 x 2048 at M = 3
+// 5.9 -> 5.1 us, 4096 x 2048 at M = 4 3.8 -> 3.4 us).
+constexpr int kQ4VectorNarrowN = 2048;
 
 static int lds_rounds_bytes(int M, int K) { return M * K + 8 * M * (K >> 5); }
 
@@ -942,7 +964,7 @@ static hipError_t launch_m(const uint8_t *w_qs, const uint16_t *w_d, int N, int 
 }
 
 // Plain LDS-staged vector kernel for 3 <= M <= 5 on matrices wider than
-// N = 6144 (narrower ones take the staged kernel in rounds): eight waves per
+// N = 8192 (narrower ones take the staged kernel in rounds): eight waves per
 // workgroup.
 template <int M>
 static hipError_t launch_lds_plain(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
@@ -954,10 +976,15 @@ static hipError_t launch_lds_plain(const uint8_t *w_qs, const uint16_t *w_d, int
 hipError_t launch_mmvq_q4_0(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                             const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
                             int M, float *y, hipStream_t stream) {
-  // Narrow matrices (N <= 6144) from M = 3: the staged kernel in rounds.  Both staged
+  // Small matrices at M <= 4: the vector kernel.
+  if (M >= 3 && M <= 4 && N <= kQ4VectorNarrowN && K <= 8192)
+    return M == 3 ? launch_m<3>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream)
+                  : launch_m<4>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+  // Narrow matrices from M = 3: the staged kernel in rounds.  Both staged
   // kernels copy the Q8_1 scales in 16-byte pieces of 8, so they need
   // M * K / 32 to be a multiple of 8.
-  if (M >= 3 && N <= kQ4RoundsMaxN && (M * (K >> 5)) % 8 == 0 &&
+  const int rounds_max_n = M >= kQ4RoundsWideM ? kQ4RoundsMaxNWide : kQ4RoundsMaxN;
+  if (M >= 3 && N <= rounds_max_n && (M * (K >> 5)) % 8 == 0 &&
       lds_rounds_bytes(M, K) <= 160 * 1024) {
     switch (M) {
       case 3: return launch_lds_rounds<3>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);

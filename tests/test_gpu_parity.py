@@ -206,20 +206,29 @@ Q4_GATE = [
     (1, 1031, 13824),     # vector kernel, one round of eight blocks per lane
     (1, 300, 20480),      # vector kernel, K split over two waves (six blocks each)
     (1, 1031, 28672),     # vector kernel, rounds of six blocks per lane
-    (2, 301, 17408),      # vector kernel at M = 2, K split over two waves
     (2, 1031, 4096),      # vector kernel at M = 2
     (2, 300, 16384),      # vector kernel at M = 2, eight blocks per lane
+    (2, 301, 17408),      # vector kernel at M = 2, K split over two waves
     (2, 9000, 4096),      # plain staged-activation kernel (M = 2, N >= 8192)
-    (3, 1031, 4096), (4, 1031, 4096), (6, 1031, 4096), (8, 1031, 4096),
-    (5, 6000, 4096), (8, 6144, 4096),
-                          # staged kernel in rounds (M >= 3, N <= 6144)
-    (4, 5120, 13824),     # staged kernel in rounds past the plain staged kernel's K
+    (3, 1031, 4096), (4, 1031, 4096), (4, 2048, 8192),
+                          # vector kernel (M <= 4, N <= 2048, K <= 8192)
+    (3, 3000, 4096), (6, 1031, 4096), (8, 1031, 4096), (5, 6000, 4096),
+    (6, 7000, 4096), (6, 8192, 4096),
+                          # staged kernel in rounds (M <= 6 up to N = 8192, M = 7, 8
+                          # up to N = 4096)
+    (4, 5120, 13824), (3, 5000, 12800),
+                          # staged kernel in rounds past the plain staged kernel's K
     (3, 9000, 4096), (4, 25000, 4096), (5, 9000, 4096),
                           # plain staged-activation kernel (M = 3..5, wider)
-    (6, 7000, 4096), (8, 7000, 4096),
-                          # matrix cores, eight K slices, chunks of 4 steps
+    (8, 7000, 4096), (8, 6144, 4096),
+                          # matrix cores below 512 tiles: two K slices of 8 steps
+    (8, 5000, 8192),      # ... two tiles per wave, four K slices (K >= 8192)
+    (8, 3000, 16896),     # ... below 256 tiles: four K slices (activations past LDS)
+    (8, 5000, 3840),      # ... eight K slices of 4 steps (K % 512 == 256)
     (6, 9000, 4096), (7, 9000, 4096), (8, 9000, 4096),
                           # matrix cores, two K slices, chunks of 8 steps
+    (6, 14000, 4096), (8, 16393, 4096), (7, 14000, 3840),
+                          # matrix cores, two waves share activations and two K slices
     (6, 25000, 4096), (8, 25000, 4096),
                           # matrix cores, two waves share each activation chunk
     (7, 30000, 4096), (8, 30000, 4096),
@@ -228,7 +237,6 @@ Q4_GATE = [
     (3, 9000, 12800), (4, 9000, 12800),
                           # matrix cores with 4 padded activation rows (K past the
                           # plain staged kernel's limit)
-    (3, 5000, 12800),     # staged kernel in rounds at the same K
 ]
 
 
