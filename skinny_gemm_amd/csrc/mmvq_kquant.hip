@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256) void mmvq_q6_k_kernel(
 }
 
 // Q4_K with the Q8_1 activation rows staged in LDS once per workgroup
-// (M >= 3, matrices up to N = 16383): codes int8 [M][K], then d8 and s8 as
+// (M >= 3, matrices up to N = 6144): codes int8 [M][K], then d8 and s8 as
 // float [M][K/32] each.  The mapping, header sharing and per-block
 // arithmetic are mmvq_q4_k_kernel's; as in the staged Q6_K kernel below,
 // activations are loaded once per workgroup (issued first, first batch
@@ -604,18 +604,22 @@ static hipError_t launch_q6k_m(const uint8_t *w_ql, const uint8_t *w_qh, const i
 #undef SKINNY_Q6K
 }
 
-// Routing.  From M = 3 matrices below N = 16384 take the staged kernel (when
-// the activation rows fit in LDS).  Wider ones take, from M = 5, the Q4_0
-// matrix-core kernel (its header array has the geometry of the Q4_0 block
-// scales; 4096 x 24576 at M = 8 2.5 -> 3.5 TB/s there), and below that the
-// plain vector kernel.  Shapes the staged kernel cannot hold keep the
-// earlier rule: the matrix cores from M = 5 except mid-width short matrices.
-// Staged Q4_K (3 <= M <= 8, N < 16384): three rows per wave on mid-width
+// Routing.  From M = 3 matrices of at most 6144 rows take the staged kernel
+// (when the activation rows fit in LDS), and matrices of fewer than 1100
+// tiles of 16 rows the Q4_0 matrix-core kernel (its header array has the
+// geometry of the Q4_0 block scales).  Wider ones take the matrix cores from
+// M = 5 (4096 x 24576 at M = 8 2.5 -> 3.5 TB/s there), and below that the
+// plain vector kernel.
+// Staged Q4_K (3 <= M <= 8, N <= 6144): three rows per wave on mid-width
 // matrices, two otherwise, eight waves per workgroup (measured on MI355X over
 // the Qwen3-8B projections at M = 3..8: 4096 x 4096 at M = 5 5.9 -> 4.9 us,
-// 12288 x 4096 at M = 4 10.3 -> 8.9 us, 4096 x 6144 at M = 8 8.1 -> 7.3 us;
-// 4096 x 24576 is faster on the other kernels from M = 4 and keeps them).
-constexpr int kQ4kLdsMaxN = 16383;
+// 12288 x 4096 at M = 4 10.3 -> 8.9 us, 4096 x 6144 at M = 8 8.1 -> 7.3 us).
+// From N = 7168 the matrix cores are faster at every M from 3 (measured over
+// every configuration on nine shapes: 8192 x 8192 at M = 8 21.9 -> 14.1 us,
+// 7168 x 7168 at M = 4 13.8 -> 10.7 us, 5120 x 13824 at M = 6 19.2 -> 14.0
+// us; at M = 3 2560 x 10240 and 5120 x 13824 lose 2-4%).
+constexpr int kQ4kLdsMaxN = 6144;
+constexpr int kQ4kMfmaNarrowTiles = 1100;
 
 static int q4k_lds_bytes(int M, int K) { return M * K + 8 * M * (K >> 5); }
 
@@ -668,7 +672,7 @@ hipError_t launch_mmvq_q4_k(const uint8_t *w_qs, const uint8_t *w_hdr, int N, in
     }
   }
   const int tiles = (N + 15) / 16;
-  if (M >= 5 && (tiles >= 512 || tiles <= 256 || K >= 8192))
+  if (M >= 5 || (M >= 3 && tiles < kQ4kMfmaNarrowTiles))
     return launch_mmvq_q4_k_mfma(w_qs, w_hdr, N, K, a_qs, a_d, a_s, M, y, stream);
   switch (M) {
 #define SKINNY_Q4K(MM) \

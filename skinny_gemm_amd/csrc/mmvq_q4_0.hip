@@ -497,7 +497,8 @@ static hipError_t launch_mfma_cfg(const uint8_t *w_qs, const uint16_t *w_d, int 
 // on rows up to K = 8191 (7168 x 7168 at M = 8 15.7 -> 11.8 us, 5120 x 5120
 // 12.4 -> 9.3 us), two tiles per wave with a four-way split on longer rows
 // (13824 x 5120 23.9 -> 17.6 us), four-way below 256 tiles; chunks of 4
-// steps (K % 512 == 256) keep the eight-way split there.
+// steps (K % 512 == 256) keep the eight-way split there.  Q4_K has rows of
+// its own below 1100 tiles.
 template <int MP, bool KQ>
 static hipError_t launch_mfma_mp(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                                  const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
@@ -506,6 +507,21 @@ static hipError_t launch_mfma_mp(const uint8_t *w_qs, const uint16_t *w_d, int N
   const bool s8 = K % 512 == 0;
 #define SKINNY_Q4(T, WR, KS, S) \
   return launch_mfma_cfg<T, WR, KS, S, MP, 1, KQ>(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream)
+  if constexpr (KQ) {
+    // Q4_K (its per-step header decode makes shorter chunks pay below 800
+    // tiles; measured as above: 7168 x 7168 at M = 8 13.6 -> 12.9 us,
+    // 2560 x 10240 8.5 -> 7.9 us against the Q4_0 choices)
+    if (tiles < 1100) {
+      if (tiles >= 800) {
+        if (s8) SKINNY_Q4(1, 2, 2, 8);
+        SKINNY_Q4(1, 2, 2, 4);
+      }
+      if (tiles >= 600) SKINNY_Q4(1, 1, 2, 4);
+      if (tiles > 256) SKINNY_Q4(1, 1, 4, 4);
+      if (s8) SKINNY_Q4(1, 1, 4, 8);
+      SKINNY_Q4(1, 1, 8, 4);
+    }
+  }
   if (tiles >= 1800) {
     if (s8) SKINNY_Q4(1, 4, 1, 8);
     SKINNY_Q4(1, 4, 1, 4);
@@ -523,7 +539,7 @@ static hipError_t launch_mfma_mp(const uint8_t *w_qs, const uint16_t *w_d, int N
     SKINNY_Q4(1, 1, 2, 4);
   }
   if (s8) {
-    if (tiles < 256) SKINNY_Q4(1, 1, 4, 8);
+    if (tiles <= 256) SKINNY_Q4(1, 1, 4, 8);
     if (K >= 8192) SKINNY_Q4(2, 1, 4, 8);
     SKINNY_Q4(1, 1, 2, 8);
   }

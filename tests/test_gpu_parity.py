@@ -438,13 +438,18 @@ Q4K_GATE = [
     (1, 300, 4096, 7), (2, 300, 4096, 7),       # vector kernel
     (1, 1031, 13824, 3), (2, 300, 16384, 3),    # vector kernel, eight blocks per lane
     (1, 300, 20480, 3),                         # vector kernel, rounds of six blocks
-    (3, 300, 4096, 7), (8, 300, 4096, 7),       # staged-activation kernel (N < 16384)
-    (4, 16393, 4096, 7),                        # vector kernel (M < 5, wide)
-    (5, 16393, 4096, 7), (8, 16393, 4096, 7),   # matrix cores, two waves share activations
+    (3, 300, 4096, 7), (8, 300, 4096, 7),       # staged-activation kernel (N <= 6144)
+    (4, 20000, 4096, 7),                        # vector kernel (M < 5, >= 1100 tiles)
+    (3, 7000, 4096, 7), (8, 9000, 16640, 3),    # matrix cores, Q4_K narrow table: four
+                                                # K slices of 4 steps
+    (8, 5000, 16640, 3),                        # ... the same past the staged kernel's LDS
+    (5, 10240, 2560, 7),                        # ... two K slices of 4 steps (600+ tiles)
+    (4, 16393, 4096, 7), (8, 16393, 4096, 7),   # ... two waves share activations, two K
+    (6, 14000, 3840, 7),                        # slices (800+ tiles), chunks of 8 and 4
+    (8, 3000, 20480, 3), (8, 3000, 20736, 3),   # ... <= 256 tiles, activations past LDS:
+                                                # four slices of 8 steps, eight of 4
+    (6, 20000, 4096, 7),                        # matrix cores, two waves share activations
     (8, 28805, 4096, 7),                        # matrix cores, four waves share activations
-    (8, 5000, 16640, 3),                        # matrix cores, eight K slices (activations
-                                                # past the staged kernel's LDS)
-    (8, 9000, 16640, 3),                        # matrix cores, two K slices
 ]
 
 
