@@ -685,8 +685,8 @@ hipError_t launch_mmvq_q4_k(const uint8_t *w_qs, const uint8_t *w_hdr, int N, in
 }
 
 // Staged Q6_K (3 <= M <= 8): one block per lane per round; four rows per
-// wave and four waves on wide matrices, three rows on mid-width ones, two
-// rows and eight waves otherwise (measured on MI355X over the Qwen3-8B
+// wave and four waves on wide matrices, eight waves of one to four rows on
+// mid-width ones (below), two rows and eight waves otherwise (measured on MI355X over the Qwen3-8B
 // projections at M = 4 and 8: at M = 8 4096 x 6144 9.9 -> 8.6 us, 4096 x 4096
 // 7.1 -> 6.4 us, 12288 x 4096 16.9 -> 14.3 us, 4096 x 24576 27.4 -> 27.1 us
 // against the plain kernel).
@@ -725,9 +725,23 @@ template <int M>
 static hipError_t launch_q6k_lds(const uint8_t *w_ql, const uint8_t *w_qh, const int8_t *w_sc,
                                  const uint16_t *w_d, int N, int K, const int8_t *a_qs,
                                  const uint16_t *a_d, float *y, hipStream_t stream) {
-  if (N >= 16384) return launch_q6k_lds_rw<M, 4, 4>(w_ql, w_qh, w_sc, w_d, N, K, a_qs, a_d, y, stream);
-  if (N > 4096) return launch_q6k_lds_rw<M, 3, 8>(w_ql, w_qh, w_sc, w_d, N, K, a_qs, a_d, y, stream);
-  return launch_q6k_lds_rw<M, 2, 8>(w_ql, w_qh, w_sc, w_d, N, K, a_qs, a_d, y, stream);
+#define SKINNY_Q6RW(R, W) \
+  return launch_q6k_lds_rw<M, R, W>(w_ql, w_qh, w_sc, w_d, N, K, a_qs, a_d, y, stream)
+  if (N >= 16384) SKINNY_Q6RW(4, 4);
+  if (N > 4096) {
+    // mid-width matrices: rows of K >= 7168 four rows per wave from M = 6,
+    // two below; shorter rows one row per wave (measured on MI355X over
+    // every R in 1..4 and W in 2, 4, 8 at M = 3, 4, 6, 8 on six shapes:
+    // 8192 x 8192 at M = 8 24.8 -> 16.8 us, 7168 x 7168 at M = 4
+    // 16.7 -> 12.0 us, 5120 x 13824 at M = 8 27.8 -> 22.0 us)
+    if (K >= 7168) {
+      if (M >= 6) SKINNY_Q6RW(4, 8);
+      SKINNY_Q6RW(2, 8);
+    }
+    SKINNY_Q6RW(1, 8);
+  }
+  SKINNY_Q6RW(2, 8);
+#undef SKINNY_Q6RW
 }
 
 hipError_t launch_mmvq_q6_k(const uint8_t *w_ql, const uint8_t *w_qh, const int8_t *w_sc,

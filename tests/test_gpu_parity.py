@@ -387,6 +387,7 @@ def run_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d):
 
 KQ_SHAPES = [(1, 256), (4096 + 37, 256), (4099, 1280), (257, 12288), (1000, 4096), (63, 16384),
              (301, 13824), (77, 20480),   # one round of eight blocks per lane; rounds of six
+             (5000, 8192),                # mid-width staged shapes (Q6_K: two or four rows)
              (16384 + 9, 512),   # four-row vector shapes; two waves share activations (M >= 3)
              (28800 + 5, 512)]   # four waves share activations (Q4_K, M >= 3)
 
@@ -472,6 +473,8 @@ def test_q4_k_integer_gate_bit_exact(M, N, K, sc_mask):
 @pytest.mark.parametrize("M,N,K,sc_max", [
     (1, 300, 4096, 2), (4, 300, 4096, 2), (8, 300, 4096, 2),
     (1, 1031, 13824, 1), (2, 300, 13824, 1),    # vector kernel, eight blocks per lane
+    (3, 6000, 4096, 2),                         # staged, one row per wave (mid-width)
+    (4, 5000, 8192, 1), (6, 5000, 8192, 1),     # staged, two / four rows per wave
 ])
 def test_q6_k_integer_gate_bit_exact(M, N, K, sc_max):
     # unit d, scales in -sc_max..sc_max, integer activations: exact in any order
