@@ -416,19 +416,34 @@ static hipError_t launch_mfma_mp(const uint8_t *w, const float *cs, int N, int K
 // bytes per weight byte of M <= 8; measured on MI355X at M = 12 and 16, K
 // 5120..17408, N 5120..34816: wide matrices take four tiles per wave (each
 // activation chunk feeds four tiles), mid-width ones one, narrow ones split
-// K four ways.
+// K four ways.  Measured again over every configuration on N 2048..8192:
+// 512-599 tiles split K (8192 x 8192 at M = 12 20.9 -> 17.8 us), and up to
+// 256 tiles one tile per wave with a two- or four-way split (28672 x 4096
+// 39.9 -> 29.5 us, 4096 x 4096 11.4 -> 8.5 us).
 static hipError_t launch_mfma_wide(const uint8_t *w, const float *cs, int N, int K,
                                    const uint16_t *x, int M, uint16_t *y, hipStream_t stream) {
   const int tiles = (N + 15) / 16;
   const bool s4 = K % 512 == 0;
 #define SKINNY_F8(T, KS, S) return launch_mfma_cfg<T, 1, KS, S, 16>(w, cs, N, K, x, M, y, stream)
   if (tiles >= 1536) SKINNY_F8(4, 1, 2);
-  if (tiles >= 512) {
+  if (tiles >= 600) {
     if (s4) SKINNY_F8(1, 1, 4);
     SKINNY_F8(1, 2, 2);
   }
-  if (s4 && K >= 8192) SKINNY_F8(2, 4, 4);
-  SKINNY_F8(2, 4, 2);
+  if (tiles >= 512) {
+    if (K >= 8192) SKINNY_F8(2, 4, 2);
+    if (s4) SKINNY_F8(1, 2, 4);
+    SKINNY_F8(1, 2, 2);
+  }
+  if (tiles > 256) {
+    if (s4 && K >= 8192) SKINNY_F8(2, 4, 4);
+    SKINNY_F8(2, 4, 2);
+  }
+  if (s4) {
+    if (K >= 16384) SKINNY_F8(1, 4, 4);
+    SKINNY_F8(1, 2, 4);
+  }
+  SKINNY_F8(1, 4, 2);
 #undef SKINNY_F8
 }
 

@@ -620,18 +620,23 @@ static hipError_t launch_mfma_mp(const uint8_t *codes, const uint8_t *scales, fl
 // bytes per weight byte of M <= 8, so here four waves sharing each
 // activation chunk pays on matrices wide enough to fill the chip with
 // 4-wave workgroups (measured on MI355X at M = 12 and 16, K 5120..17408,
-// N 5120..34816: 2.45 -> 2.70 TB/s on 5120 x 34816); narrow ones split K.
+// N 5120..34816: 2.45 -> 2.70 TB/s on 5120 x 34816); narrower ones split
+// K, with one tile per wave up to 256 tiles (measured over every
+// configuration on N 2048..8192: 8192 x 8192 at M = 12 23.5 -> 13.9 us with
+// the split from 512 tiles, 28672 x 4096 36.2 -> 26.9 us, 4096 x 4096
+// 8.4 -> 6.9 us with one tile per wave).
 static hipError_t launch_mfma_wide(const uint8_t *codes, const uint8_t *scales, float g, int N,
                                    int K, const uint16_t *x, int M, uint16_t *y,
                                    hipStream_t stream) {
   const int tiles = (N + 15) / 16;
 #define SKINNY_NV(T, WR, KS, S) \
   return launch_mfma_cfg<T, WR, KS, S, 16>(codes, scales, g, N, K, x, M, y, stream)
-  if (tiles >= 512) {
+  if (tiles >= 600) {
     if (K % 512 == 0) SKINNY_NV(1, 4, 1, 4);
     SKINNY_NV(2, 2, 1, 2);
   }
-  SKINNY_NV(2, 1, 4, 2);
+  if (tiles > 256) SKINNY_NV(2, 1, 4, 2);
+  SKINNY_NV(1, 1, 4, 2);
 #undef SKINNY_NV
 }
 
