@@ -662,6 +662,12 @@ static hipError_t launch_q4k_lds(const uint8_t *w_qs, const uint8_t *w_hdr, int 
 hipError_t launch_mmvq_q4_k(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
                             const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s, int M,
                             float *y, hipStream_t stream) {
+  // Rows past K = 12288 at M <= 2 on matrices of 4096 rows or more: the
+  // staged kernel (measured on MI355X: 13824 x 5120 at M = 2 16.2 -> 10.3
+  // us, 17408 x 5120 at M = 1 13.2 -> 11.0 us; 12288 x 4096 and N = 2048 lose)
+  if (M <= 2 && K > 12288 && N >= 4096 && q4k_lds_bytes(M, K) <= 160 * 1024)
+    return M == 1 ? launch_q4k_lds<1>(w_qs, w_hdr, N, K, a_qs, a_d, a_s, y, stream)
+                  : launch_q4k_lds<2>(w_qs, w_hdr, N, K, a_qs, a_d, a_s, y, stream);
   if (M >= 3 && N <= kQ4kLdsMaxN && q4k_lds_bytes(M, K) <= 160 * 1024) {
     switch (M) {
 #define SKINNY_Q4L(MM) \
@@ -747,6 +753,14 @@ static hipError_t launch_q6k_lds(const uint8_t *w_ql, const uint8_t *w_qh, const
 hipError_t launch_mmvq_q6_k(const uint8_t *w_ql, const uint8_t *w_qh, const int8_t *w_sc,
                             const uint16_t *w_d, int N, int K, const int8_t *a_qs,
                             const uint16_t *a_d, int M, float *y, hipStream_t stream) {
+  // Long rows at M <= 2 on matrices of 4096 rows or more: the staged kernel
+  // (measured on MI355X: at M = 2 past K = 12288, 14336 x 4096 14.7 -> 10.8
+  // us, 13824 x 5120 20.5 -> 16.1 us; at M = 1 past K = 16384, 28672 x 4096
+  // 20.9 -> 18.6 us; shorter rows, and N = 2048, stay on the vector kernel)
+  if (M <= 2 && (M == 2 ? K > 12288 : K > 16384) && N >= 4096 &&
+      q6k_lds_bytes(M, K) <= kQ6LdsMaxBytes)
+    return M == 1 ? launch_q6k_lds<1>(w_ql, w_qh, w_sc, w_d, N, K, a_qs, a_d, y, stream)
+                  : launch_q6k_lds<2>(w_ql, w_qh, w_sc, w_d, N, K, a_qs, a_d, y, stream);
   if (M >= 3 && q6k_lds_bytes(M, K) <= kQ6LdsMaxBytes) {
     switch (M) {
 #define SKINNY_Q6L(MM) \

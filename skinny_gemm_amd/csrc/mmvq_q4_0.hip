@@ -992,6 +992,18 @@ static hipError_t launch_lds_plain(const uint8_t *w_qs, const uint16_t *w_d, int
 hipError_t launch_mmvq_q4_0(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                             const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
                             int M, float *y, hipStream_t stream) {
+  // Long rows at M <= 2 on matrices of 4096 rows or more: the staged kernel
+  // in rounds (measured on MI355X: at M = 2 rows past K = 12288, 13824 x 5120
+  // 14.2 -> 10.2 us, 14336 x 4096 10.3 -> 8.6 us, 28672 x 4096 16.5 -> 14.8
+  // us; at M = 1 rows past 12 blocks per lane, 28672 x 4096 14.7 -> 13.4
+  // us; shorter rows, and N = 2048, stay on the vector kernel).
+  {
+    const int per_lane = ((K >> 5) + kWave - 1) / kWave;
+    const bool long_rows = M == 2 ? per_lane > 6 : M == 1 && per_lane > 12;
+    if (long_rows && N >= 4096 && (M * (K >> 5)) % 8 == 0 && lds_rounds_bytes(M, K) <= 160 * 1024)
+      return M == 1 ? launch_lds_rounds<1>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream)
+                    : launch_lds_rounds<2>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+  }
   // Small matrices at M <= 4: the vector kernel.
   if (M >= 3 && M <= 4 && N <= kQ4VectorNarrowN && K <= 8192)
     return M == 3 ? launch_m<3>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream)

@@ -210,6 +210,8 @@ Q4_GATE = [
     (2, 300, 16384),      # vector kernel at M = 2, eight blocks per lane
     (2, 301, 17408),      # vector kernel at M = 2, K split over two waves
     (2, 9000, 4096),      # plain staged-activation kernel (M = 2, N >= 8192)
+    (1, 4096, 28672), (2, 4100, 13824),
+                          # staged kernel in rounds for long rows at M <= 2
     (3, 1031, 4096), (4, 1031, 4096), (4, 2048, 8192),
                           # vector kernel (M <= 4, N <= 2048, K <= 8192)
     (3, 3000, 4096), (6, 1031, 4096), (8, 1031, 4096), (5, 6000, 4096),
@@ -388,6 +390,7 @@ def run_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d):
 KQ_SHAPES = [(1, 256), (4096 + 37, 256), (4099, 1280), (257, 12288), (1000, 4096), (63, 16384),
              (301, 13824), (77, 20480),   # one round of eight blocks per lane; rounds of six
              (5000, 8192),                # mid-width staged shapes (Q6_K: two or four rows)
+             (4096, 17408),               # long rows staged at M <= 2
              (16384 + 9, 512),   # four-row vector shapes; two waves share activations (M >= 3)
              (28800 + 5, 512)]   # four waves share activations (Q4_K, M >= 3)
 
@@ -439,6 +442,7 @@ Q4K_GATE = [
     (1, 300, 4096, 7), (2, 300, 4096, 7),       # vector kernel
     (1, 1031, 13824, 3), (2, 300, 16384, 3),    # vector kernel, eight blocks per lane
     (1, 300, 20480, 3),                         # vector kernel, rounds of six blocks
+    (1, 4096, 13824, 3), (2, 4096, 13824, 3),   # staged kernel, long rows at M <= 2
     (3, 300, 4096, 7), (8, 300, 4096, 7),       # staged-activation kernel (N <= 6144)
     (4, 20000, 4096, 7),                        # vector kernel (M < 5, >= 1100 tiles)
     (3, 7000, 4096, 7), (8, 9000, 16640, 3),    # matrix cores, Q4_K narrow table: four
@@ -473,6 +477,7 @@ def test_q4_k_integer_gate_bit_exact(M, N, K, sc_mask):
 @pytest.mark.parametrize("M,N,K,sc_max", [
     (1, 300, 4096, 2), (4, 300, 4096, 2), (8, 300, 4096, 2),
     (1, 1031, 13824, 1), (2, 300, 13824, 1),    # vector kernel, eight blocks per lane
+    (2, 4100, 13824, 1),                        # staged, long rows at M = 2
     (3, 6000, 4096, 2),                         # staged, one row per wave (mid-width)
     (4, 5000, 8192, 1), (6, 5000, 8192, 1),     # staged, two / four rows per wave
 ])
