@@ -719,13 +719,14 @@ def test_gemv_fp8_chunked_vs_oracle(M, N, K):
     check_f16(y, y_acc, fp8_mag(w, cs, x), K, "fp8 M=%d N=%d K=%d" % (M, N, K))
 
 
-@pytest.mark.parametrize("N", [256,             # narrow: three groups of 32 rows
-                               24576 + 256])    # wide: one pass, six column tiles
-def test_gemv_fp8_ninety_six_rows_bit_exact(N):
+@pytest.mark.parametrize("N,K", [(256, 256),          # narrow: three groups of 32 rows
+                                 (256, 512),          # narrow, K % 512 == 0: six groups
+                                                      # of 16 rows with a K split
+                                 (24576 + 256, 256)]) # wide: one pass, six column tiles
+def test_gemv_fp8_ninety_six_rows_bit_exact(N, K):
     # M = 96 on the chunked path: row n holds code n % 256 at element n % 256;
     # x row m is 1 at the elements k with k % 96 == m (so each output has at
     # most one exact term) -- pins the mapping of all 96 activation rows
-    K = 256
     w = np.zeros((N, K), np.uint8)
     codes = np.arange(256)
     codes[[0x7F, 0xFF]] = 0x38
