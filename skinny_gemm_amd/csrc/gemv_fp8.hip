@@ -12,8 +12,9 @@
 // chunks c = l, l + 64, ...: one 128-bit weight load per row, the chunk's
 // activations (M x 32 B) loaded once and reused for all R rows, and a
 // transposing butterfly for the R*M partial sums at the end.  At M <= 5
-// (and M = 6 on narrow matrices) the same mapping runs with the activation
-// rows staged in LDS once per workgroup (gemv_fp8_lds_kernel).
+// (and M = 6 up to 8192 rows) the same mapping runs with the activation
+// rows staged in LDS once per workgroup (gemv_fp8_lds_kernel), except from
+// M = 3 on matrices of at most 4096 rows with K >= 8192 (matrix cores).
 // Bytes per call: N*K + 4*N weights and scales + 2*M*K + 2*M*N.
 #include "device.h"
 #include "launch.h"
@@ -658,7 +659,7 @@ static hipError_t launch_m(const uint8_t *w, const float *cs, int N, int K, cons
   }
 }
 
-// Staged-activation vector kernel (M <= 5, and M = 6 on narrow matrices):
+// Staged-activation vector kernel (M <= 5, and M = 6 up to 8192 rows):
 // three rows per wave, eight waves per workgroup (two rows and four waves on
 // small matrices: at M = 1 with N and K up to 8192, at M = 2 up to 2^24
 // weights, below; measured on MI355X over K

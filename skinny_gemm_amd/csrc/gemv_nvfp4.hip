@@ -20,7 +20,7 @@
 // At M <= 2 the same mapping runs with the activation rows staged in LDS
 // once per workgroup (gemv_nvfp4_lds_kernel, and gemv_nvfp4_flat_kernel,
 // which spreads a wave's rows evenly over its lanes); M >= 3 takes the
-// matrix cores.
+// matrix cores (M = 3 on 4097..5120 rows the staged kernel).
 // Bytes per call: N*K*(1/2 + 1/16) weights + 2*M*K activations + 2*M*N out.
 #include "device.h"
 #include "launch.h"
@@ -677,7 +677,7 @@ static hipError_t launch_m(const uint8_t *codes, const uint8_t *scales, float g,
   }
 }
 
-// Staged-activation vector kernel (M <= 2, and M = 3 up to N = 5120): three
+// Staged-activation vector kernel (M <= 2, and M = 3 on 4097..5120 rows): three
 // rows per wave, four waves per workgroup at M = 1 and eight at M = 2 and 3
 // (measured on MI355X over K 5120 and 17408, N 5120 to 34816: 5120 x 34816 at
 // M = 1 24.7 -> 19.0 us, at M = 2 28.3 -> 24.9 us against the matrix cores;
@@ -795,7 +795,7 @@ static hipError_t launch_vector(const uint8_t *codes, const uint8_t *scales, flo
 
 // M <= 2 takes the staged-activation vector kernel while the rows fit in
 // LDS (its flat variant at M = 1 on wide matrices with K = 3072 or 5120),
-// and so does M = 3 on matrices up to N = 5120.
+// and so does M = 3 on matrices of 4097 to 5120 rows.
 // The matrix-core kernel takes every M >= 3 in one weight pass when K is a
 // whole number of 256-element chunks.  Otherwise the plain vector kernel
 // serves up to 8 rows per pass: rows 9..M take a second pass.
