@@ -39,6 +39,7 @@
 #ifndef SKINNY_GEMM_H
 #define SKINNY_GEMM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -213,6 +214,52 @@ int mmvq_q6_k(const uint8_t *w_ql, const uint8_t *w_qh, const int8_t *w_sc,
 int gemv_nvfp4_w4a16(const uint8_t *w_codes, const uint8_t *w_scales,
                      float global_scale, int N, int K,
                      const uint16_t *x, int M, uint16_t *y, void *stream);
+
+/*
+ * NVFP4 weights pre-permuted into matrix-core operand order.
+ *
+ * "v100-skinny README", "How QPN works": the weights are rearranged once, at
+ * load time, into the order in which the matrix instructions consume them,
+ * so the GEMV's main loop does no shuffling.  The three calls below give the
+ * same product as gemv_nvfp4_w4a16 from such a copy of the weights.
+ *
+ * Packed layout (K % 256 == 0; U = ceil(N/16) tiles of 16 rows, S = K/128
+ * steps of 128 elements, V = ceil(S/8)); lane l = 16 g + i, g < 4, i < 16:
+ *   codes plane: U*S blocks of 1024 bytes, block (u, s) at byte 1024*(u*S + s);
+ *     bytes 16l .. 16l+15 of it = w_codes[16u + i][64s + 16g .. 64s + 16g + 15]
+ *     (elements 128s + 32g .. +31 of that row);
+ *   scale plane, after the codes plane: U*V blocks of 1024 bytes, block (u, v)
+ *     at byte 1024*(U*S + u*V + v); bytes 16l + 2t and 16l + 2t + 1 (t < 8) =
+ *     w_scales[16u + i][8*(8v + t) + 2g] and [.. + 1];
+ *   bytes for rows >= N or steps >= S are zero.
+ */
+
+/*
+ * prepack_nvfp4_size -- bytes of the packed copy of an N x K NVFP4 matrix:
+ * 1024 * U * (S + V).  Host only, no HIP call.
+ *   0 <= N <= SKINNY_MAX_N; K % 256 == 0 (else SKINNY_ERR_SHAPE); bytes != NULL.
+ */
+int prepack_nvfp4_size(int N, int K, size_t *bytes);
+
+/*
+ * prepack_nvfp4 -- write the packed copy of canonical NVFP4 weights.
+ *   w_codes, w_scales as for gemv_nvfp4_w4a16 (w_codes 16-byte aligned,
+ *   w_scales 2-byte aligned); w_packed: prepack_nvfp4_size bytes, 16-byte
+ *   aligned, caller-owned, not overlapping the inputs.  Every byte of it is
+ *   written.  K % 256 == 0.
+ */
+int prepack_nvfp4(const uint8_t *w_codes, const uint8_t *w_scales, int N, int K,
+                  uint8_t *w_packed, void *stream);
+
+/*
+ * gemv_nvfp4_w4a16_packed -- gemv_nvfp4_w4a16 on the packed copy.
+ *   w_packed from prepack_nvfp4 for the same N and K, 16-byte aligned;
+ *   global_scale, x, y, M as for gemv_nvfp4_w4a16 (0 <= M <= 16, one weight
+ *   pass for all M rows); K % 256 == 0.  The result matches the definition
+ *   to float32 summation-order rounding, as gemv_nvfp4_w4a16 does.
+ */
+int gemv_nvfp4_w4a16_packed(const uint8_t *w_packed, float global_scale, int N, int K,
+                            const uint16_t *x, int M, uint16_t *y, void *stream);
 
 /*
  * gemv_fp8_w8a16 -- y = x * W^T for FP8 E4M3 weights and binary16 activations.

@@ -12,12 +12,15 @@ from ._lib import (  # noqa: F401
     SkinnyError,
     gemv_fp8_w8a16,
     gemv_nvfp4_w4a16,
+    gemv_nvfp4_w4a16_packed,
     lib,
     library_path,
     mmvq_q4_0,
     mmvq_q4_0_f32act,
     mmvq_q4_k,
     mmvq_q6_k,
+    prepack_nvfp4,
+    prepack_nvfp4_size,
     quantize_act_q8_1,
     status_string,
 )

@@ -24,7 +24,8 @@ ERR_M = -4
 ERR_LAUNCH = -5
 
 EXPORTS = ("skinny_status_string", "quantize_act_q8_1", "mmvq_q4_0", "mmvq_q4_0_f32act",
-           "mmvq_q4_k", "mmvq_q6_k", "gemv_nvfp4_w4a16", "gemv_fp8_w8a16")
+           "mmvq_q4_k", "mmvq_q6_k", "gemv_nvfp4_w4a16", "prepack_nvfp4_size", "prepack_nvfp4",
+           "gemv_nvfp4_w4a16_packed", "gemv_fp8_w8a16")
 
 _lib = None
 
@@ -64,6 +65,12 @@ def lib():
     L.mmvq_q6_k.restype = I
     L.gemv_nvfp4_w4a16.argtypes = [P, P, ctypes.c_float, I, I, P, I, P, P]
     L.gemv_nvfp4_w4a16.restype = I
+    L.prepack_nvfp4_size.argtypes = [I, I, ctypes.POINTER(ctypes.c_size_t)]
+    L.prepack_nvfp4_size.restype = I
+    L.prepack_nvfp4.argtypes = [P, P, I, I, P, P]
+    L.prepack_nvfp4.restype = I
+    L.gemv_nvfp4_w4a16_packed.argtypes = [P, ctypes.c_float, I, I, P, I, P, P]
+    L.gemv_nvfp4_w4a16_packed.restype = I
     L.gemv_fp8_w8a16.argtypes = [P, P, I, I, P, I, P, P]
     L.gemv_fp8_w8a16.restype = I
     _lib = L
@@ -245,6 +252,47 @@ def gemv_nvfp4_w4a16(w_codes, w_scales, global_scale, x, y=None, stream=None):
         y = torch.empty((M, N), dtype=torch.float16, device=x.device)
     _req(y, "y", _f16_bits_dtypes(), (M, N))
     _run("gemv_nvfp4_w4a16", (w_codes, w_scales, x, y), stream, _ptr(w_codes), _ptr(w_scales),
+         float(global_scale), N, K, _ptr(x), M, _ptr(y))
+    return y
+
+
+def prepack_nvfp4_size(N: int, K: int) -> int:
+    """Bytes of the packed copy of an N x K NVFP4 matrix (K % 256 == 0)."""
+    n = ctypes.c_size_t(0)
+    _check("prepack_nvfp4_size", lib().prepack_nvfp4_size(int(N), int(K), ctypes.byref(n)))
+    return n.value
+
+
+def prepack_nvfp4(w_codes, w_scales, w_packed=None, stream=None):
+    """Canonical NVFP4 weights [N][K/2] codes + [N][K/16] E4M3 scales -> the
+    packed copy (uint8, prepack_nvfp4_size(N, K) bytes)."""
+    torch = _torch()
+    _req(w_codes, "w_codes", (torch.uint8,))
+    N, K2 = w_codes.shape
+    K = 2 * K2
+    _req(w_scales, "w_scales", (torch.uint8, torch.float8_e4m3fn), (N, K // 16))
+    nbytes = prepack_nvfp4_size(N, K)
+    if w_packed is None:
+        w_packed = torch.empty((nbytes,), dtype=torch.uint8, device=w_codes.device)
+    _req(w_packed, "w_packed", (torch.uint8,), (nbytes,))
+    _run("prepack_nvfp4", (w_codes, w_scales, w_packed), stream, _ptr(w_codes), _ptr(w_scales),
+         N, K, _ptr(w_packed))
+    return w_packed
+
+
+def gemv_nvfp4_w4a16_packed(w_packed, N, K, global_scale, x, y=None, stream=None):
+    """Packed NVFP4 weights (from prepack_nvfp4, N x K), binary16 x [M][K]
+    -> binary16 y [M][N]."""
+    torch = _torch()
+    N, K = int(N), int(K)
+    _req(w_packed, "w_packed", (torch.uint8,), (prepack_nvfp4_size(N, K),))
+    _req(x, "x", _f16_bits_dtypes())
+    M = x.shape[0]
+    _req(x, "x", _f16_bits_dtypes(), (M, K))
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    _req(y, "y", _f16_bits_dtypes(), (M, N))
+    _run("gemv_nvfp4_w4a16_packed", (w_packed, x, y), stream, _ptr(w_packed),
          float(global_scale), N, K, _ptr(x), M, _ptr(y))
     return y
 

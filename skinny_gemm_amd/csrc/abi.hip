@@ -123,6 +123,39 @@ int gemv_nvfp4_w4a16(const uint8_t *w_codes, const uint8_t *w_scales, float glob
                                             (hipStream_t)stream));
 }
 
+int prepack_nvfp4_size(int N, int K, size_t *bytes) {
+  const int st = shape_status(N, K, 256);
+  if (st) return st;
+  if (!bytes) return SKINNY_ERR_NULL;
+  const size_t U = ((size_t)N + 15) / 16, S = (size_t)K / 128, V = (S + 7) / 8;
+  *bytes = 1024 * U * (S + V);
+  return SKINNY_OK;
+}
+
+int prepack_nvfp4(const uint8_t *w_codes, const uint8_t *w_scales, int N, int K,
+                  uint8_t *w_packed, void *stream) {
+  const int st = shape_status(N, K, 256);
+  if (st) return st;
+  if (N == 0) return SKINNY_OK;
+  if (!w_codes || !w_scales || !w_packed) return SKINNY_ERR_NULL;
+  if (!aligned(w_codes, 16) || !aligned(w_scales, 2) || !aligned(w_packed, 16))
+    return SKINNY_ERR_ALIGN;
+  return launched(skinny::launch_prepack_nvfp4(w_codes, w_scales, N, K, w_packed,
+                                               (hipStream_t)stream));
+}
+
+int gemv_nvfp4_w4a16_packed(const uint8_t *w_packed, float global_scale, int N, int K,
+                            const uint16_t *x, int M, uint16_t *y, void *stream) {
+  int st = gemv_m_status(M, SKINNY_MAX_M_F16ACT);
+  if (st) return st;
+  if ((st = shape_status(N, K, 256))) return st;
+  if (M == 0 || N == 0) return SKINNY_OK;
+  if (!w_packed || !x || !y) return SKINNY_ERR_NULL;
+  if (!aligned(w_packed, 16) || !aligned(x, 16) || !aligned(y, 2)) return SKINNY_ERR_ALIGN;
+  return launched(skinny::launch_gemv_nvfp4_packed(w_packed, global_scale, N, K, x, M, y,
+                                                   (hipStream_t)stream));
+}
+
 int gemv_fp8_w8a16(const uint8_t *w, const float *channel_scale, int N, int K,
                    const uint16_t *x, int M, uint16_t *y, void *stream) {
   int st = gemv_m_status(M, SKINNY_MAX_M_FP8);

@@ -38,6 +38,13 @@ hipError_t launch_gemv_nvfp4(const uint8_t *w_codes, const uint8_t *w_scales,
                              float g, int N, int K, const uint16_t *x, int M,
                              uint16_t *y, hipStream_t stream);
 
+// Pre-permuted NVFP4 (gemv_nvfp4_packed.hip).
+hipError_t launch_prepack_nvfp4(const uint8_t *codes, const uint8_t *scales, int N, int K,
+                                uint8_t *w_packed, hipStream_t stream);
+
+hipError_t launch_gemv_nvfp4_packed(const uint8_t *w_packed, float g, int N, int K,
+                                    const uint16_t *x, int M, uint16_t *y, hipStream_t stream);
+
 hipError_t launch_gemv_fp8(const uint8_t *w, const float *cs, int N, int K,
                            const uint16_t *x, int M, uint16_t *y, hipStream_t stream);
 

@@ -33,7 +33,9 @@ def L():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["skinny_status_string", "quantize_act_q8_1",
                                            "mmvq_q4_0", "mmvq_q4_0_f32act", "mmvq_q4_k",
-                                           "mmvq_q6_k", "gemv_nvfp4_w4a16", "gemv_fp8_w8a16"])
+                                           "mmvq_q6_k", "gemv_nvfp4_w4a16", "gemv_fp8_w8a16",
+                                           "prepack_nvfp4_size", "prepack_nvfp4",
+                                           "gemv_nvfp4_w4a16_packed"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -238,3 +240,58 @@ def test_k_quant_null_and_alignment(L):
     # the weaker requirements really are weaker
     assert q6k(L, qh=A + 8, y=0) == -1
     assert q6k(L, sc=A + 2, y=0) == -1
+
+
+def nvp(L, w=A, N=64, K=256, x=A, M=1, y=A):
+    return L.gemv_nvfp4_w4a16_packed(V(w), 1.0, N, K, V(x), M, V(y), None)
+
+
+def pre(L, c=A, s=A, N=64, K=256, w=A):
+    return L.prepack_nvfp4(V(c), V(s), N, K, V(w), None)
+
+
+def test_prepack_size_is_whole_tiles_and_scale_blocks(L):
+    import skinny_gemm_amd
+
+    n = ctypes.c_size_t(0)
+    # U = ceil(N/16) tiles, S = K/128 steps, V = ceil(S/8) scale blocks: 1024 U (S + V)
+    for N, K, want in ((1, 256, 1024 * 1 * (2 + 1)), (16, 1024, 1024 * (8 + 1)),
+                       (17, 2304, 1024 * 2 * (18 + 3)), (4096, 4096, 1024 * 256 * (32 + 4)),
+                       (0, 256, 0)):
+        assert L.prepack_nvfp4_size(N, K, ctypes.byref(n)) == 0
+        assert n.value == want, (N, K)
+        assert skinny_gemm_amd.prepack_nvfp4_size(N, K) == want
+    # whole 16-row tiles and 1024-element K give exactly the canonical bytes
+    assert skinny_gemm_amd.prepack_nvfp4_size(5120, 17408) == 5120 * 17408 * 9 // 16
+    assert L.prepack_nvfp4_size(16, 128, ctypes.byref(n)) == -2
+    assert L.prepack_nvfp4_size(16, 0, ctypes.byref(n)) == -2
+    assert L.prepack_nvfp4_size(-1, 256, ctypes.byref(n)) == -2
+    assert L.prepack_nvfp4_size((1 << 24) + 1, 256, ctypes.byref(n)) == -2
+    assert L.prepack_nvfp4_size(16, 256, None) == -1
+
+
+def test_packed_validation(L):
+    assert nvp(L, M=17) == -4
+    assert nvp(L, M=-1) == -4
+    assert nvp(L, M=16, y=0) == -1
+    for K in (0, 128, 32, 384, (1 << 20) + 256):
+        assert nvp(L, K=K) == -2, K
+        assert pre(L, K=K) == -2, K
+    assert nvp(L, K=1 << 20, y=0) == -1
+    assert nvp(L, N=-1) == -2
+    assert nvp(L, N=(1 << 24) + 1) == -2
+    for kw in ("w", "x", "y"):
+        assert nvp(L, **{kw: 0}) == -1, kw
+    for kw in ("c", "s", "w"):
+        assert pre(L, **{kw: 0}) == -1, kw
+    for kw, off in (("w", 8), ("x", 8), ("y", 1)):
+        assert nvp(L, **{kw: A + off}) == -3, kw
+    for kw, off in (("c", 8), ("s", 1), ("w", 8)):
+        assert pre(L, **{kw: A + off}) == -3, kw
+    # scales need only 2-byte alignment, y only 2
+    assert pre(L, s=A + 2, c=0) == -1
+    assert nvp(L, y=A + 2, w=0) == -1
+    # nothing to compute
+    assert nvp(L, w=0, x=0, y=0, M=0) == 0
+    assert nvp(L, w=0, x=0, y=0, N=0) == 0
+    assert pre(L, c=0, s=0, w=0, N=0) == 0

@@ -665,6 +665,126 @@ def test_gemv_nvfp4_sixteen_rows_bit_exact():
     assert np.count_nonzero(f16(want)) > 200
 
 
+# ------------------------------------------------------------------ NVFP4, pre-permuted
+
+def run_nvfp4_packed(codes, scales, g, x):
+    import skinny_gemm_amd as sk
+
+    N, K = codes.shape[0], 2 * codes.shape[1]
+    wp = sk.prepack_nvfp4(dev(codes), dev(scales))
+    return host(sk.gemv_nvfp4_w4a16_packed(wp, N, K, g, dev(x)), np.uint16)
+
+
+def packed_layout_source(N, K):
+    """For every byte of the packed copy, the flat index of the canonical
+    byte it holds (codes: n * K/2 + b; scales: N * K/2 + n * K/16 + b), or -1
+    for a zero byte, from the layout the header defines."""
+    U, S = (N + 15) // 16, K // 128
+    V = (S + 7) // 8
+    src = np.full(1024 * U * (S + V), -1, np.int64)
+    for u in range(U):
+        for l in range(64):
+            i, g = l % 16, l // 16
+            n = 16 * u + i
+            if n >= N:
+                continue
+            for s in range(S):
+                at = 1024 * (u * S + s) + 16 * l
+                src[at:at + 16] = n * (K // 2) + 64 * s + 16 * g + np.arange(16)
+            for v in range(V):
+                for t in range(8):
+                    step = 8 * v + t
+                    if step >= S:
+                        continue
+                    at = 1024 * (U * S + u * V + v) + 16 * l + 2 * t
+                    src[at:at + 2] = N * (K // 2) + n * (K // 16) + 8 * step + 2 * g + np.arange(2)
+    return src
+
+
+@pytest.mark.parametrize("N,K", [(40, 2304), (16, 256), (1, 1280)])
+def test_prepack_nvfp4_layout(N, K):
+    # every canonical byte gets a distinct 16-bit label (index + 1), sent
+    # through prepack_nvfp4 as two byte planes; the packed copy must hold
+    # each label exactly where the layout puts it, and 0 in the padding
+    import skinny_gemm_amd as sk
+
+    nc, ns = N * K // 2, N * K // 16
+    label = np.arange(1, nc + ns + 1, dtype=np.int64)
+    assert label[-1] < 1 << 16
+    got = np.zeros(sk.prepack_nvfp4_size(N, K), np.int64)
+    for shift in (0, 8):
+        plane = ((label >> shift) & 255).astype(np.uint8)
+        codes = plane[:nc].reshape(N, K // 2)
+        scales = plane[nc:].reshape(N, K // 16)
+        got |= host(sk.prepack_nvfp4(dev(codes), dev(scales))).astype(np.int64) << shift
+    assert np.array_equal(got - 1, packed_layout_source(N, K))
+
+
+# (N, K) of the packed parity test: every row of the packed dispatch tables
+# at M <= 2, M = 3..4 and M = 5..16 (tiles >= 1536, 1100..1535, 800..1099,
+# 600..799, 512..599, 257..511 with K >= 8192 or shorter, <= 256 with
+# K <= 8192 or longer), each with chunks of 4 steps (K % 512 == 0) and of 2
+# (K % 512 == 256), ragged last tiles, and K slices of unequal length
+NVP_SHAPES = [(25000, 768), (25000, 1024), (20000, 768), (20000, 1024), (16000, 1280),
+              (16000, 1024), (9000, 1280), (9000, 2048), (5000, 8192), (5000, 8448),
+              (5000, 1280), (2000, 4096), (40, 768), (2000, 11008), (1, 256), (129, 17408)]
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 9, 12, 16])
+@pytest.mark.parametrize("N,K", NVP_SHAPES)
+def test_gemv_nvfp4_packed_vs_oracle(M, N, K):
+    codes, scales, g = inputs.nvfp4_weights(N, K, 7 * N + K)
+    x = inputs.normal_f16_bits(M, K, 3 * M + K)
+    y = run_nvfp4_packed(codes, scales, g, x)
+    y_acc, _ = oracle.gemv_nvfp4_w4a16(codes, scales, g, x)
+    check_f16(y, y_acc, nvfp4_mag(codes, scales, g, x), K,
+              "nvfp4 packed M=%d N=%d K=%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 512, 5120), (2, 512, 5120), (8, 512, 5120),
+                                   (16, 512, 5120), (8, 25000, 768)])
+def test_gemv_nvfp4_packed_outliers(M, N, K):
+    # activation outliers of +-2e4, as for the canonical layout
+    codes, scales, _ = inputs.nvfp4_weights(N, K, 61 + K)
+    x = inputs.normal_f16_bits(M, K, 62 + M).view(np.float16).copy()
+    rng = np.random.Generator(np.random.PCG64(63 + M))
+    idx = rng.integers(0, K, size=(M, 24))
+    for m in range(M):
+        x[m, idx[m]] = np.float16(2.0e4) * np.where(rng.integers(0, 2, 24) == 0, -1, 1)
+    xb = x.view(np.uint16)
+    y = run_nvfp4_packed(codes, scales, 1.0, xb)
+    y_acc, _ = oracle.gemv_nvfp4_w4a16(codes, scales, 1.0, xb)
+    assert np.all(np.isfinite(y_acc))
+    check_f16(y, y_acc, nvfp4_mag(codes, scales, 1.0, xb), K,
+              "nvfp4 packed outliers M=%d N=%d K=%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 16])
+def test_gemv_nvfp4_packed_one_term_bit_exact(M):
+    # one exact E2M1 x E4M3 term per output through the packed copy, at every
+    # padded row count: row n holds code (n // 16) % 16 at element n under
+    # group scale n (NaN codes replaced by 1.0), every other code +0; x row m
+    # is 1 at the elements k with k % 16 == m, so y[m][n] is that one term
+    # when n % 16 == m and 0 otherwise, and each row m < M meets every code
+    N = K = 256
+    codes = np.zeros((N, K // 2), np.uint8)
+    n = np.arange(N)
+    code = (n // 16) % 16
+    codes[n, n // 2] = np.where(n % 2 == 0, code, code << 4).astype(np.uint8)
+    scales = np.zeros((N, K // 16), np.uint8)
+    sc = np.arange(256)
+    sc[[0x7F, 0xFF]] = 0x38
+    scales[n, n // 16] = sc
+    x = np.zeros((16, K), np.float16)
+    for m in range(16):
+        x[m, m::16] = 1.0
+    xb = x.view(np.uint16)[:M]
+    y = run_nvfp4_packed(codes, scales, 1.0, xb)
+    _, want = oracle.gemv_nvfp4_w4a16(codes, scales, 1.0, xb)
+    assert np.array_equal(y, want)
+    assert np.count_nonzero(f16(want)) >= 12 * M
+
+
 # ------------------------------------------------------------------ FP8
 
 def run_fp8(w, cs, x):
@@ -926,6 +1046,21 @@ def test_nvfp4_full_sizes_sampled(M):
         y_acc, _ = oracle.gemv_nvfp4_w4a16(codes[rows], scales[rows], g, x)
         check_f16(y[:, rows], y_acc, nvfp4_mag(codes[rows], scales[rows], g, x), K,
                   "nvfp4 full M=%d %dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 16])
+def test_nvfp4_packed_full_sizes_sampled(M):
+    import skinny_gemm_amd as sk
+
+    for si, (N, K) in enumerate(QWEN_FP):
+        codes, scales, g = inputs.nvfp4_weights(N, K, inputs.seed(3, si, 0))
+        x = inputs.normal_f16_bits(M, K, inputs.seed(3, si, 2) + M)
+        wp = sk.prepack_nvfp4(dev(codes), dev(scales))
+        y = host(sk.gemv_nvfp4_w4a16_packed(wp, N, K, g, dev(x)), np.uint16)
+        rows = sample_rows(N, seed=si)
+        y_acc, _ = oracle.gemv_nvfp4_w4a16(codes[rows], scales[rows], g, x)
+        check_f16(y[:, rows], y_acc, nvfp4_mag(codes[rows], scales[rows], g, x), K,
+                  "nvfp4 packed full M=%d %dx%d" % (M, N, K))
 
 
 @pytest.mark.parametrize("M", [1, 4, 8, 16, 32, 96])
