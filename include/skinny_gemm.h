@@ -216,6 +216,50 @@ int gemv_nvfp4_w4a16(const uint8_t *w_codes, const uint8_t *w_scales,
                      const uint16_t *x, int M, uint16_t *y, void *stream);
 
 /*
+ * Q4_0 weights pre-permuted into matrix-core operand order.
+ *
+ * "v100-skinny README", "How QPN works": the weights are rearranged once, at
+ * load time, into the order in which the matrix instructions consume them,
+ * so the main loop does no shuffling.  The calls below give the same product
+ * as mmvq_q4_0 from such a copy of the weights (same Q8_1 activations, same
+ * exact int32 block sums).
+ *
+ * Packed layout (K % 256 == 0; U = ceil(N/16) tiles of 16 rows, P = K/128,
+ * V = ceil(K/512); nb = K/32 blocks per row); lane l = 16 g + j with
+ * g = 2 h + b (h, b < 2), j < 16:
+ *   codes plane: U*P blocks of 1024 bytes, block (u, p) at byte 1024*(u*P + p);
+ *     bytes 16l + 8e .. 16l + 8e + 7 (e < 2) of it =
+ *     w_qs[16u + j][16*(4p + 2e + h) + 8b .. + 7];
+ *   scale plane, after the codes plane: U*V blocks of 512 bytes, block (u, v)
+ *     at byte 1024*U*P + 512*(u*V + v); the binary16 at bytes 256h + 16j + 2t
+ *     (t < 8) = w_d[16u + j][16v + 2t + h];
+ *   bytes for rows >= N or blocks >= nb are zero.
+ */
+
+/* prepack_q4_0_size -- bytes of the packed copy: 1024*U*P + 512*U*V.  Host
+ * only.  0 <= N <= SKINNY_MAX_N; K % 256 == 0 (else SKINNY_ERR_SHAPE). */
+int prepack_q4_0_size(int N, int K, size_t *bytes);
+
+/*
+ * prepack_q4_0 -- write the packed copy of planar Q4_0 weights.
+ *   w_qs, w_d as for mmvq_q4_0 (w_qs 16-byte aligned, w_d 2-byte aligned);
+ *   w_packed: prepack_q4_0_size bytes, 16-byte aligned, caller-owned, not
+ *   overlapping the inputs.  Every byte of it is written.  K % 256 == 0.
+ */
+int prepack_q4_0(const uint8_t *w_qs, const uint16_t *w_d, int N, int K, uint8_t *w_packed,
+                 void *stream);
+
+/*
+ * mmvq_q4_0_packed -- mmvq_q4_0 on the packed copy.
+ *   w_packed from prepack_q4_0 for the same N and K, 16-byte aligned;
+ *   a_qs, a_d, a_s, y, M as for mmvq_q4_0 (0 <= M <= SKINNY_MAX_M_GEMV);
+ *   K % 256 == 0.  Block sums are exact integers; the float result matches
+ *   the definition to float32 summation-order rounding.
+ */
+int mmvq_q4_0_packed(const uint8_t *w_packed, int N, int K, const int8_t *a_qs,
+                     const uint16_t *a_d, const uint16_t *a_s, int M, float *y, void *stream);
+
+/*
  * NVFP4 weights pre-permuted into matrix-core operand order.
  *
  * "v100-skinny README", "How QPN works": the weights are rearranged once, at

@@ -17,9 +17,12 @@ from ._lib import (  # noqa: F401
     library_path,
     mmvq_q4_0,
     mmvq_q4_0_f32act,
+    mmvq_q4_0_packed,
     mmvq_q4_k,
     mmvq_q6_k,
     prepack_nvfp4,
+    prepack_q4_0,
+    prepack_q4_0_size,
     prepack_nvfp4_size,
     quantize_act_q8_1,
     status_string,

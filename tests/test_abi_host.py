@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
                                            "mmvq_q4_0", "mmvq_q4_0_f32act", "mmvq_q4_k",
                                            "mmvq_q6_k", "gemv_nvfp4_w4a16", "gemv_fp8_w8a16",
                                            "prepack_nvfp4_size", "prepack_nvfp4",
-                                           "gemv_nvfp4_w4a16_packed"])
+                                           "gemv_nvfp4_w4a16_packed", "prepack_q4_0_size",
+                                           "prepack_q4_0", "mmvq_q4_0_packed"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -295,3 +296,54 @@ def test_packed_validation(L):
     assert nvp(L, w=0, x=0, y=0, M=0) == 0
     assert nvp(L, w=0, x=0, y=0, N=0) == 0
     assert pre(L, c=0, s=0, w=0, N=0) == 0
+
+
+def q4p(L, w=A, N=64, K=256, aq=A, ad=A, as_=A, M=1, y=A):
+    return L.mmvq_q4_0_packed(V(w), N, K, V(aq), V(ad), V(as_), M, V(y), None)
+
+
+def q4pre(L, w=A, d=A, N=64, K=256, p=A):
+    return L.prepack_q4_0(V(w), V(d), N, K, V(p), None)
+
+
+def test_prepack_q4_0_size(L):
+    import skinny_gemm_amd
+
+    n = ctypes.c_size_t(0)
+    # 1024 U P + 512 U V, U = ceil(N/16), P = K/128, V = ceil(K/512)
+    for N, K, want in ((1, 256, 1024 * 2 + 512), (16, 512, 1024 * 4 + 512),
+                       (17, 768, 2 * (1024 * 6 + 512 * 2)), (0, 256, 0),
+                       (4096, 4096, 256 * (1024 * 32 + 512 * 8))):
+        assert L.prepack_q4_0_size(N, K, ctypes.byref(n)) == 0
+        assert n.value == want, (N, K)
+        assert skinny_gemm_amd.prepack_q4_0_size(N, K) == want
+    # whole tiles and K % 512 == 0: exactly the canonical bytes
+    assert skinny_gemm_amd.prepack_q4_0_size(4096, 11264) == 4096 * 11264 * 18 // 32
+    for N, K in ((16, 128), (16, 0), (-1, 256), ((1 << 24) + 1, 256)):
+        assert L.prepack_q4_0_size(N, K, ctypes.byref(n)) == -2
+    assert L.prepack_q4_0_size(16, 256, None) == -1
+
+
+def test_q4_0_packed_validation(L):
+    assert q4p(L, M=9) == -4
+    assert q4p(L, M=-1) == -4
+    assert q4p(L, M=8, y=0) == -1
+    for K in (0, 128, 32, 384, (1 << 20) + 256):
+        assert q4p(L, K=K) == -2, K
+        assert q4pre(L, K=K) == -2, K
+    assert q4p(L, K=1 << 20, y=0) == -1
+    assert q4p(L, N=-1) == -2
+    assert q4p(L, N=(1 << 24) + 1) == -2
+    for kw in ("w", "aq", "ad", "as_", "y"):
+        assert q4p(L, **{kw: 0}) == -1, kw
+    for kw in ("w", "d", "p"):
+        assert q4pre(L, **{kw: 0}) == -1, kw
+    for kw, off in (("w", 8), ("aq", 8), ("ad", 8), ("as_", 8), ("y", 2)):
+        assert q4p(L, **{kw: A + off}) == -3, kw
+    for kw, off in (("w", 8), ("d", 1), ("p", 8)):
+        assert q4pre(L, **{kw: A + off}) == -3, kw
+    assert q4pre(L, d=A + 2, w=0) == -1
+    assert q4p(L, y=A + 4, w=0) == -1
+    assert q4p(L, w=0, aq=0, ad=0, as_=0, y=0, M=0) == 0
+    assert q4p(L, w=0, aq=0, ad=0, as_=0, y=0, N=0) == 0
+    assert q4pre(L, w=0, d=0, p=0, N=0) == 0

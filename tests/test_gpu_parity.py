@@ -194,6 +194,113 @@ def _check_q4_0(M, N, K):
     check_f32(y, ref, q4_mag(w_qs, w_d, a_qs, a_d, a_s), K, "q4_0 M=%d N=%d K=%d" % (M, N, K))
 
 
+# ------------------------------------------------------------------ Q4_0, pre-permuted
+
+def run_q4_packed(w_qs, w_d, a_qs, a_d, a_s):
+    import skinny_gemm_amd as sk
+
+    N, K = w_qs.shape[0], 2 * w_qs.shape[1]
+    wp = sk.prepack_q4_0(dev(w_qs), dev(w_d))
+    return host(sk.mmvq_q4_0_packed(wp, N, K, dev(a_qs), dev(a_d), dev(a_s)))
+
+
+def q4_packed_layout_source(N, K):
+    """From the layout the header defines: for every byte of the codes plane
+    the flat index n * K/2 + byte of the code byte it holds, and for every
+    binary16 of the scale plane the flat index n * K/32 + block of the scale
+    it holds (-1 where zero)."""
+    U, P, V, nb = (N + 15) // 16, K // 128, (K + 511) // 512, K // 32
+    codes = np.full(1024 * U * P, -1, np.int64)
+    scl = np.full(256 * U * V, -1, np.int64)
+    for u in range(U):
+        for l in range(64):
+            j, g = l % 16, l // 16
+            h, b = g // 2, g % 2
+            n = 16 * u + j
+            if n >= N:
+                continue
+            for p in range(P):
+                for e in range(2):
+                    at = 1024 * (u * P + p) + 16 * l + 8 * e
+                    codes[at:at + 8] = n * (K // 2) + 16 * (4 * p + 2 * e + h) + 8 * b + np.arange(8)
+        for h in range(2):
+            for j in range(16):
+                n = 16 * u + j
+                if n >= N:
+                    continue
+                for v in range(V):
+                    for t in range(8):
+                        blk = 16 * v + 2 * t + h
+                        if blk < nb:
+                            scl[(512 * (u * V + v) + 256 * h + 16 * j + 2 * t) // 2] = n * nb + blk
+    return codes, scl
+
+
+@pytest.mark.parametrize("N,K", [(40, 2304), (16, 256), (3, 768)])
+def test_prepack_q4_0_layout(N, K):
+    # code bytes carry 16-bit labels (index + 1) sent as two byte planes,
+    # scales carry their index + 1 directly; the packed copy must hold each
+    # label exactly where the layout puts it, and 0 in the padding
+    import skinny_gemm_amd as sk
+
+    nc, ns = N * K // 2, N * K // 32
+    label = np.arange(1, nc + 1, dtype=np.int64)
+    assert nc < 1 << 16 and ns < 1 << 16
+    w_d = np.arange(1, ns + 1, dtype=np.uint16).reshape(N, K // 32)
+    size = sk.prepack_q4_0_size(N, K)
+    U, P = (N + 15) // 16, K // 128
+    got = np.zeros(size, np.int64)
+    for shift in (0, 8):
+        w_qs = ((label >> shift) & 255).astype(np.uint8).reshape(N, K // 2)
+        packed = host(sk.prepack_q4_0(dev(w_qs), dev(w_d)))
+        got |= packed.astype(np.int64) << shift
+    scl = packed[1024 * U * P:].view(np.uint16)
+    want_codes, want_scl = q4_packed_layout_source(N, K)
+    assert np.array_equal(got[:1024 * U * P] - 1, want_codes)
+    assert np.array_equal(scl.astype(np.int64) - 1, want_scl)
+
+
+# (N, K) of the packed Q4_0 tests: every row of the packed dispatch table
+# (>= 1100 tiles, 800..1099, 512..799, 257..511 with K >= 8192 or shorter,
+# <= 256), each with chunks of 8 steps (K % 512 == 0) where it has them and
+# of 4, ragged last tiles and K slices of unequal length
+Q4P_SHAPES = [(30000, 1024), (30000, 768), (25000, 768), (16393, 4096), (16000, 1280),
+              (9000, 1280), (9000, 2048), (5000, 8192), (5000, 1280), (3000, 4096),
+              (129, 17408), (40, 768), (1, 256)]
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("N,K", Q4P_SHAPES)
+def test_mmvq_q4_0_packed_vs_oracle(M, N, K):
+    w_qs, w_d = inputs.q4_0_weights(N, K, 5 * N + K)
+    x = inputs.normal_f32(M, K, 7 * M + K)
+    a_qs, a_d, a_s = oracle.quantize_q8_1(x)
+    y = run_q4_packed(w_qs, w_d, a_qs, a_d, a_s)
+    ref = oracle.mmvq_q4_0(w_qs, w_d, a_qs, a_d, a_s)
+    check_f32(y, ref, q4_mag(w_qs, w_d, a_qs, a_d, a_s), K,
+              "q4_0 packed M=%d N=%d K=%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 6, 8])
+@pytest.mark.parametrize("N,K", [(30000, 1024), (25000, 768), (16393, 4096), (16000, 1280),
+                                 (9000, 1280), (5000, 8192), (3000, 4096), (5000, 1280),
+                                 (40, 768)])
+def test_mmvq_q4_0_packed_integer_gate_bit_exact(M, N, K):
+    # unit scales and integer activations, as for the canonical layout:
+    # every partial sum is an exact integer, so the result is the oracle's
+    # bit for bit
+    x = inputs.q8_1_unit_scale_source(M, K, 290 + M + K)
+    a_qs, a_d, a_s = oracle.quantize_q8_1(x)
+    assert np.all(a_d == 0x3C00)
+    assert 8 * np.abs(a_qs.astype(np.int64)).sum(axis=1).max() < 2 ** 24
+    w_qs, _ = inputs.q4_0_weights(N, K, 291 + N)
+    w_d = np.full((N, K // 32), 0x3C00, np.uint16)
+    y = run_q4_packed(w_qs, w_d, a_qs, a_d, a_s)
+    exact = oracle.mmvq_q4_0(w_qs, w_d, a_qs, a_d, a_s)
+    assert np.array_equal(exact, np.rint(exact))
+    assert np.array_equal(y.astype(np.float64), exact), "M=%d N=%d K=%d" % (M, N, K)
+
+
 # (M, N, K) of the exact-integer gate, one or more per dispatch route of
 # mmvq_q4_0 (the route each reaches is named).  With unit scales every block
 # term isum - 8 s8 = sum (code - 8) q8 is an integer, and the sum of their
@@ -1021,6 +1128,22 @@ def test_q4_0_full_sizes_sampled(M):
         ref = oracle.mmvq_q4_0(w_qs[rows], w_d[rows], a_qs, a_d, a_s)
         mag = q4_mag(w_qs[rows], w_d[rows], a_qs, a_d, a_s)
         check_f32(y[:, rows], ref, mag, K, "q4_0 full M=%d %dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
+def test_q4_0_packed_full_sizes_sampled(M):
+    import skinny_gemm_amd as sk
+
+    for si, (N, K) in enumerate(LLAMA_Q4):
+        w_qs, w_d = inputs.q4_0_weights(N, K, inputs.seed(1, si, 0))
+        x = inputs.normal_f32(M, K, inputs.seed(2, si, 2) + M)
+        a_qs, a_d, a_s = oracle.quantize_q8_1(x)
+        wp = sk.prepack_q4_0(dev(w_qs), dev(w_d))
+        y = host(sk.mmvq_q4_0_packed(wp, N, K, dev(a_qs), dev(a_d), dev(a_s)))
+        rows = sample_rows(N, seed=si)
+        ref = oracle.mmvq_q4_0(w_qs[rows], w_d[rows], a_qs, a_d, a_s)
+        mag = q4_mag(w_qs[rows], w_d[rows], a_qs, a_d, a_s)
+        check_f32(y[:, rows], ref, mag, K, "q4_0 packed full M=%d %dx%d" % (M, N, K))
 
 
 @pytest.mark.parametrize("M", [1, 2])
