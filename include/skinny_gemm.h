@@ -327,6 +327,43 @@ int gemv_nvfp4_w4a16_packed(const uint8_t *w_packed, float global_scale, int N, 
 int gemv_fp8_w8a16(const uint8_t *w, const float *channel_scale, int N, int K,
                    const uint16_t *x, int M, uint16_t *y, void *stream);
 
+/*
+ * FP8 weights pre-permuted into matrix-core operand order.
+ *
+ * "v100-skinny README", "How QPN works": the weights are rearranged once, at
+ * load time, into the order in which the matrix instructions consume them.
+ * The calls below give the same product as gemv_fp8_w8a16 from such a copy.
+ *
+ * Packed layout (K % 256 == 0; U = ceil(N/16) tiles of 16 rows, S = K/128
+ * steps); lane l = 16 g + i, g < 4, i < 16: U*S blocks of 2048 bytes, block
+ * (u, s) at byte 2048*(u*S + s); bytes 1024e + 16l .. 1024e + 16l + 15
+ * (e < 2) of it = w[16u + i][128s + 32g + 16e .. + 15]; bytes for rows >= N
+ * are zero.  The channel scales are not part of the copy.
+ */
+
+/* prepack_fp8_size -- bytes of the packed copy: 16 * U * K.  Host only.
+ * 0 <= N <= SKINNY_MAX_N; K % 256 == 0 (else SKINNY_ERR_SHAPE). */
+int prepack_fp8_size(int N, int K, size_t *bytes);
+
+/*
+ * prepack_fp8 -- write the packed copy of an E4M3 weight matrix.
+ *   w as for gemv_fp8_w8a16 (16-byte aligned); w_packed: prepack_fp8_size
+ *   bytes, 16-byte aligned, caller-owned, not overlapping w.  Every byte of
+ *   it is written.  K % 256 == 0.
+ */
+int prepack_fp8(const uint8_t *w, int N, int K, uint8_t *w_packed, void *stream);
+
+/*
+ * gemv_fp8_w8a16_packed -- gemv_fp8_w8a16 on the packed copy.
+ *   w_packed from prepack_fp8 for the same N and K, 16-byte aligned;
+ *   channel_scale, x, y, M as for gemv_fp8_w8a16 (0 <= M <= SKINNY_MAX_M_FP8);
+ *   K % 256 == 0.  One weight pass for M <= 16; above, one pass on matrices
+ *   of 1536 tiles or more, else one pass per group of 16 rows.  The result
+ *   matches the definition to float32 summation-order rounding.
+ */
+int gemv_fp8_w8a16_packed(const uint8_t *w_packed, const float *channel_scale, int N, int K,
+                          const uint16_t *x, int M, uint16_t *y, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

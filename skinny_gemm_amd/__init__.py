@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     EXPORTS,
     SkinnyError,
     gemv_fp8_w8a16,
+    gemv_fp8_w8a16_packed,
     gemv_nvfp4_w4a16,
     gemv_nvfp4_w4a16_packed,
     lib,
@@ -20,6 +21,8 @@ from ._lib import (  # noqa: F401
     mmvq_q4_0_packed,
     mmvq_q4_k,
     mmvq_q6_k,
+    prepack_fp8,
+    prepack_fp8_size,
     prepack_nvfp4,
     prepack_q4_0,
     prepack_q4_0_size,

@@ -26,7 +26,8 @@ ERR_LAUNCH = -5
 EXPORTS = ("skinny_status_string", "quantize_act_q8_1", "mmvq_q4_0", "mmvq_q4_0_f32act",
            "mmvq_q4_k", "mmvq_q6_k", "prepack_q4_0_size", "prepack_q4_0", "mmvq_q4_0_packed",
            "gemv_nvfp4_w4a16", "prepack_nvfp4_size", "prepack_nvfp4",
-           "gemv_nvfp4_w4a16_packed", "gemv_fp8_w8a16")
+           "gemv_nvfp4_w4a16_packed", "gemv_fp8_w8a16", "prepack_fp8_size", "prepack_fp8",
+           "gemv_fp8_w8a16_packed")
 
 _lib = None
 
@@ -80,6 +81,12 @@ def lib():
     L.gemv_nvfp4_w4a16_packed.restype = I
     L.gemv_fp8_w8a16.argtypes = [P, P, I, I, P, I, P, P]
     L.gemv_fp8_w8a16.restype = I
+    L.prepack_fp8_size.argtypes = [I, I, ctypes.POINTER(ctypes.c_size_t)]
+    L.prepack_fp8_size.restype = I
+    L.prepack_fp8.argtypes = [P, I, I, P, P]
+    L.prepack_fp8.restype = I
+    L.gemv_fp8_w8a16_packed.argtypes = [P, P, I, I, P, I, P, P]
+    L.gemv_fp8_w8a16_packed.restype = I
     _lib = L
     return L
 
@@ -362,4 +369,42 @@ def gemv_fp8_w8a16(w, channel_scale, x, y=None, stream=None):
     _req(y, "y", _f16_bits_dtypes(), (M, N))
     _run("gemv_fp8_w8a16", (w, channel_scale, x, y), stream, _ptr(w), _ptr(channel_scale), N, K,
          _ptr(x), M, _ptr(y))
+    return y
+
+
+def prepack_fp8_size(N: int, K: int) -> int:
+    """Bytes of the packed copy of an N x K FP8 matrix (K % 256 == 0)."""
+    n = ctypes.c_size_t(0)
+    _check("prepack_fp8_size", lib().prepack_fp8_size(int(N), int(K), ctypes.byref(n)))
+    return n.value
+
+
+def prepack_fp8(w, w_packed=None, stream=None):
+    """E4M3 weights [N][K] -> the packed copy (uint8, prepack_fp8_size(N, K) bytes)."""
+    torch = _torch()
+    _req(w, "w", (torch.uint8, torch.float8_e4m3fn))
+    N, K = w.shape
+    nbytes = prepack_fp8_size(N, K)
+    if w_packed is None:
+        w_packed = torch.empty((nbytes,), dtype=torch.uint8, device=w.device)
+    _req(w_packed, "w_packed", (torch.uint8,), (nbytes,))
+    _run("prepack_fp8", (w, w_packed), stream, _ptr(w), N, K, _ptr(w_packed))
+    return w_packed
+
+
+def gemv_fp8_w8a16_packed(w_packed, N, K, channel_scale, x, y=None, stream=None):
+    """Packed FP8 weights (from prepack_fp8, N x K), float32 channel scales
+    [N], binary16 x [M][K] -> binary16 y [M][N]."""
+    torch = _torch()
+    N, K = int(N), int(K)
+    _req(w_packed, "w_packed", (torch.uint8,), (prepack_fp8_size(N, K),))
+    _req(channel_scale, "channel_scale", (torch.float32,), (N,))
+    _req(x, "x", _f16_bits_dtypes())
+    M = x.shape[0]
+    _req(x, "x", _f16_bits_dtypes(), (M, K))
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    _req(y, "y", _f16_bits_dtypes(), (M, N))
+    _run("gemv_fp8_w8a16_packed", (w_packed, channel_scale, x, y), stream, _ptr(w_packed),
+         _ptr(channel_scale), N, K, _ptr(x), M, _ptr(y))
     return y

@@ -201,4 +201,34 @@ int gemv_fp8_w8a16(const uint8_t *w, const float *channel_scale, int N, int K,
   return launched(skinny::launch_gemv_fp8(w, channel_scale, N, K, x, M, y, (hipStream_t)stream));
 }
 
+int prepack_fp8_size(int N, int K, size_t *bytes) {
+  const int st = shape_status(N, K, 256);
+  if (st) return st;
+  if (!bytes) return SKINNY_ERR_NULL;
+  *bytes = 16 * (((size_t)N + 15) / 16) * (size_t)K;
+  return SKINNY_OK;
+}
+
+int prepack_fp8(const uint8_t *w, int N, int K, uint8_t *w_packed, void *stream) {
+  const int st = shape_status(N, K, 256);
+  if (st) return st;
+  if (N == 0) return SKINNY_OK;
+  if (!w || !w_packed) return SKINNY_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(w_packed, 16)) return SKINNY_ERR_ALIGN;
+  return launched(skinny::launch_prepack_fp8(w, N, K, w_packed, (hipStream_t)stream));
+}
+
+int gemv_fp8_w8a16_packed(const uint8_t *w_packed, const float *channel_scale, int N, int K,
+                          const uint16_t *x, int M, uint16_t *y, void *stream) {
+  int st = gemv_m_status(M, SKINNY_MAX_M_FP8);
+  if (st) return st;
+  if ((st = shape_status(N, K, 256))) return st;
+  if (M == 0 || N == 0) return SKINNY_OK;
+  if (!w_packed || !channel_scale || !x || !y) return SKINNY_ERR_NULL;
+  if (!aligned(w_packed, 16) || !aligned(channel_scale, 4) || !aligned(x, 16) || !aligned(y, 2))
+    return SKINNY_ERR_ALIGN;
+  return launched(skinny::launch_gemv_fp8_packed(w_packed, channel_scale, N, K, x, M, y,
+                                                 (hipStream_t)stream));
+}
+
 }  // extern "C"

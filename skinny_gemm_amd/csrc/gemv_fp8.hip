@@ -17,6 +17,7 @@
 // M = 3 on matrices of at most 4096 rows with K >= 8192 (matrix cores).
 // Bytes per call: N*K + 4*N weights and scales + 2*M*K + 2*M*N.
 #include "device.h"
+#include "fp8.h"
 #include "launch.h"
 
 namespace skinny {
@@ -135,19 +136,6 @@ __global__ __launch_bounds__(256) void gemv_fp8_kernel(
 // distinct banks, and is read back in the operand layout.  Loads are issued
 // in the order they are consumed, so each wait covers exactly one chunk.
 // The KS partial tiles are summed in LDS.
-__device__ __forceinline__ void fp8_decode(const uint4_t (&wq)[2], half8_t (&a)[4]) {
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const uint32_t w0 = wq[u >> 1][2 * (u & 1)];
-    const uint32_t w1 = wq[u >> 1][2 * (u & 1) + 1];
-    const half2_t h0 = e4m3x2_to_h2<false>(w0);
-    const half2_t h1 = e4m3x2_to_h2<true>(w0);
-    const half2_t h2 = e4m3x2_to_h2<false>(w1);
-    const half2_t h3 = e4m3x2_to_h2<true>(w1);
-    a[u] = half8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
-  }
-}
-
 namespace f8 {
 template <int T, int WR, int KS, int S, int MP>
 struct Cfg {

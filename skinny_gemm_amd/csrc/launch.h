@@ -53,6 +53,13 @@ hipError_t launch_prepack_nvfp4(const uint8_t *codes, const uint8_t *scales, int
 hipError_t launch_gemv_nvfp4_packed(const uint8_t *w_packed, float g, int N, int K,
                                     const uint16_t *x, int M, uint16_t *y, hipStream_t stream);
 
+// Pre-permuted FP8 (gemv_fp8_packed.hip).
+hipError_t launch_prepack_fp8(const uint8_t *w, int N, int K, uint8_t *w_packed,
+                              hipStream_t stream);
+
+hipError_t launch_gemv_fp8_packed(const uint8_t *w_packed, const float *cs, int N, int K,
+                                  const uint16_t *x, int M, uint16_t *y, hipStream_t stream);
+
 hipError_t launch_gemv_fp8(const uint8_t *w, const float *cs, int N, int K,
                            const uint16_t *x, int M, uint16_t *y, hipStream_t stream);
 

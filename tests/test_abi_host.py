@@ -36,7 +36,8 @@ def test_header_declares_the_entry_points():
                                            "mmvq_q6_k", "gemv_nvfp4_w4a16", "gemv_fp8_w8a16",
                                            "prepack_nvfp4_size", "prepack_nvfp4",
                                            "gemv_nvfp4_w4a16_packed", "prepack_q4_0_size",
-                                           "prepack_q4_0", "mmvq_q4_0_packed"])
+                                           "prepack_q4_0", "mmvq_q4_0_packed", "prepack_fp8_size",
+                                           "prepack_fp8", "gemv_fp8_w8a16_packed"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -347,3 +348,42 @@ def test_q4_0_packed_validation(L):
     assert q4p(L, w=0, aq=0, ad=0, as_=0, y=0, M=0) == 0
     assert q4p(L, w=0, aq=0, ad=0, as_=0, y=0, N=0) == 0
     assert q4pre(L, w=0, d=0, p=0, N=0) == 0
+
+
+def f8p(L, w=A, cs=A, N=64, K=256, x=A, M=1, y=A):
+    return L.gemv_fp8_w8a16_packed(V(w), V(cs), N, K, V(x), M, V(y), None)
+
+
+def f8pre(L, w=A, N=64, K=256, p=A):
+    return L.prepack_fp8(V(w), N, K, V(p), None)
+
+
+def test_fp8_packed_validation(L):
+    import skinny_gemm_amd
+
+    n = ctypes.c_size_t(0)
+    for N, K, want in ((1, 256, 16 * 256), (17, 512, 32 * 512), (0, 256, 0)):
+        assert L.prepack_fp8_size(N, K, ctypes.byref(n)) == 0
+        assert n.value == want
+        assert skinny_gemm_amd.prepack_fp8_size(N, K) == want
+    assert L.prepack_fp8_size(16, 128, ctypes.byref(n)) == -2
+    assert L.prepack_fp8_size(16, 256, None) == -1
+    assert f8p(L, M=97) == -4
+    assert f8p(L, M=-1) == -4
+    assert f8p(L, M=96, y=0) == -1
+    for K in (0, 128, 16, 384, (1 << 20) + 256):
+        assert f8p(L, K=K) == -2, K
+        assert f8pre(L, K=K) == -2, K
+    assert f8p(L, N=-1) == -2
+    for kw in ("w", "cs", "x", "y"):
+        assert f8p(L, **{kw: 0}) == -1, kw
+    for kw in ("w", "p"):
+        assert f8pre(L, **{kw: 0}) == -1, kw
+    for kw, off in (("w", 8), ("cs", 2), ("x", 8), ("y", 1)):
+        assert f8p(L, **{kw: A + off}) == -3, kw
+    for kw, off in (("w", 8), ("p", 8)):
+        assert f8pre(L, **{kw: A + off}) == -3, kw
+    assert f8p(L, cs=A + 4, y=A + 2, w=0) == -1
+    assert f8p(L, w=0, cs=0, x=0, y=0, M=0) == 0
+    assert f8p(L, w=0, cs=0, x=0, y=0, N=0) == 0
+    assert f8pre(L, w=0, p=0, N=0) == 0

@@ -1009,6 +1009,108 @@ def test_gemv_fp8_sixteen_rows_bit_exact():
     assert np.count_nonzero(f16(want)) > 200
 
 
+# ------------------------------------------------------------------ FP8, pre-permuted
+
+def run_fp8_packed(w, cs, x):
+    import skinny_gemm_amd as sk
+
+    N, K = w.shape
+    wp = sk.prepack_fp8(dev(w))
+    return host(sk.gemv_fp8_w8a16_packed(wp, N, K, dev(cs), dev(x)), np.uint16)
+
+
+def fp8_packed_layout_source(N, K):
+    """From the layout the header defines: for every packed byte the flat
+    index n * K + k of the weight byte it holds (-1 where zero)."""
+    U, S = (N + 15) // 16, K // 128
+    src = np.full(2048 * U * S, -1, np.int64)
+    for u in range(U):
+        for l in range(64):
+            i, g = l % 16, l // 16
+            n = 16 * u + i
+            if n >= N:
+                continue
+            for s in range(S):
+                for e in range(2):
+                    at = 2048 * (u * S + s) + 1024 * e + 16 * l
+                    src[at:at + 16] = n * K + 128 * s + 32 * g + 16 * e + np.arange(16)
+    return src
+
+
+@pytest.mark.parametrize("N,K", [(40, 768), (16, 256), (3, 512)])
+def test_prepack_fp8_layout(N, K):
+    # every weight byte gets a distinct 16-bit label (index + 1) sent as two
+    # byte planes; each must land where the layout puts it, 0 in the padding
+    import skinny_gemm_amd as sk
+
+    label = np.arange(1, N * K + 1, dtype=np.int64)
+    assert label[-1] < 1 << 16
+    got = np.zeros(sk.prepack_fp8_size(N, K), np.int64)
+    for shift in (0, 8):
+        w = ((label >> shift) & 255).astype(np.uint8).reshape(N, K)
+        got |= host(sk.prepack_fp8(dev(w))).astype(np.int64) << shift
+    assert np.array_equal(got - 1, fp8_packed_layout_source(N, K))
+
+
+# (N, K) of the packed FP8 parity test: every row of the packed dispatch
+# tables at M <= 2, M = 3..4 and M = 5..16 (tiles >= 1536, 1100..1535,
+# 600..1099, 512..599, 257..511 with K >= 8192 or shorter, <= 256), with
+# chunks of 4 steps (K % 512 == 0) and of 2, ragged last tiles and unequal K
+# slices; the one row these sizes cannot reach at oracle cost (>= 1536 tiles
+# with K >= 8192 at M > 8) is in the sampled full-size test
+F8P_SHAPES = [(25000, 768), (25000, 1024), (20000, 768), (20000, 1024), (16000, 1280),
+              (16000, 1024), (9000, 1280), (9000, 2048), (5000, 8192), (5000, 8448),
+              (5000, 1280), (2000, 4096), (2000, 11008), (129, 17408), (40, 768), (1, 256)]
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 9, 12, 16])
+@pytest.mark.parametrize("N,K", F8P_SHAPES)
+def test_gemv_fp8_packed_vs_oracle(M, N, K):
+    w, cs = inputs.fp8_weights(N, K, 17 * N + K)
+    x = inputs.normal_f16_bits(M, K, 5 * M + K)
+    y = run_fp8_packed(w, cs, x)
+    y_acc, _ = oracle.gemv_fp8_w8a16(w, cs, x)
+    check_f16(y, y_acc, fp8_mag(w, cs, x), K, "fp8 packed M=%d N=%d K=%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M", [17, 31, 48, 64, 80, 96])
+@pytest.mark.parametrize("N,K", [(24576 + 40, 256),   # wide: one pass, MP / 16 column tiles
+                                 (24576 + 40, 768),
+                                 (9000, 1280),        # narrower: groups of 16 rows, two
+                                 (3000, 1280),        # tiles per wave and four waves sharing
+                                 (600, 17408),        # (below 512 tiles up to M = 48: one
+                                 (40, 768)])          # tile per wave)
+def test_gemv_fp8_packed_many_rows_vs_oracle(M, N, K):
+    w, cs = inputs.fp8_weights(N, K, 19 * N + K)
+    x = inputs.normal_f16_bits(M, K, 8 * M + K)
+    y = run_fp8_packed(w, cs, x)
+    y_acc, _ = oracle.gemv_fp8_w8a16(w, cs, x)
+    check_f16(y, y_acc, fp8_mag(w, cs, x), K, "fp8 packed M=%d N=%d K=%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 256, 256), (2, 256, 256), (4, 256, 256), (8, 256, 256),
+                                   (16, 256, 256), (96, 256, 256), (96, 24576 + 256, 256)])
+def test_gemv_fp8_packed_one_term_bit_exact(M, N, K):
+    # row n holds code n % 256 at element n % 256 (NaN codes replaced by 1.0);
+    # x row m is 1 at the elements k with k % M' == m (M' = 16, or 96 for
+    # M = 96), so each output has at most one exact term: pins the packed
+    # order and the mapping of every activation row
+    w = np.zeros((N, K), np.uint8)
+    codes = np.arange(256)
+    codes[[0x7F, 0xFF]] = 0x38
+    w[np.arange(N), np.arange(N) % 256] = codes[np.arange(N) % 256]
+    cs = np.ones(N, np.float32)
+    period = 96 if M == 96 else 16
+    x = np.zeros((M, K), np.float16)
+    for m in range(M):
+        x[m, m::period] = 1.0
+    xb = x.view(np.uint16)
+    y = run_fp8_packed(w, cs, xb)
+    _, want = oracle.gemv_fp8_w8a16(w, cs, xb)
+    assert np.array_equal(y, want)
+    assert np.count_nonzero(f16(want)) >= 12 * min(M, 16)
+
+
 @pytest.mark.parametrize("fmt,M,K", [
     # activations staged in LDS up to M K = 80 K elements: at the limit the
     # staging takes several batches per thread; just past it, the plain kernel
@@ -1184,6 +1286,23 @@ def test_nvfp4_packed_full_sizes_sampled(M):
         y_acc, _ = oracle.gemv_nvfp4_w4a16(codes[rows], scales[rows], g, x)
         check_f16(y[:, rows], y_acc, nvfp4_mag(codes[rows], scales[rows], g, x), K,
                   "nvfp4 packed full M=%d %dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M", [1, 4, 8, 16, 32, 96])
+def test_fp8_packed_full_sizes_sampled(M):
+    import skinny_gemm_amd as sk
+
+    # the Qwen-shaped matrices, and a wide one with long rows (>= 1536 tiles,
+    # K >= 8192: its own table row at M = 9..16)
+    for si, (N, K) in enumerate(QWEN_FP + [(24576 + 16, 8192)]):
+        w, cs = inputs.fp8_weights(N, K, inputs.seed(4, si, 0))
+        x = inputs.normal_f16_bits(M, K, inputs.seed(4, si, 2) + M)
+        wp = sk.prepack_fp8(dev(w))
+        y = host(sk.gemv_fp8_w8a16_packed(wp, N, K, dev(cs), dev(x)), np.uint16)
+        rows = sample_rows(N, seed=si)
+        y_acc, _ = oracle.gemv_fp8_w8a16(w[rows], cs[rows], x)
+        check_f16(y[:, rows], y_acc, fp8_mag(w[rows], cs[rows], x), K,
+                  "fp8 packed full M=%d %dx%d" % (M, N, K))
 
 
 @pytest.mark.parametrize("M", [1, 4, 8, 16, 32, 96])
