@@ -66,11 +66,10 @@ struct Cfg {
 };
 }  // namespace nvp
 
-template <int T, int S, int APW>
-struct NvpChunk {
+template <int T, int S>
+struct NvpWeights {
   uint4_t c[T * S];                                         // codes, [tile][step]
   std::conditional_t<S == 4, uint2_t, uint32_t> s[T];       // 2 scale bytes per step
-  uint4_t a[APW];                                           // activation pieces
 };
 
 // (No __restrict__ on the inputs: the issue fences below must be able to
@@ -79,7 +78,7 @@ template <int T, int WR, int KS, int S, int MP>
 __global__ __launch_bounds__(64 * WR * KS) void gemv_nvfp4_packed_kernel(
     const uint8_t *wp, float g, int N, int K, const uint16_t *x, int M, uint16_t *y) {
   using C = nvp::Cfg<T, WR, KS, S, MP>;
-  using R = NvpChunk<T, S, C::kApw>;
+  using R = NvpWeights<T, S>;
   extern __shared__ uint4_t smem4[];
   uint8_t *smem = reinterpret_cast<uint8_t *>(smem4);
   const int lane = threadIdx.x & 63;
@@ -113,7 +112,11 @@ __global__ __launch_bounds__(64 * WR * KS) void gemv_nvfp4_packed_kernel(
     const int j = (lane / C::kRpa) ^ p;
     asrc[a] = x + (size_t)r * K + 8 * j;
   }
-  auto load = [&](int c, R &rg) {
+  // Weights and activations are loaded into separate registers: two weight
+  // sets alternate (one is consumed while the next is in flight), one
+  // activation set suffices (it goes to LDS before the next is loaded).
+  uint4_t av[C::kApw];
+  auto load_w = [&](int c, R &rg) {
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
@@ -128,14 +131,17 @@ __global__ __launch_bounds__(64 * WR * KS) void gemv_nvfp4_packed_kernel(
       if constexpr (S == 4) rg.s[t] = load8(p);
       else rg.s[t] = *reinterpret_cast<const uint32_t *>(p);
     }
-#pragma unroll
-    for (int a = 0; a < C::kApw; ++a) rg.a[a] = load16(asrc[a] + (size_t)c * (128 * S));
-    issue_fence();   // keep each chunk's loads together and ahead of later work
+    issue_fence();   // keep the loads in the order they are waited for
   };
-  auto store_act = [&](const R &rg, uint8_t *ab) {
+  auto load_a = [&](int c) {
+#pragma unroll
+    for (int a = 0; a < C::kApw; ++a) av[a] = load16(asrc[a] + (size_t)c * (128 * S));
+    issue_fence();
+  };
+  auto store_act = [&](uint8_t *ab) {
 #pragma unroll
     for (int a = 0; a < C::kApw; ++a)
-      *reinterpret_cast<uint4_t *>(ab + 1024 * apiece[a] + 16 * lane) = rg.a[a];
+      *reinterpret_cast<uint4_t *>(ab + 1024 * apiece[a] + 16 * lane) = av[a];
   };
 
   float4_t acc[T];
@@ -166,24 +172,26 @@ __global__ __launch_bounds__(64 * WR * KS) void gemv_nvfp4_packed_kernel(
     }
   };
 
-  // One chunk: issue the next chunk's loads (LOAD), stage this chunk's
-  // activations, and consume it from registers.  Waves that share
-  // activations run cps chunks in lockstep (the barrier); chunks past a
-  // slice's end re-read its last chunk and compute nothing.  The last chunk
-  // issues no loads.
+  // One chunk: issue the next chunk's weight loads (LOAD), stage this
+  // chunk's activations and issue the next chunk's, then consume this chunk
+  // from registers.  Waves that share activations run cps chunks in
+  // lockstep (the barrier); chunks past a slice's end re-read its last chunk
+  // and compute nothing.  The last chunk issues no loads.
   const int steps = WR > 1 ? cps : ce - cb;
   const int cl = max(ce - 1, 0);
   auto chunk = [&](int k, R &cur, R &nxt, auto load_next) {
     const int c = cb + k;
-    if constexpr (decltype(load_next)::value) load(min(c + 1, cl), nxt);
+    if constexpr (decltype(load_next)::value) load_w(min(c + 1, cl), nxt);
     uint8_t *ab = abuf + (k & (C::kNab - 1)) * C::kAst;
-    store_act(cur, ab);
+    store_act(ab);
+    if constexpr (decltype(load_next)::value) load_a(min(c + 1, cl));
     if constexpr (WR > 1) wg_barrier();
     if (c < ce) consume(ab, cur);
   };
   if (steps > 0) {
     R ra, rb;
-    load(min(cb, cl), ra);
+    load_w(min(cb, cl), ra);
+    load_a(min(cb, cl));
     int k = 0;
     for (; k + 2 < steps; k += 2) {
       chunk(k, ra, rb, std::true_type{});
