@@ -260,6 +260,39 @@ int mmvq_q4_0_packed(const uint8_t *w_packed, int N, int K, const int8_t *a_qs,
                      const uint16_t *a_d, const uint16_t *a_s, int M, float *y, void *stream);
 
 /*
+ * Q4_K weights pre-permuted into matrix-core operand order: the codes plane
+ * of the Q4_0 layout above (Q4_K codes have the Q4_0 nibble order), then a
+ * header plane of U*(K/256) blocks of 256 bytes, block (u, q) at byte
+ * 1024*U*P + 256*(u*(K/256) + q), whose bytes 16j .. 16j + 15 are
+ * w_hdr[16u + j][16q .. 16q + 15] (the header of super-block q of that row);
+ * bytes for rows >= N are zero.  The calls below give the same product as
+ * mmvq_q4_k from such a copy.
+ */
+
+/* prepack_q4_k_size -- bytes of the packed copy: 1024*U*P + U*K.  Host only.
+ * 0 <= N <= SKINNY_MAX_N; K % 256 == 0 (else SKINNY_ERR_SHAPE). */
+int prepack_q4_k_size(int N, int K, size_t *bytes);
+
+/*
+ * prepack_q4_k -- write the packed copy of planar Q4_K weights.
+ *   w_qs, w_hdr as for mmvq_q4_k (16-byte aligned); w_packed: prepack_q4_k_size
+ *   bytes, 16-byte aligned, caller-owned, not overlapping the inputs.  Every
+ *   byte of it is written.  K % 256 == 0.
+ */
+int prepack_q4_k(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K, uint8_t *w_packed,
+                 void *stream);
+
+/*
+ * mmvq_q4_k_packed -- mmvq_q4_k on the packed copy.
+ *   w_packed from prepack_q4_k for the same N and K, 16-byte aligned;
+ *   a_qs, a_d, a_s, y, M as for mmvq_q4_k (0 <= M <= SKINNY_MAX_M_GEMV).
+ *   Block sums are exact integers; the float result matches the definition
+ *   to float32 summation-order rounding.
+ */
+int mmvq_q4_k_packed(const uint8_t *w_packed, int N, int K, const int8_t *a_qs,
+                     const uint16_t *a_d, const uint16_t *a_s, int M, float *y, void *stream);
+
+/*
  * NVFP4 weights pre-permuted into matrix-core operand order.
  *
  * "v100-skinny README", "How QPN works": the weights are rearranged once, at

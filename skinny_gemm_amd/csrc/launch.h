@@ -38,11 +38,18 @@ hipError_t launch_gemv_nvfp4(const uint8_t *w_codes, const uint8_t *w_scales,
                              float g, int N, int K, const uint16_t *x, int M,
                              uint16_t *y, hipStream_t stream);
 
-// Pre-permuted Q4_0 (mmvq_q4_0_packed.hip).
+// Pre-permuted Q4_0 and Q4_K (mmvq_q4_0_packed.hip).
 hipError_t launch_prepack_q4_0(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                                uint8_t *w_packed, hipStream_t stream);
 
 hipError_t launch_mmvq_q4_0_packed(const uint8_t *w_packed, int N, int K, const int8_t *a_qs,
+                                   const uint16_t *a_d, const uint16_t *a_s, int M, float *y,
+                                   hipStream_t stream);
+
+hipError_t launch_prepack_q4_k(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
+                               uint8_t *w_packed, hipStream_t stream);
+
+hipError_t launch_mmvq_q4_k_packed(const uint8_t *w_packed, int N, int K, const int8_t *a_qs,
                                    const uint16_t *a_d, const uint16_t *a_s, int M, float *y,
                                    hipStream_t stream);
 

@@ -216,18 +216,6 @@ struct Chunk {
 };
 }  // namespace q4
 
-// Q4_K epilogue of one step (KQ): the lane's sub-block scale and min come
-// from its super-block header, acc += d sc d8 isum - dmin m s8, with the
-// staged activation pairs (d8, 8 s8) and dmm8 = dmin m / 8 (exact).
-__device__ __forceinline__ void q4k_mfma_epilogue(const int4_t &isum, float dsc, float dmm8,
-                                                  const float4_t &sa, const float4_t &sb,
-                                                  float4_t &acc) {
-  acc[0] = fmaf(dsc, sa[0] * (float)isum[0], fmaf(-dmm8, sa[1], acc[0]));
-  acc[1] = fmaf(dsc, sa[2] * (float)isum[1], fmaf(-dmm8, sa[3], acc[1]));
-  acc[2] = fmaf(dsc, sb[0] * (float)isum[2], fmaf(-dmm8, sb[1], acc[2]));
-  acc[3] = fmaf(dsc, sb[2] * (float)isum[3], fmaf(-dmm8, sb[3], acc[3]));
-}
-
 // (No __restrict__ on the inputs: the issue fence below must be able to
 // order their loads.)
 //

@@ -1,6 +1,6 @@
-// mmvq_q4_0_packed.hip -- Q4_0 weights permuted once, when they are loaded,
-// into the matrix cores' operand order, and the MMVQ that streams them
-// (M = 1..8 rows of Q8_1 activations).
+// mmvq_q4_0_packed.hip -- Q4_0 and Q4_K weights permuted once, when they are
+// loaded, into the matrix cores' operand order, and the MMVQ that streams
+// them (M = 1..8 rows of Q8_1 activations).
 //
 // "v100-skinny README", "How QPN works": the weights are rearranged at load
 // time into the order in which the matrix instructions consume them, so the
@@ -30,6 +30,15 @@
 //   Rows at or past N and blocks at or past K / 32 hold zero bytes.
 // Size: 1024 U P + 512 U V bytes: the canonical bytes of 16 U rows, rounded
 // up to whole 512-element scale blocks.
+//
+// Q4_K (KQ) has the same 4-bit codes in the same nibble order, so its codes
+// plane is the same; its headers (16 bytes per row and 256-element
+// super-block: d, dmin, 12 bytes of 6-bit scales and mins) form the second
+// plane, tile-major: U K/256 blocks of 256 bytes, block (u, q) at byte
+// 1024 U P + 256 (u K/256 + q), whose bytes 16 j .. 16 j + 15 are the header
+// of super-block q of row 16 u + j, unchanged.  Size 1024 U P + U K bytes.
+// The four lanes of row j read the same 16 bytes; the epilogue takes its
+// sub-block's scale and min from them.
 // Bytes per call: 1024 U P + 512 U V weights + M K (1 + 4 / 32) activations
 // + 4 M N out.
 #include <type_traits>
@@ -72,21 +81,22 @@ struct Cfg {
 };
 }  // namespace q4p
 
-template <int T, int S, int APW>
+template <int T, int S, int APW, bool KQ>
 struct Q4pChunk {
   uint4_t c[T][S / 2];                                      // codes, two steps per load
-  std::conditional_t<S == 8, uint4_t, uint2_t> s[T];        // 2 scale bytes per step
+  std::conditional_t<S == 8, uint4_t, uint2_t> s[T];        // Q4_0: 2 scale bytes per step
+  uint4_t h[KQ ? T : 1][KQ ? S / 4 : 1];                    // Q4_K: a header per 4 steps
   uint4_t a[APW];                                           // activation pieces
 };
 
 // (No __restrict__ on the inputs: the issue fences below must be able to
 // order their loads.)
-template <int T, int WR, int KS, int S, int MP>
+template <int T, int WR, int KS, int S, int MP, bool KQ = false>
 __global__ __launch_bounds__(64 * WR * KS) void mmvq_q4_0_packed_kernel(
     const uint8_t *wp, int N, int K, const int8_t *a_qs, const uint16_t *a_d,
     const uint16_t *a_s, int M, float *y) {
   using C = q4p::Cfg<T, WR, KS, S, MP>;
-  using R = Q4pChunk<T, S, C::kApw>;
+  using R = Q4pChunk<T, S, C::kApw, KQ>;
   extern __shared__ uint4_t smem4[];
   uint8_t *smem = reinterpret_cast<uint8_t *>(smem4);
   const int lane = threadIdx.x & 63;
@@ -109,7 +119,8 @@ __global__ __launch_bounds__(64 * WR * KS) void mmvq_q4_0_packed_kernel(
   for (int t = 0; t < T; ++t) {
     const size_t u = (size_t)min(u0 + t, U - 1);
     cp[t] = wp + u * P * 1024 + 16 * lane;
-    sp[t] = wp + (size_t)U * P * 1024 + u * V * 512 + 256 * hb + 16 * j;
+    if constexpr (KQ) sp[t] = wp + (size_t)U * P * 1024 + u * (size_t)(K >> 8) * 256 + 16 * j;
+    else sp[t] = wp + (size_t)U * P * 1024 + u * V * 512 + 256 * hb + 16 * j;
   }
   // activation pieces of this wave: p = wr, wr + WR, ... (the last repeated);
   // pieces 0 .. kAi-1 are code blocks, piece kAi the scales (lanes [0, kNd)
@@ -144,9 +155,14 @@ __global__ __launch_bounds__(64 * WR * KS) void mmvq_q4_0_packed_kernel(
     const int s0 = c * S;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      const uint8_t *p = sp[t] + (size_t)(s0 >> 3) * 512 + 2 * (s0 & 7);
-      if constexpr (S == 8) rg.s[t] = load16(p);
-      else rg.s[t] = load8(p);
+      if constexpr (KQ) {
+#pragma unroll
+        for (int q = 0; q < S / 4; ++q) rg.h[t][q] = load16(sp[t] + (size_t)(c * (S / 4) + q) * 256);
+      } else {
+        const uint8_t *p = sp[t] + (size_t)(s0 >> 3) * 512 + 2 * (s0 & 7);
+        if constexpr (S == 8) rg.s[t] = load16(p);
+        else rg.s[t] = load8(p);
+      }
     }
 #pragma unroll
     for (int a = 0; a < C::kApw; ++a)
@@ -209,8 +225,20 @@ __global__ __launch_bounds__(64 * WR * KS) void mmvq_q4_0_packed_kernel(
       const float4_t sa = asf[0], sb = asf[1];
 #pragma unroll
       for (int t = 0; t < T; ++t) {
-        const uint32_t dw = rg.s[t][st >> 1] >> (16 * (st & 1));
-        q4_mfma_epilogue(isum[st][t], f16_bits_to_f32((uint16_t)dw), sa, sb, acc[t]);
+        if constexpr (KQ) {
+          // sub-block sj = 2 (st % 4) + hb of the step's super-block: scale
+          // byte 4 + sj, min high bits in nibble hb of byte 12 + st % 4
+          const uint4_t &h = rg.h[t][st >> 2];
+          const uint32_t pb = (h[1 + ((st & 3) >> 1)] >> (8 * (2 * (st & 1) + hb))) & 255u;
+          const uint32_t ph = (h[3] >> (8 * (st & 3) + 4 * hb)) & 15u;
+          const float dsc = f16_bits_to_f32((uint16_t)(h[0] & 0xFFFFu)) * (float)(pb & 63u);
+          const float dmm8 = f16_bits_to_f32((uint16_t)(h[0] >> 16)) *
+                             (float)((pb >> 6) | (ph << 2)) * 0.125f;
+          q4k_mfma_epilogue(isum[st][t], dsc, dmm8, sa, sb, acc[t]);
+        } else {
+          const uint32_t dw = rg.s[t][st >> 1] >> (16 * (st & 1));
+          q4_mfma_epilogue(isum[st][t], f16_bits_to_f32((uint16_t)dw), sa, sb, acc[t]);
+        }
       }
     }
   };
@@ -278,18 +306,18 @@ __global__ __launch_bounds__(64 * WR * KS) void mmvq_q4_0_packed_kernel(
   }
 }
 
-template <int T, int WR, int KS, int S, int MP>
+template <int T, int WR, int KS, int S, int MP, bool KQ = false>
 static hipError_t launch_q4p_cfg(const uint8_t *wp, int N, int K, const int8_t *a_qs,
                                  const uint16_t *a_d, const uint16_t *a_s, int M, float *y,
                                  hipStream_t stream) {
   using C = q4p::Cfg<T, WR, KS, S, MP>;
   if (K % (64 * S) != 0) return hipErrorInvalidValue;   // chunks must tile K
   const hipError_t lds_ok =
-      allow_lds((const void *)mmvq_q4_0_packed_kernel<T, WR, KS, S, MP>, C::kLds);
+      allow_lds((const void *)mmvq_q4_0_packed_kernel<T, WR, KS, S, MP, KQ>, C::kLds);
   if (lds_ok != hipSuccess) return lds_ok;
   const int tiles = (N + 15) / 16;
   const int blocks = (tiles + T * WR - 1) / (T * WR);
-  hipLaunchKernelGGL((mmvq_q4_0_packed_kernel<T, WR, KS, S, MP>), dim3(blocks),
+  hipLaunchKernelGGL((mmvq_q4_0_packed_kernel<T, WR, KS, S, MP, KQ>), dim3(blocks),
                      dim3(64 * C::kWaves), C::kLds, stream, wp, N, K, a_qs, a_d, a_s, M, y);
   return hipGetLastError();
 }
@@ -303,14 +331,24 @@ static hipError_t launch_q4p_cfg(const uint8_t *wp, int N, int K, const int8_t *
 // K split of 2 (with sharing at M >= 5); narrower ones a split of 4 (two
 // tiles per wave at M >= 5, and at M = 3, 4 on rows of 8192 or more); up to
 // 256 tiles a split of 8.
-template <int MP>
+template <int MP, bool KQ>
 static hipError_t launch_q4p_mp(const uint8_t *wp, int N, int K, const int8_t *a_qs,
                                 const uint16_t *a_d, const uint16_t *a_s, int M, float *y,
                                 hipStream_t stream) {
   const int tiles = (N + 15) / 16;
   const bool s8 = K % 512 == 0;
 #define SKINNY_Q4P(T, WR, KS, S) \
-  return launch_q4p_cfg<T, WR, KS, S, MP>(wp, N, K, a_qs, a_d, a_s, M, y, stream)
+  return launch_q4p_cfg<T, WR, KS, S, MP, KQ>(wp, N, K, a_qs, a_d, a_s, M, y, stream)
+  if constexpr (KQ) {
+    // Q4_K: its per-step header decode makes chunks of 4 steps pay at every
+    // width (measured on the Qwen3-8B projections and six more matrices at
+    // M = 1, 4, 5, 8: 4096 x 24576 at M = 8 15.2 -> 14.1 us against the
+    // Q4_0 rows, 4096 x 16384 11.7 -> 10.7 us)
+    if (tiles >= 1100) SKINNY_Q4P(1, 2, 2, 4);
+    if (tiles >= 800) SKINNY_Q4P(1, 2, 4, 4);
+    if (tiles > 256) SKINNY_Q4P(1, 1, 4, 4);
+    SKINNY_Q4P(1, 1, 8, 4);
+  }
   if (tiles >= 1100) {
     if (s8 && MP >= 4) SKINNY_Q4P(1, 2, 1, 8);
     SKINNY_Q4P(1, 2, 1, 4);
@@ -338,23 +376,33 @@ static hipError_t launch_q4p_mp(const uint8_t *wp, int N, int K, const int8_t *a
 hipError_t launch_mmvq_q4_0_packed(const uint8_t *wp, int N, int K, const int8_t *a_qs,
                                    const uint16_t *a_d, const uint16_t *a_s, int M, float *y,
                                    hipStream_t stream) {
-  if (M <= 1) return launch_q4p_mp<1>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
-  if (M <= 2) return launch_q4p_mp<2>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
-  if (M <= 4) return launch_q4p_mp<4>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
-  return launch_q4p_mp<8>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
+  if (M <= 1) return launch_q4p_mp<1, false>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
+  if (M <= 2) return launch_q4p_mp<2, false>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
+  if (M <= 4) return launch_q4p_mp<4, false>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
+  return launch_q4p_mp<8, false>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
+}
+
+hipError_t launch_mmvq_q4_k_packed(const uint8_t *wp, int N, int K, const int8_t *a_qs,
+                                   const uint16_t *a_d, const uint16_t *a_s, int M, float *y,
+                                   hipStream_t stream) {
+  if (M <= 1) return launch_q4p_mp<1, true>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
+  if (M <= 2) return launch_q4p_mp<2, true>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
+  if (M <= 4) return launch_q4p_mp<4, true>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
+  return launch_q4p_mp<8, true>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
 }
 
 // ------------------------------------------------------------------ prepack
 
 // One thread per 16 packed bytes, grid-stride over both planes: codes
-// pieces first (a lane's two 8-byte halves), then scale pieces (the 16 bytes
-// at 256 h + 16 j of a scale block).
+// pieces first (a lane's two 8-byte halves), then scale pieces (Q4_0: the 16
+// bytes at 256 h + 16 j of a scale block; Q4_K: one row's header).
+template <bool KQ>
 __global__ __launch_bounds__(256) void prepack_q4_0_kernel(
-    const uint8_t *__restrict__ w_qs, const uint16_t *__restrict__ w_d, int N, int K,
+    const uint8_t *__restrict__ w_qs, const uint8_t *__restrict__ scl, int N, int K,
     uint8_t *__restrict__ wp) {
   const size_t U = (size_t)(N + 15) / 16, P = (size_t)K / 128, V = ((size_t)K + 511) / 512;
-  const size_t nb = (size_t)K / 32;
-  const size_t nc = U * P * 64, total = nc + U * V * 32;
+  const size_t nb = (size_t)K / 32, nsb = (size_t)K / 256;
+  const size_t nc = U * P * 64, total = nc + (KQ ? U * nsb * 16 : U * V * 32);
   for (size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
        q += (size_t)gridDim.x * blockDim.x) {
     uint4_t v = uint4_t{0u, 0u, 0u, 0u};
@@ -368,7 +416,12 @@ __global__ __launch_bounds__(256) void prepack_q4_0_kernel(
         const uint2_t e1 = load8(src + 16 * (4 * p + 2 + h));
         v = uint4_t{e0.x, e0.y, e1.x, e1.y};
       }
+    } else if constexpr (KQ) {
+      const size_t r = q - nc, blk = r >> 4, u = blk / nsb, sb = blk - u * nsb;
+      const size_t row = 16 * u + (r & 15);
+      if (row < (size_t)N) v = load16(scl + row * (nsb * 16) + 16 * sb);
     } else {
+      const uint16_t *w_d = reinterpret_cast<const uint16_t *>(scl);
       const size_t r = q - nc, blk = r >> 5, u = blk / V, vb = blk - u * V;
       const int piece = (int)(r & 31), h = piece >> 4, jj = piece & 15;
       const size_t row = 16 * u + jj;
@@ -384,15 +437,26 @@ __global__ __launch_bounds__(256) void prepack_q4_0_kernel(
   }
 }
 
-hipError_t launch_prepack_q4_0(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
-                               uint8_t *wp, hipStream_t stream) {
+template <bool KQ>
+static hipError_t launch_prepack(const uint8_t *w_qs, const uint8_t *scl, int N, int K,
+                                 uint8_t *wp, hipStream_t stream) {
   const size_t U = (size_t)(N + 15) / 16, P = (size_t)K / 128, V = ((size_t)K + 511) / 512;
-  const size_t total = U * P * 64 + U * V * 32;
+  const size_t total = U * P * 64 + (KQ ? U * ((size_t)K / 256) * 16 : U * V * 32);
   size_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(prepack_q4_0_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w_qs,
-                     w_d, N, K, wp);
+  hipLaunchKernelGGL(prepack_q4_0_kernel<KQ>, dim3((unsigned)blocks), dim3(256), 0, stream, w_qs,
+                     scl, N, K, wp);
   return hipGetLastError();
+}
+
+hipError_t launch_prepack_q4_0(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
+                               uint8_t *wp, hipStream_t stream) {
+  return launch_prepack<false>(w_qs, reinterpret_cast<const uint8_t *>(w_d), N, K, wp, stream);
+}
+
+hipError_t launch_prepack_q4_k(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
+                               uint8_t *wp, hipStream_t stream) {
+  return launch_prepack<true>(w_qs, w_hdr, N, K, wp, stream);
 }
 
 }  // namespace skinny

@@ -1,6 +1,6 @@
-// q4_mfma.h -- the Q4_0 matrix-core step shared by the kernels that stream
-// canonical and pre-permuted Q4_0 weights: exact int32 block sums from
-// v_mfma_i32_16x16x64_i8 and the float32 block epilogue.
+// q4_mfma.h -- the Q4_0 / Q4_K matrix-core step shared by the kernels that
+// stream canonical and pre-permuted weights: exact int32 block sums from
+// v_mfma_i32_16x16x64_i8 and the float32 block epilogues.
 #pragma once
 
 #include "device.h"
@@ -30,6 +30,18 @@ __device__ __forceinline__ void q4_mfma_epilogue(const int4_t &isum, float d4,
   acc[1] = fmaf(d4, fmaf(sa[2], (float)isum[1], -sa[3]), acc[1]);
   acc[2] = fmaf(d4, fmaf(sb[0], (float)isum[2], -sb[1]), acc[2]);
   acc[3] = fmaf(d4, fmaf(sb[2], (float)isum[3], -sb[3]), acc[3]);
+}
+
+// Q4_K epilogue of one step (KQ): the lane's sub-block scale and min come
+// from its super-block header, acc += d sc d8 isum - dmin m s8, with the
+// staged activation pairs (d8, 8 s8) and dmm8 = dmin m / 8 (exact).
+__device__ __forceinline__ void q4k_mfma_epilogue(const int4_t &isum, float dsc, float dmm8,
+                                                  const float4_t &sa, const float4_t &sb,
+                                                  float4_t &acc) {
+  acc[0] = fmaf(dsc, sa[0] * (float)isum[0], fmaf(-dmm8, sa[1], acc[0]));
+  acc[1] = fmaf(dsc, sa[2] * (float)isum[1], fmaf(-dmm8, sa[3], acc[1]));
+  acc[2] = fmaf(dsc, sb[0] * (float)isum[2], fmaf(-dmm8, sb[1], acc[2]));
+  acc[3] = fmaf(dsc, sb[2] * (float)isum[3], fmaf(-dmm8, sb[3], acc[3]));
 }
 
 }  // namespace skinny

@@ -37,7 +37,8 @@ def test_header_declares_the_entry_points():
                                            "prepack_nvfp4_size", "prepack_nvfp4",
                                            "gemv_nvfp4_w4a16_packed", "prepack_q4_0_size",
                                            "prepack_q4_0", "mmvq_q4_0_packed", "prepack_fp8_size",
-                                           "prepack_fp8", "gemv_fp8_w8a16_packed"])
+                                           "prepack_fp8", "gemv_fp8_w8a16_packed", "prepack_q4_k_size",
+                                           "prepack_q4_k", "mmvq_q4_k_packed"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -387,3 +388,35 @@ def test_fp8_packed_validation(L):
     assert f8p(L, w=0, cs=0, x=0, y=0, M=0) == 0
     assert f8p(L, w=0, cs=0, x=0, y=0, N=0) == 0
     assert f8pre(L, w=0, p=0, N=0) == 0
+
+
+def q4kp(L, w=A, N=64, K=256, aq=A, ad=A, as_=A, M=1, y=A):
+    return L.mmvq_q4_k_packed(V(w), N, K, V(aq), V(ad), V(as_), M, V(y), None)
+
+
+def test_q4_k_packed_validation(L):
+    import skinny_gemm_amd
+
+    n = ctypes.c_size_t(0)
+    for N, K, want in ((1, 256, 1024 * 2 + 256), (17, 512, 2 * (1024 * 4 + 512)), (0, 256, 0)):
+        assert L.prepack_q4_k_size(N, K, ctypes.byref(n)) == 0
+        assert n.value == want
+        assert skinny_gemm_amd.prepack_q4_k_size(N, K) == want
+    # whole tiles: exactly the canonical bytes (codes + 16-byte headers)
+    assert skinny_gemm_amd.prepack_q4_k_size(4096, 12288) == 4096 * 12288 * 9 // 16
+    assert L.prepack_q4_k_size(16, 128, ctypes.byref(n)) == -2
+    assert L.prepack_q4_k_size(16, 256, None) == -1
+    assert q4kp(L, M=9) == -4
+    assert q4kp(L, M=8, y=0) == -1
+    for K in (0, 128, 384):
+        assert q4kp(L, K=K) == -2, K
+        assert L.prepack_q4_k(V(A), V(A), 64, K, V(A), None) == -2, K
+    for kw in ("w", "aq", "ad", "as_", "y"):
+        assert q4kp(L, **{kw: 0}) == -1, kw
+    assert L.prepack_q4_k(V(0), V(A), 64, 256, V(A), None) == -1
+    assert L.prepack_q4_k(V(A), V(A + 8), 64, 256, V(A), None) == -3
+    assert L.prepack_q4_k(V(A), V(A), 64, 256, V(A + 8), None) == -3
+    for kw, off in (("w", 8), ("aq", 8), ("ad", 8), ("as_", 8), ("y", 2)):
+        assert q4kp(L, **{kw: A + off}) == -3, kw
+    assert q4kp(L, w=0, aq=0, ad=0, as_=0, y=0, M=0) == 0
+    assert L.prepack_q4_k(V(0), V(0), 0, 256, V(0), None) == 0

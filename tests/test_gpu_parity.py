@@ -581,6 +581,75 @@ def test_q4_k_integer_gate_bit_exact(M, N, K, sc_mask):
     assert np.array_equal(y.astype(np.float64), ref), "M=%d N=%d K=%d" % (M, N, K)
 
 
+# ------------------------------------------------------------------ Q4_K, pre-permuted
+
+def run_q4_k_packed(w_qs, w_hdr, a_qs, a_d, a_s):
+    import skinny_gemm_amd as sk
+
+    N, K = w_qs.shape[0], 2 * w_qs.shape[1]
+    wp = sk.prepack_q4_k(dev(w_qs), dev(w_hdr))
+    return host(sk.mmvq_q4_k_packed(wp, N, K, dev(a_qs), dev(a_d), dev(a_s)))
+
+
+@pytest.mark.parametrize("N,K", [(40, 2304), (16, 256), (3, 768)])
+def test_prepack_q4_k_layout(N, K):
+    # code and header bytes carry 16-bit labels (index + 1) sent as two byte
+    # planes: codes as in the Q4_0 layout, each row's 16-byte headers in
+    # tile-major blocks of 256 bytes, zeros in the padding
+    import skinny_gemm_amd as sk
+
+    nc, nh = N * K // 2, N * K // 16
+    label = np.arange(1, nc + nh + 1, dtype=np.int64)
+    assert label[-1] < 1 << 16
+    U, P, SB = (N + 15) // 16, K // 128, K // 256
+    got = np.zeros(sk.prepack_q4_k_size(N, K), np.int64)
+    for shift in (0, 8):
+        plane = ((label >> shift) & 255).astype(np.uint8)
+        w_qs = plane[:nc].reshape(N, K // 2)
+        w_hdr = plane[nc:].reshape(N, SB, 16)
+        got |= host(sk.prepack_q4_k(dev(w_qs), dev(w_hdr))).astype(np.int64) << shift
+    want_codes, _ = q4_packed_layout_source(N, K)
+    assert np.array_equal(got[:1024 * U * P] - 1, want_codes)
+    hdr = np.full(256 * U * SB, -1, np.int64)
+    for u in range(U):
+        for q in range(SB):
+            for j in range(16):
+                n = 16 * u + j
+                if n < N:
+                    at = 256 * (u * SB + q) + 16 * j
+                    hdr[at:at + 16] = nc + n * (K // 16) + 16 * q + np.arange(16)
+    assert np.array_equal(got[1024 * U * P:] - 1, hdr)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("N,K", Q4P_SHAPES)
+def test_mmvq_q4_k_packed_vs_oracle(M, N, K):
+    w_qs, w_hdr = inputs.q4_k_weights(N, K, 9 * N + K)
+    x = inputs.normal_f32(M, K, 11 * M + K)
+    a_qs, a_d, a_s = oracle.quantize_q8_1(x)
+    y = run_q4_k_packed(w_qs, w_hdr, a_qs, a_d, a_s)
+    ref = oracle.mmvq_q4_k(w_qs, w_hdr, a_qs, a_d, a_s)
+    check_f32(y, ref, q4_k_mag(w_qs, w_hdr, a_qs, a_d, a_s), K,
+              "q4_k packed M=%d N=%d K=%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M", [1, 3, 5, 8])
+@pytest.mark.parametrize("N,K,sc_mask", [(30000, 1024, 7), (25000, 768, 7), (16393, 4096, 7),
+                                         (16000, 1280, 7), (9000, 1280, 7), (5000, 8192, 3),
+                                         (3000, 4096, 7), (5000, 1280, 7), (40, 768, 7)])
+def test_mmvq_q4_k_packed_integer_gate_bit_exact(M, N, K, sc_mask):
+    # unit d and dmin, small scales and mins, integer activations, as for the
+    # canonical layout: exact in any summation order
+    x = inputs.q8_1_unit_scale_source(M, K, 170 + M + K)
+    a_qs, a_d, a_s = oracle.quantize_q8_1(x)
+    w_qs, w_hdr = _q4_k_gate_weights(N, K, 171 + N, sc_mask)
+    assert _q4_k_gate_bound(w_qs, w_hdr, a_qs, a_s) < 2 ** 24
+    y = run_q4_k_packed(w_qs, w_hdr, a_qs, a_d, a_s)
+    ref = oracle.mmvq_q4_k(w_qs, w_hdr, a_qs, a_d, a_s)
+    assert np.array_equal(ref, np.round(ref))
+    assert np.array_equal(y.astype(np.float64), ref), "M=%d N=%d K=%d" % (M, N, K)
+
+
 @pytest.mark.parametrize("M,N,K,sc_max", [
     (1, 300, 4096, 2), (4, 300, 4096, 2), (8, 300, 4096, 2),
     (1, 1031, 13824, 1), (2, 300, 13824, 1),    # vector kernel, eight blocks per lane
@@ -1246,6 +1315,22 @@ def test_q4_0_packed_full_sizes_sampled(M):
         ref = oracle.mmvq_q4_0(w_qs[rows], w_d[rows], a_qs, a_d, a_s)
         mag = q4_mag(w_qs[rows], w_d[rows], a_qs, a_d, a_s)
         check_f32(y[:, rows], ref, mag, K, "q4_0 packed full M=%d %dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_q4_k_packed_full_sizes_sampled(M):
+    import skinny_gemm_amd as sk
+
+    for si, (N, K) in enumerate([(6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288)]):
+        w_qs, w_hdr = inputs.q4_k_weights(N, K, inputs.seed(5, si, 0))
+        x = inputs.normal_f32(M, K, inputs.seed(5, si, 2) + M)
+        a_qs, a_d, a_s = oracle.quantize_q8_1(x)
+        wp = sk.prepack_q4_k(dev(w_qs), dev(w_hdr))
+        y = host(sk.mmvq_q4_k_packed(wp, N, K, dev(a_qs), dev(a_d), dev(a_s)))
+        rows = sample_rows(N, seed=si)
+        ref = oracle.mmvq_q4_k(w_qs[rows], w_hdr[rows], a_qs, a_d, a_s)
+        mag = q4_k_mag(w_qs[rows], w_hdr[rows], a_qs, a_d, a_s)
+        check_f32(y[:, rows], ref, mag, K, "q4_k packed full M=%d %dx%d" % (M, N, K))
 
 
 @pytest.mark.parametrize("M", [1, 2])
