@@ -1507,6 +1507,9 @@ def test_graph_replays_match_eager():
     xf = {M: inputs.normal_f32_torch(M, K, 30 + M, d) for M in (1, 2, 8)}
     xh = {M: inputs.normal_f16_torch(M, K, 40 + M, d) for M in (1, 2, 4, 8, 32)}
     q8 = {M: sk.quantize_act_q8_1(xf[M]) for M in (1, 2, 8)}
+    # pre-permuted copies (prepacked outside the graph, as at load time)
+    p_q4, p_q4k = sk.prepack_q4_0(w_qs, w_d), sk.prepack_q4_k(k_qs, k_hdr)
+    p_nv, p_f8 = sk.prepack_nvfp4(codes, scales), sk.prepack_fp8(w8)
     outs = []
 
     def run():
@@ -1523,6 +1526,13 @@ def test_graph_replays_match_eager():
         outs.append(sk.gemv_nvfp4_w4a16(fc, fs, 1.0, fx))
         for M in (1, 2, 4, 8, 32):
             outs.append(sk.gemv_fp8_w8a16(w8, cs, xh[M]))
+        for M in (1, 2, 8):
+            outs.append(sk.mmvq_q4_0_packed(p_q4, N, K, *q8[M]))
+            outs.append(sk.mmvq_q4_k_packed(p_q4k, N, K, *q8[M]))
+        for M in (1, 2, 4, 8):
+            outs.append(sk.gemv_nvfp4_w4a16_packed(p_nv, N, K, 1.0, xh[M]))
+        for M in (1, 2, 4, 8, 32):
+            outs.append(sk.gemv_fp8_w8a16_packed(p_f8, N, K, cs, xh[M]))
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -1563,6 +1573,35 @@ def test_largest_k_small_n():
     y = run_q4(w_qs, w_d, a_qs, a_d, a_s)
     ref = oracle.mmvq_q4_0(w_qs, w_d, a_qs, a_d, a_s)
     check_f32(y, ref, q4_mag(w_qs, w_d, a_qs, a_d, a_s), K, "q4_0 max K")
+
+
+def test_largest_k_packed():
+    # K at the documented maximum through every pre-permuted entry point:
+    # long K slices, the last tile ragged (N = 17)
+    import skinny_gemm_amd as sk
+
+    N, K = 17, 1 << 20
+    w_qs, w_d = inputs.q4_0_weights(N, K, 12)
+    k_qs, k_hdr = inputs.q4_k_weights(N, K, 13)
+    for M in (1, 8):
+        xf = inputs.normal_f32(M, K, 14 + M)
+        a_qs, a_d, a_s = oracle.quantize_q8_1(xf)
+        y = run_q4_packed(w_qs, w_d, a_qs, a_d, a_s)
+        check_f32(y, oracle.mmvq_q4_0(w_qs, w_d, a_qs, a_d, a_s),
+                  q4_mag(w_qs, w_d, a_qs, a_d, a_s), K, "q4_0 packed max K M=%d" % M)
+        y = run_q4_k_packed(k_qs, k_hdr, a_qs, a_d, a_s)
+        check_f32(y, oracle.mmvq_q4_k(k_qs, k_hdr, a_qs, a_d, a_s),
+                  q4_k_mag(k_qs, k_hdr, a_qs, a_d, a_s), K, "q4_k packed max K M=%d" % M)
+    codes, scales, g = inputs.nvfp4_weights(N, K, 15)
+    w8, cs = inputs.fp8_weights(N, K, 16)
+    for M in (1, 8, 16):
+        x = inputs.normal_f16_bits(M, K, 17 + M, std=0.1)
+        y = run_nvfp4_packed(codes, scales, g, x)
+        y_acc, _ = oracle.gemv_nvfp4_w4a16(codes, scales, g, x)
+        check_f16(y, y_acc, nvfp4_mag(codes, scales, g, x), K, "nvfp4 packed max K M=%d" % M)
+        y = run_fp8_packed(w8, cs, x)
+        y_acc, _ = oracle.gemv_fp8_w8a16(w8, cs, x)
+        check_f16(y, y_acc, fp8_mag(w8, cs, x), K, "fp8 packed max K M=%d" % M)
 
 
 def test_empty_and_invalid_calls_on_device():
