@@ -293,6 +293,50 @@ int mmvq_q4_k_packed(const uint8_t *w_packed, int N, int K, const int8_t *a_qs,
                      const uint16_t *a_d, const uint16_t *a_s, int M, float *y, void *stream);
 
 /*
+ * Q6_K weights pre-permuted into matrix-core operand order.
+ *
+ * The matrix cores take one 16-element sub-block per K slot (lane
+ * l = 16 g + j, g < 4: sub-block g of each 64-element step, row j of a
+ * 16-row tile).  Packed layout (K % 256 == 0; U = ceil(N/16), P = K/128,
+ * Q = K/256), four planes:
+ *   L: U*P blocks of 1024 bytes, block (u, p) at byte 1024*(u*P + p); byte
+ *      16l + 8e + c (e < 2, c < 8) = low(c) | low(8 + c) << 4, low(x) = the
+ *      low 4 bits of element x of sub-block g of step 2p + e of row 16u + j;
+ *   H: from 1024*U*P, U*Q blocks of 1024 bytes, block (u, q); bytes
+ *      16l + 4t .. + 3 (t < 4) = w_qh[16u + j][8b + 4h .. + 3] with
+ *      b = 2*(4q + t) + g/2, h = g % 2 (the high bits of that sub-block);
+ *   C: from 1024*U*(P + Q), U*Q blocks of 256 bytes, block (u, q); byte
+ *      4l + t = w_sc[16u + j][16q + 4t + g];
+ *   D: from 1024*U*(P + Q) + 256*U*Q, U*Q blocks of 32 bytes, block (u, q);
+ *      bytes 2j, 2j + 1 = w_d[16u + j][q];
+ *   bytes for rows >= N are zero.
+ */
+
+/* prepack_q6_k_size -- bytes of the packed copy: 1024*U*P + 1312*U*Q.  Host
+ * only.  0 <= N <= SKINNY_MAX_N; K % 256 == 0 (else SKINNY_ERR_SHAPE). */
+int prepack_q6_k_size(int N, int K, size_t *bytes);
+
+/*
+ * prepack_q6_k -- write the packed copy of planar Q6_K weights.
+ *   w_ql, w_qh, w_sc, w_d as for mmvq_q6_k (w_ql 16-byte, w_qh 8-byte, w_sc
+ *   and w_d 2-byte aligned); w_packed: prepack_q6_k_size bytes, 16-byte
+ *   aligned, caller-owned, not overlapping the inputs.  Every byte of it is
+ *   written.  K % 256 == 0.
+ */
+int prepack_q6_k(const uint8_t *w_ql, const uint8_t *w_qh, const int8_t *w_sc,
+                 const uint16_t *w_d, int N, int K, uint8_t *w_packed, void *stream);
+
+/*
+ * mmvq_q6_k_packed -- mmvq_q6_k on the packed copy (matrix cores at every M).
+ *   w_packed from prepack_q6_k for the same N and K, 16-byte aligned;
+ *   a_qs, a_d (16-byte aligned), y, M as for mmvq_q6_k
+ *   (0 <= M <= SKINNY_MAX_M_GEMV).  Sub-block sums are exact integers; the
+ *   float result matches the definition to float32 summation-order rounding.
+ */
+int mmvq_q6_k_packed(const uint8_t *w_packed, int N, int K, const int8_t *a_qs,
+                     const uint16_t *a_d, int M, float *y, void *stream);
+
+/*
  * NVFP4 weights pre-permuted into matrix-core operand order.
  *
  * "v100-skinny README", "How QPN works": the weights are rearranged once, at

@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     mmvq_q4_k,
     mmvq_q4_k_packed,
     mmvq_q6_k,
+    mmvq_q6_k_packed,
     prepack_fp8,
     prepack_fp8_size,
     prepack_nvfp4,
@@ -29,6 +30,8 @@ from ._lib import (  # noqa: F401
     prepack_q4_0_size,
     prepack_q4_k,
     prepack_q4_k_size,
+    prepack_q6_k,
+    prepack_q6_k_size,
     prepack_nvfp4_size,
     quantize_act_q8_1,
     status_string,

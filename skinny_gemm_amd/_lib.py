@@ -27,7 +27,8 @@ EXPORTS = ("skinny_status_string", "quantize_act_q8_1", "mmvq_q4_0", "mmvq_q4_0_
            "mmvq_q4_k", "mmvq_q6_k", "prepack_q4_0_size", "prepack_q4_0", "mmvq_q4_0_packed",
            "gemv_nvfp4_w4a16", "prepack_nvfp4_size", "prepack_nvfp4",
            "gemv_nvfp4_w4a16_packed", "gemv_fp8_w8a16", "prepack_fp8_size", "prepack_fp8",
-           "gemv_fp8_w8a16_packed", "prepack_q4_k_size", "prepack_q4_k", "mmvq_q4_k_packed")
+           "gemv_fp8_w8a16_packed", "prepack_q4_k_size", "prepack_q4_k", "mmvq_q4_k_packed",
+           "prepack_q6_k_size", "prepack_q6_k", "mmvq_q6_k_packed")
 
 _lib = None
 
@@ -79,6 +80,12 @@ def lib():
     L.prepack_q4_k.restype = I
     L.mmvq_q4_k_packed.argtypes = [P, I, I, P, P, P, I, P, P]
     L.mmvq_q4_k_packed.restype = I
+    L.prepack_q6_k_size.argtypes = [I, I, ctypes.POINTER(ctypes.c_size_t)]
+    L.prepack_q6_k_size.restype = I
+    L.prepack_q6_k.argtypes = [P, P, P, P, I, I, P, P]
+    L.prepack_q6_k.restype = I
+    L.mmvq_q6_k_packed.argtypes = [P, I, I, P, P, I, P, P]
+    L.mmvq_q6_k_packed.restype = I
     L.prepack_nvfp4_size.argtypes = [I, I, ctypes.POINTER(ctypes.c_size_t)]
     L.prepack_nvfp4_size.restype = I
     L.prepack_nvfp4.argtypes = [P, P, I, I, P, P]
@@ -456,4 +463,48 @@ def mmvq_q4_k_packed(w_packed, N, K, a_qs, a_d, a_s, y=None, stream=None):
     _req(y, "y", (torch.float32,), (M, N))
     _run("mmvq_q4_k_packed", (w_packed, a_qs, a_d, a_s, y), stream, _ptr(w_packed), N, K,
          _ptr(a_qs), _ptr(a_d), _ptr(a_s), M, _ptr(y))
+    return y
+
+
+def prepack_q6_k_size(N: int, K: int) -> int:
+    """Bytes of the packed copy of an N x K Q6_K matrix (K % 256 == 0)."""
+    n = ctypes.c_size_t(0)
+    _check("prepack_q6_k_size", lib().prepack_q6_k_size(int(N), int(K), ctypes.byref(n)))
+    return n.value
+
+
+def prepack_q6_k(w_ql, w_qh, w_sc, w_d, w_packed=None, stream=None):
+    """Planar Q6_K weights (ql [N][K/2], qh [N][K/4], sc int8 [N][K/16], d
+    binary16 [N][K/256]) -> the packed copy (uint8, prepack_q6_k_size bytes)."""
+    torch = _torch()
+    _req(w_ql, "w_ql", (torch.uint8,))
+    N, K2 = w_ql.shape
+    K = 2 * K2
+    _req(w_qh, "w_qh", (torch.uint8,), (N, K // 4))
+    _req(w_sc, "w_sc", (torch.int8,), (N, K // 16))
+    _req(w_d, "w_d", _f16_bits_dtypes(), (N, K // 256))
+    nbytes = prepack_q6_k_size(N, K)
+    if w_packed is None:
+        w_packed = torch.empty((nbytes,), dtype=torch.uint8, device=w_ql.device)
+    _req(w_packed, "w_packed", (torch.uint8,), (nbytes,))
+    _run("prepack_q6_k", (w_ql, w_qh, w_sc, w_d, w_packed), stream, _ptr(w_ql), _ptr(w_qh),
+         _ptr(w_sc), _ptr(w_d), N, K, _ptr(w_packed))
+    return w_packed
+
+
+def mmvq_q6_k_packed(w_packed, N, K, a_qs, a_d, y=None, stream=None):
+    """Packed Q6_K weights (from prepack_q6_k, N x K) x Q8_1 activations
+    (codes and d8) -> float32 y [M][N]."""
+    torch = _torch()
+    N, K = int(N), int(K)
+    _req(w_packed, "w_packed", (torch.uint8,), (prepack_q6_k_size(N, K),))
+    _req(a_qs, "a_qs", (torch.int8,))
+    M = a_qs.shape[0]
+    _req(a_qs, "a_qs", (torch.int8,), (M, K))
+    _req(a_d, "a_d", _f16_bits_dtypes(), (M, K // 32))
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=a_qs.device)
+    _req(y, "y", (torch.float32,), (M, N))
+    _run("mmvq_q6_k_packed", (w_packed, a_qs, a_d, y), stream, _ptr(w_packed), N, K,
+         _ptr(a_qs), _ptr(a_d), M, _ptr(y))
     return y

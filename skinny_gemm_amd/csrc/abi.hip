@@ -190,6 +190,41 @@ int mmvq_q4_k_packed(const uint8_t *w_packed, int N, int K, const int8_t *a_qs,
                                                   (hipStream_t)stream));
 }
 
+int prepack_q6_k_size(int N, int K, size_t *bytes) {
+  const int st = shape_status(N, K, 256);
+  if (st) return st;
+  if (!bytes) return SKINNY_ERR_NULL;
+  const size_t U = ((size_t)N + 15) / 16;
+  *bytes = 1024 * U * ((size_t)K / 128) + 1312 * U * ((size_t)K / 256);
+  return SKINNY_OK;
+}
+
+int prepack_q6_k(const uint8_t *w_ql, const uint8_t *w_qh, const int8_t *w_sc,
+                 const uint16_t *w_d, int N, int K, uint8_t *w_packed, void *stream) {
+  const int st = shape_status(N, K, 256);
+  if (st) return st;
+  if (N == 0) return SKINNY_OK;
+  if (!w_ql || !w_qh || !w_sc || !w_d || !w_packed) return SKINNY_ERR_NULL;
+  if (!aligned(w_ql, 16) || !aligned(w_qh, 8) || !aligned(w_sc, 2) || !aligned(w_d, 2) ||
+      !aligned(w_packed, 16))
+    return SKINNY_ERR_ALIGN;
+  return launched(skinny::launch_prepack_q6_k(w_ql, w_qh, w_sc, w_d, N, K, w_packed,
+                                              (hipStream_t)stream));
+}
+
+int mmvq_q6_k_packed(const uint8_t *w_packed, int N, int K, const int8_t *a_qs,
+                     const uint16_t *a_d, int M, float *y, void *stream) {
+  int st = gemv_m_status(M, SKINNY_MAX_M_GEMV);
+  if (st) return st;
+  if ((st = shape_status(N, K, 256))) return st;
+  if (M == 0 || N == 0) return SKINNY_OK;
+  if (!w_packed || !a_qs || !a_d || !y) return SKINNY_ERR_NULL;
+  if (!aligned(w_packed, 16) || !aligned(a_qs, 16) || !aligned(a_d, 16) || !aligned(y, 4))
+    return SKINNY_ERR_ALIGN;
+  return launched(skinny::launch_mmvq_q6_k_packed(w_packed, N, K, a_qs, a_d, M, y,
+                                                  (hipStream_t)stream));
+}
+
 int prepack_nvfp4_size(int N, int K, size_t *bytes) {
   const int st = shape_status(N, K, 256);
   if (st) return st;

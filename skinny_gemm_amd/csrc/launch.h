@@ -53,6 +53,14 @@ hipError_t launch_mmvq_q4_k_packed(const uint8_t *w_packed, int N, int K, const 
                                    const uint16_t *a_d, const uint16_t *a_s, int M, float *y,
                                    hipStream_t stream);
 
+// Pre-permuted Q6_K (mmvq_q6_k_packed.hip).
+hipError_t launch_prepack_q6_k(const uint8_t *ql, const uint8_t *qh, const int8_t *sc,
+                               const uint16_t *d, int N, int K, uint8_t *w_packed,
+                               hipStream_t stream);
+
+hipError_t launch_mmvq_q6_k_packed(const uint8_t *w_packed, int N, int K, const int8_t *a_qs,
+                                   const uint16_t *a_d, int M, float *y, hipStream_t stream);
+
 // Pre-permuted NVFP4 (gemv_nvfp4_packed.hip).
 hipError_t launch_prepack_nvfp4(const uint8_t *codes, const uint8_t *scales, int N, int K,
                                 uint8_t *w_packed, hipStream_t stream);

@@ -38,7 +38,8 @@ def test_header_declares_the_entry_points():
                                            "gemv_nvfp4_w4a16_packed", "prepack_q4_0_size",
                                            "prepack_q4_0", "mmvq_q4_0_packed", "prepack_fp8_size",
                                            "prepack_fp8", "gemv_fp8_w8a16_packed", "prepack_q4_k_size",
-                                           "prepack_q4_k", "mmvq_q4_k_packed"])
+                                           "prepack_q4_k", "mmvq_q4_k_packed", "prepack_q6_k_size",
+                                           "prepack_q6_k", "mmvq_q6_k_packed"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -420,3 +421,39 @@ def test_q4_k_packed_validation(L):
         assert q4kp(L, **{kw: A + off}) == -3, kw
     assert q4kp(L, w=0, aq=0, ad=0, as_=0, y=0, M=0) == 0
     assert L.prepack_q4_k(V(0), V(0), 0, 256, V(0), None) == 0
+
+
+def test_q6_k_packed_validation(L):
+    import skinny_gemm_amd
+
+    n = ctypes.c_size_t(0)
+    for N, K, want in ((1, 256, 1024 * 2 + 1312), (17, 512, 2 * (1024 * 4 + 1312 * 2)), (0, 256, 0)):
+        assert L.prepack_q6_k_size(N, K, ctypes.byref(n)) == 0
+        assert n.value == want
+        assert skinny_gemm_amd.prepack_q6_k_size(N, K) == want
+    # whole tiles: exactly the canonical bytes (6.5625 bits per weight)
+    assert skinny_gemm_amd.prepack_q6_k_size(4096, 12288) == 4096 * 12288 * 105 // 128
+    assert L.prepack_q6_k_size(16, 128, ctypes.byref(n)) == -2
+    assert L.prepack_q6_k_size(16, 256, None) == -1
+
+    def q6p(w=A, N=64, K=256, aq=A, ad=A, M=1, y=A):
+        return L.mmvq_q6_k_packed(V(w), N, K, V(aq), V(ad), M, V(y), None)
+
+    def pre(ql=A, qh=A, sc=A, d=A, N=64, K=256, p=A):
+        return L.prepack_q6_k(V(ql), V(qh), V(sc), V(d), N, K, V(p), None)
+
+    assert q6p(M=9) == -4
+    assert q6p(M=8, y=0) == -1
+    for K in (0, 128, 384):
+        assert q6p(K=K) == -2, K
+        assert pre(K=K) == -2, K
+    for kw in ("w", "aq", "ad", "y"):
+        assert q6p(**{kw: 0}) == -1, kw
+    for kw in ("ql", "qh", "sc", "d", "p"):
+        assert pre(**{kw: 0}) == -1, kw
+    for kw, off in (("w", 8), ("aq", 8), ("ad", 8), ("y", 2)):
+        assert q6p(**{kw: A + off}) == -3, kw
+    for kw, off in (("ql", 8), ("qh", 4), ("sc", 1), ("d", 1), ("p", 8)):
+        assert pre(**{kw: A + off}) == -3, kw
+    assert q6p(w=0, aq=0, ad=0, y=0, M=0) == 0
+    assert pre(ql=0, qh=0, sc=0, d=0, p=0, N=0) == 0

@@ -650,6 +650,95 @@ def test_mmvq_q4_k_packed_integer_gate_bit_exact(M, N, K, sc_mask):
     assert np.array_equal(y.astype(np.float64), ref), "M=%d N=%d K=%d" % (M, N, K)
 
 
+# ------------------------------------------------------------------ Q6_K, pre-permuted
+
+def run_q6_k_packed(w_ql, w_qh, w_sc, w_d, a_qs, a_d):
+    import skinny_gemm_amd as sk
+
+    N, K = w_ql.shape[0], 2 * w_ql.shape[1]
+    wp = sk.prepack_q6_k(dev(w_ql), dev(w_qh), dev(w_sc), dev(w_d))
+    return host(sk.mmvq_q6_k_packed(wp, N, K, dev(a_qs), dev(a_d)))
+
+
+def q6_k_packed_expected(w_ql, w_qh, w_sc, w_d):
+    """The packed bytes the header's layout defines, from the canonical arrays."""
+    N, K = w_ql.shape[0], 2 * w_ql.shape[1]
+    U, P, Q = (N + 15) // 16, K // 128, K // 256
+    out = np.zeros(1024 * U * P + 1312 * U * Q, np.uint8)
+    oH, oC = 1024 * U * P, 1024 * U * (P + Q)
+    oD = oC + 256 * U * Q
+    sc8 = w_sc.view(np.uint8)
+    d8 = w_d.view(np.uint8)
+    for u in range(U):
+        for l in range(64):
+            j, g = l % 16, l // 16
+            n = 16 * u + j
+            if n >= N:
+                continue
+            h = g % 2
+            for p in range(P):
+                for e in range(2):
+                    b = 2 * (2 * p + e) + g // 2
+                    low = (w_ql[n, 16 * b:16 * b + 16] >> (4 * h)) & 15
+                    at = 1024 * (u * P + p) + 16 * l + 8 * e
+                    out[at:at + 8] = low[:8] | (low[8:] << 4)
+            for q in range(Q):
+                for t in range(4):
+                    b = 2 * (4 * q + t) + g // 2
+                    at = oH + 1024 * (u * Q + q) + 16 * l + 4 * t
+                    out[at:at + 4] = w_qh[n, 8 * b + 4 * h:8 * b + 4 * h + 4]
+                    out[oC + 256 * (u * Q + q) + 4 * l + t] = sc8[n, 16 * q + 4 * t + g]
+        for j in range(16):
+            n = 16 * u + j
+            if n < N:
+                for q in range(Q):
+                    at = oD + 32 * (u * Q + q) + 2 * j
+                    out[at:at + 2] = d8[n, 2 * q:2 * q + 2]
+    return out
+
+
+@pytest.mark.parametrize("N,K", [(40, 2304), (16, 256), (3, 768)])
+def test_prepack_q6_k_layout(N, K):
+    # random canonical arrays through prepack_q6_k against the bytes the
+    # header's layout defines (padding rows zero)
+    import skinny_gemm_amd as sk
+
+    w_ql, w_qh, w_sc, w_d = inputs.q6_k_weights(N, K, 5 + N + K)
+    got = host(sk.prepack_q6_k(dev(w_ql), dev(w_qh), dev(w_sc), dev(w_d)))
+    assert np.array_equal(got, q6_k_packed_expected(w_ql, w_qh, w_sc, w_d))
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("N,K", Q4P_SHAPES)
+def test_mmvq_q6_k_packed_vs_oracle(M, N, K):
+    w_ql, w_qh, w_sc, w_d = inputs.q6_k_weights(N, K, 13 * N + K)
+    x = inputs.normal_f32(M, K, 17 * M + K)
+    a_qs, a_d, _ = oracle.quantize_q8_1(x)
+    y = run_q6_k_packed(w_ql, w_qh, w_sc, w_d, a_qs, a_d)
+    ref = oracle.mmvq_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d)
+    check_f32(y, ref, q6_k_mag(w_ql, w_qh, w_sc, w_d, a_qs, a_d), K,
+              "q6_k packed M=%d N=%d K=%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M", [1, 3, 5, 8])
+@pytest.mark.parametrize("N,K,sc_max", [(30000, 1024, 2), (16393, 4096, 2), (16000, 1280, 2),
+                                        (9000, 1280, 2), (5000, 8192, 1), (3000, 4096, 2),
+                                        (40, 768, 2)])
+def test_mmvq_q6_k_packed_integer_gate_bit_exact(M, N, K, sc_max):
+    # unit d, scales in -sc_max..sc_max, integer activations: exact in any
+    # order, so equal to the oracle bit for bit
+    x = inputs.q8_1_unit_scale_source(M, K, 370 + M + K)
+    a_qs, a_d, _ = oracle.quantize_q8_1(x)
+    w_ql, w_qh, w_sc, _ = inputs.q6_k_weights(N, K, 372 + N)
+    w_sc = (w_sc.astype(np.int64) % (2 * sc_max + 1) - sc_max).astype(np.int8)
+    w_d = np.full((N, K // 256), 0x3C00, np.uint16)
+    assert 32 * sc_max * np.abs(a_qs.astype(np.int64)).sum(axis=1).max() < 2 ** 24
+    y = run_q6_k_packed(w_ql, w_qh, w_sc, w_d, a_qs, a_d)
+    ref = oracle.mmvq_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d)
+    assert np.array_equal(ref, np.round(ref))
+    assert np.array_equal(y.astype(np.float64), ref), "M=%d N=%d K=%d" % (M, N, K)
+
+
 @pytest.mark.parametrize("M,N,K,sc_max", [
     (1, 300, 4096, 2), (4, 300, 4096, 2), (8, 300, 4096, 2),
     (1, 1031, 13824, 1), (2, 300, 13824, 1),    # vector kernel, eight blocks per lane
@@ -1333,6 +1422,22 @@ def test_q4_k_packed_full_sizes_sampled(M):
         check_f32(y[:, rows], ref, mag, K, "q4_k packed full M=%d %dx%d" % (M, N, K))
 
 
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_q6_k_packed_full_sizes_sampled(M):
+    import skinny_gemm_amd as sk
+
+    for si, (N, K) in enumerate([(6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288)]):
+        w_ql, w_qh, w_sc, w_d = inputs.q6_k_weights(N, K, inputs.seed(6, si, 0))
+        x = inputs.normal_f32(M, K, inputs.seed(6, si, 2) + M)
+        a_qs, a_d, _ = oracle.quantize_q8_1(x)
+        wp = sk.prepack_q6_k(dev(w_ql), dev(w_qh), dev(w_sc), dev(w_d))
+        y = host(sk.mmvq_q6_k_packed(wp, N, K, dev(a_qs), dev(a_d)))
+        rows = sample_rows(N, seed=si)
+        ref = oracle.mmvq_q6_k(w_ql[rows], w_qh[rows], w_sc[rows], w_d[rows], a_qs, a_d)
+        mag = q6_k_mag(w_ql[rows], w_qh[rows], w_sc[rows], w_d[rows], a_qs, a_d)
+        check_f32(y[:, rows], ref, mag, K, "q6_k packed full M=%d %dx%d" % (M, N, K))
+
+
 @pytest.mark.parametrize("M", [1, 2])
 def test_q4_0_f32act_full_sizes_sampled(M):
     for si, (N, K) in enumerate(LLAMA_Q4):
@@ -1510,6 +1615,7 @@ def test_graph_replays_match_eager():
     # pre-permuted copies (prepacked outside the graph, as at load time)
     p_q4, p_q4k = sk.prepack_q4_0(w_qs, w_d), sk.prepack_q4_k(k_qs, k_hdr)
     p_nv, p_f8 = sk.prepack_nvfp4(codes, scales), sk.prepack_fp8(w8)
+    p_q6k = sk.prepack_q6_k(ql, qh, sc, dd)
     outs = []
 
     def run():
@@ -1529,6 +1635,7 @@ def test_graph_replays_match_eager():
         for M in (1, 2, 8):
             outs.append(sk.mmvq_q4_0_packed(p_q4, N, K, *q8[M]))
             outs.append(sk.mmvq_q4_k_packed(p_q4k, N, K, *q8[M]))
+            outs.append(sk.mmvq_q6_k_packed(p_q6k, N, K, q8[M][0], q8[M][1]))
         for M in (1, 2, 4, 8):
             outs.append(sk.gemv_nvfp4_w4a16_packed(p_nv, N, K, 1.0, xh[M]))
         for M in (1, 2, 4, 8, 32):
@@ -1583,6 +1690,7 @@ def test_largest_k_packed():
     N, K = 17, 1 << 20
     w_qs, w_d = inputs.q4_0_weights(N, K, 12)
     k_qs, k_hdr = inputs.q4_k_weights(N, K, 13)
+    q6 = inputs.q6_k_weights(N, K, 18)
     for M in (1, 8):
         xf = inputs.normal_f32(M, K, 14 + M)
         a_qs, a_d, a_s = oracle.quantize_q8_1(xf)
@@ -1592,6 +1700,9 @@ def test_largest_k_packed():
         y = run_q4_k_packed(k_qs, k_hdr, a_qs, a_d, a_s)
         check_f32(y, oracle.mmvq_q4_k(k_qs, k_hdr, a_qs, a_d, a_s),
                   q4_k_mag(k_qs, k_hdr, a_qs, a_d, a_s), K, "q4_k packed max K M=%d" % M)
+        y = run_q6_k_packed(*q6, a_qs, a_d)
+        check_f32(y, oracle.mmvq_q6_k(*q6, a_qs, a_d), q6_k_mag(*q6, a_qs, a_d), K,
+                  "q6_k packed max K M=%d" % M)
     codes, scales, g = inputs.nvfp4_weights(N, K, 15)
     w8, cs = inputs.fp8_weights(N, K, 16)
     for M in (1, 8, 16):
