@@ -63,6 +63,8 @@ def _load():
     lib.oracle_mmvq_q4_k.restype = None
     lib.oracle_mmvq_q6_k.argtypes = [P, P, P, P, I, I, P, P, I, P]
     lib.oracle_mmvq_q6_k.restype = None
+    lib.oracle_mmvq_iq4_xs.argtypes = [P, P, I, I, P, P, I, P]
+    lib.oracle_mmvq_iq4_xs.restype = None
     lib.oracle_gemv_nvfp4_w4a16.argtypes = [P, P, ctypes.c_float, I, I, P, I, P, P]
     lib.oracle_gemv_nvfp4_w4a16.restype = None
     lib.oracle_gemv_fp8_w8a16.argtypes = [P, P, I, I, P, I, P, P]
@@ -190,6 +192,23 @@ def mmvq_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d) -> np.ndarray:
     y = np.empty((M, N), np.float64)
     _load().oracle_mmvq_q6_k(_p(w_ql), _p(w_qh), _p(w_sc), _p(w_d), N, K, _p(a_qs), _p(a_d), M,
                              _p(y))
+    return y
+
+
+def mmvq_iq4_xs(w_qs, w_hdr, a_qs, a_d) -> np.ndarray:
+    """IQ4_XS weights (qs [N][K/2], hdr [N][K/256][8]) x Q8_1 (codes and d8)
+    -> y [M][N] float64."""
+    w_qs = _c(w_qs, np.uint8)
+    w_hdr = _c(w_hdr, np.uint8)
+    a_qs = _c(a_qs, np.int8)
+    a_d = _c(a_d, np.uint16)
+    N, K2 = w_qs.shape
+    M, K = a_qs.shape
+    assert K == 2 * K2 and K % 256 == 0
+    assert w_hdr.shape == (N, K // 256, 8)
+    assert a_d.shape == (M, K // 32)
+    y = np.empty((M, N), np.float64)
+    _load().oracle_mmvq_iq4_xs(_p(w_qs), _p(w_hdr), N, K, _p(a_qs), _p(a_d), M, _p(y))
     return y
 
 

@@ -17,8 +17,8 @@
  *     is folded into the group scales, each 16-element group being flushed
  *     into an FP32 accumulator; FP8 weights are one E4M3 byte per weight.
  *     Weights stay packed and are decoded only where they are consumed.
- *   - The same page's model table runs Q4_K and Q6_K models through that
- *     MMVQ dot; their super-block arithmetic is the published GGUF K-quant
+ *   - The same page's model table runs Q4_K, Q6_K and IQ4_XS models through
+ *     that MMVQ dot; their super-block arithmetic is the published GGUF
  *     definition (not on the pages), stated next to those functions.
  *   The pages do not spell out Q8_1, the nibble order, the FP8 scale
  *   granularity or the exact rounding rules; the readings taken here are the
@@ -351,6 +351,63 @@ void oracle_mmvq_q6_k(const uint8_t *w_ql, const uint8_t *w_qh, const int8_t *w_
                 double d = oracle_f16_to_double(w_d[(size_t)n * (K / 256) + b / 8]);
                 double d8 = oracle_f16_to_double(a_d[(size_t)m * nb + b]);
                 acc += d * (d8 * (double)itot);
+            }
+            y[(size_t)m * N + n] = acc;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* IQ4_XS weights x Q8_1 activations.                                        */
+/* ------------------------------------------------------------------------ */
+
+/* The CMP page's model table ("llama.cpp results") also runs a Qwen3-8B
+ * IQ4_XS model through the MMVQ int8 dot, without defining the format.  The
+ * published GGUF definition: super-blocks of 256 weights, one binary16 d,
+ * and per sub-block j of 32 a 6-bit scale ls_j; each weight is a 4-bit
+ * index into a fixed non-uniform table of 16 signed integers (the IQ4_NL
+ * table, below), so weight = d * (ls_j - 32) * table[q].
+ * Layout (planar, ours; the same 4.25 bits per weight as the original):
+ *   qs  [N][K/2]: indices q in 0..15, same nibble order as Q4_0 (block b of
+ *       32: byte j low nibble = element 32b+j, high nibble = 32b+16+j);
+ *   hdr [N][K/256][8]: bytes 0-1 d (binary16), bytes 2-3 a little-endian
+ *       16-bit word H whose bits 2j..2j+1 are the high two bits of ls_j,
+ *       bytes 4..7 = L[0..3] whose nibble j%2 of L[j/2] is the low four bits:
+ *       ls_j = ((L[j/2] >> (4 (j%2))) & 15) | (((H >> 2j) & 3) << 4).
+ * With Q8_1 activations, sub-block j of super-block S is activation block
+ * b = 8S + j and contributes d * (ls_j - 32) * d8_b * isum_b with
+ * isum_b = sum_{i<32} table[q] * q8 (exact int32).  The table values are
+ * signed, so there is no offset and the Q8_1 sum term is not used. */
+static const int iq4nl_table[16] = {-127, -104, -83, -65, -49, -35, -22, -10,
+                                    1,    13,   25,  38,  53,  69,  89,  113};
+
+static inline int iq4xs_scale(const uint8_t *hdr, int j)
+{
+    int H = hdr[2] | (hdr[3] << 8);
+    int lo = (hdr[4 + j / 2] >> (4 * (j % 2))) & 15;
+    int hi = (H >> (2 * j)) & 3;
+    return lo | (hi << 4);
+}
+
+void oracle_mmvq_iq4_xs(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
+                        const int8_t *a_qs, const uint16_t *a_d, int M, double *y)
+{
+    int nb = K / 32, ns = K / 256;
+#pragma omp parallel for schedule(static)
+    for (int n = 0; n < N; ++n) {
+        const uint8_t *row = w_qs + (size_t)n * (K / 2);
+        for (int m = 0; m < M; ++m) {
+            const int8_t *a = a_qs + (size_t)m * K;
+            double acc = 0.0;
+            for (int b = 0; b < nb; ++b) {
+                const uint8_t *h = w_hdr + ((size_t)n * ns + b / 8) * 8;
+                double d = oracle_f16_to_double((uint16_t)(h[0] | (h[1] << 8)));
+                int ls = iq4xs_scale(h, b % 8);
+                int32_t isum = 0;
+                for (int i = 0; i < 32; ++i)
+                    isum += iq4nl_table[q4_code(row, 32 * b + i)] * (int32_t)a[32 * b + i];
+                double d8 = oracle_f16_to_double(a_d[(size_t)m * nb + b]);
+                acc += d * (double)(ls - 32) * (d8 * (double)isum);
             }
             y[(size_t)m * N + n] = acc;
         }

@@ -25,6 +25,9 @@ Distributions (one per workload):
   * Q6_K weights: uniform random bytes for the low and high code bits (codes
     uniform over 0..63) and for the int8 sub-block scales; d ~ U[6.2e-5,
     2e-4] rounded to binary16.
+  * IQ4_XS weights: uniform random bytes for the 4-bit table indices and for
+    the 6 packed scale bytes of each super-block (every 6-bit scale uniform
+    over 0..63); d ~ U[6.2e-5, 2e-4] rounded to binary16.
 
 Seeds: ``seed(config, shape, tensor)`` = 1000*config + 10*shape + tensor,
 tensor 0 = codes/weights, 1 = scales, 2 = activations.
@@ -113,6 +116,19 @@ def q6_k_weights(N: int, K: int, base_seed: int):
     return w_ql, w_qh, w_sc, w_d
 
 
+def iq4_xs_weights(N: int, K: int, base_seed: int):
+    """-> (w_qs uint8 [N][K/2], w_hdr uint8 [N][K/256][8]: binary16 d in
+    bytes 0-1, then 6 bytes of packed sub-block scale bits)."""
+    ns = K // 256
+    w_qs = _rng(base_seed + 0).integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    r = _rng(base_seed + 1)
+    hdr = np.empty((N, ns, 8), np.uint8)
+    d = r.uniform(6.2e-5, 2e-4, size=(N, ns)).astype(np.float16)
+    hdr[:, :, 0:2] = d.view(np.uint8).reshape(N, ns, 2)
+    hdr[:, :, 2:8] = r.integers(0, 256, size=(N, ns, 6), dtype=np.uint8)
+    return w_qs, hdr
+
+
 def q8_1_unit_scale_source(M: int, K: int, s: int) -> np.ndarray:
     """float32 integer-valued activations for the exact-integer gate.
 
@@ -177,6 +193,22 @@ def q6_k_weights_torch(N: int, K: int, base_seed: int, device):
     u = torch.rand((N, K // 256), dtype=torch.float32, device=device, generator=g)
     w_d = (6.2e-5 + 1.38e-4 * u).to(torch.float16).view(torch.int16)
     return w_ql, w_qh, w_sc, w_d
+
+
+def iq4_xs_weights_torch(N: int, K: int, base_seed: int, device):
+    """Device-side draw with the distributions of ``iq4_xs_weights``.
+    -> (w_qs uint8 [N][K/2], w_hdr uint8 [N][K/256][8])."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(base_seed))
+    ns = K // 256
+    w_qs = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device=device, generator=g)
+    hdr = torch.randint(0, 256, (N, ns, 8), dtype=torch.uint8, device=device, generator=g)
+    u = torch.rand((N, ns), dtype=torch.float32, device=device, generator=g)
+    d = (6.2e-5 + 1.38e-4 * u).to(torch.float16)
+    hdr[:, :, 0:2] = d.view(torch.uint8).reshape(N, ns, 2)
+    return w_qs, hdr
 
 
 def normal_f32_torch(M: int, K: int, s: int, device):

@@ -509,6 +509,140 @@ def test_k_quant_bruteforce_is_sensitive():
 
 # ------------------------------------------------------------ NVFP4 W4A16
 
+# ------------------------------------------------------------ IQ4_XS x Q8_1
+
+def iq4_table():
+    """The 16-entry IQ4_NL table from its fixture (not from the oracle)."""
+    return np.array([int(v) for v in read_golden("iq4_nl_table.txt")[0]["table"]], np.int64)
+
+
+def iq4_xs_scales(hdr):
+    """hdr [N][ns][8] -> d [N][ns] float64, ls [N][ns*8] int (0..63)."""
+    N, ns, _ = hdr.shape
+    d = f16_bits_to_f64(hdr[:, :, 0:2].copy().view(np.uint16)[:, :, 0])
+    H = hdr[:, :, 2].astype(np.int64) | (hdr[:, :, 3].astype(np.int64) << 8)
+    L = hdr[:, :, 4:8].astype(np.int64)
+    ls = np.stack([((L[:, :, j // 2] >> (4 * (j % 2))) & 15) | (((H >> (2 * j)) & 3) << 4)
+                   for j in range(8)], axis=2)
+    return d, ls.reshape(N, ns * 8)
+
+
+def iq4_xs_header(d_bits, ls):
+    """Encode binary16 d [N][ns] and 6-bit scales ls [N][ns][8] into the
+    8-byte headers [N][ns][8]."""
+    N, ns = d_bits.shape
+    hdr = np.zeros((N, ns, 8), np.uint8)
+    hdr[:, :, 0:2] = d_bits.astype(np.uint16).view(np.uint8).reshape(N, ns, 2)
+    H = np.zeros((N, ns), np.int64)
+    for j in range(8):
+        H |= (ls[:, :, j].astype(np.int64) >> 4) << (2 * j)
+        hdr[:, :, 4 + j // 2] |= ((ls[:, :, j] & 15) << (4 * (j % 2))).astype(np.uint8)
+    hdr[:, :, 2] = (H & 255).astype(np.uint8)
+    hdr[:, :, 3] = (H >> 8).astype(np.uint8)
+    return hdr
+
+
+def brute_iq4_xs(w_qs, w_hdr, a_qs, a_d, table=None):
+    """Dequantize (d (ls - 32) T[q] per weight) and the Q8_1 codes to fp64,
+    then one matmul."""
+    T = iq4_table() if table is None else table
+    d, ls = iq4_xs_scales(w_hdr)
+    W = T[unpack_q4_0(w_qs)].astype(np.float64) * np.repeat(np.repeat(d, 8, axis=1) * (ls - 32), 32, axis=1)
+    A = a_qs.astype(np.float64) * np.repeat(f16_bits_to_f64(a_d), 32, axis=1)
+    return A @ W.T
+
+
+def test_iq4_xs_golden_superblock():
+    rec = read_golden("iq4_xs_superblock.txt")[0]
+    K = 256
+    hdr = np.array([int(v, 16) for v in rec["hdr"]], np.uint8).reshape(1, 1, 8)
+    w_qs = np.zeros((1, K // 2), np.uint8)
+    w_qs[0, 0:16] = [int(v, 16) for v in rec["qs0"]]
+    w_qs[0, 16:32] = [int(v, 16) for v in rec["qs1"]]
+    a_qs = np.ones((1, K), np.int8)
+    for blk, key in ((0, "a0_special"), (1, "a1_special")):
+        sp = [int(v) for v in rec[key]]
+        for i in range(0, len(sp), 2):
+            a_qs[0, 32 * blk + sp[i]] = sp[i + 1]
+    a_d = np.full((1, K // 32), int(rec["a_d"][0], 16), np.uint16)
+    y = oracle.mmvq_iq4_xs(w_qs, hdr, a_qs, a_d)
+    assert y[0, 0] == float(rec["y"][0])
+    # the fixture's block sums agree with an independent unpacking
+    q = iq4_table()[unpack_q4_0(w_qs)[0]]
+    isum = [int(np.dot(q[32 * b:32 * b + 32], a_qs[0, 32 * b:32 * b + 32].astype(np.int64)))
+            for b in range(2)]
+    assert isum == [int(v) for v in rec["isum"]]
+    d, ls = iq4_xs_scales(hdr)
+    assert d[0, 0] == 0.5 and list(ls[0]) == [35, 30, 32, 32, 32, 32, 32, 32]
+
+
+def test_iq4_xs_unit_vectors_recover_table_and_scales():
+    # row n holds index n everywhere, d = 1; sub-block j has scale ls_j - 32;
+    # activation row m is one code 1 (d8 = 1) in sub-block j(m), so
+    # y[m][n] = T[n] * (ls_j(m) - 32)
+    N, K = 16, 512
+    ls = np.array([0, 63, 17, 46, 32, 5, 50, 31, 33, 47, 16, 1, 62, 40, 24, 9])
+    w_qs = np.repeat((np.arange(16, dtype=np.uint8) * 17)[:, None], K // 2, axis=1)
+    hdr = iq4_xs_header(np.full((N, 2), 0x3C00), np.tile(ls.reshape(1, 2, 8), (N, 1, 1)))
+    pos = [0, 37, 70, 127, 129, 191, 200, 255, 256, 300, 330, 383, 400, 450, 480, 511]
+    M = len(pos)
+    a_qs = np.zeros((M, K), np.int8)
+    a_qs[np.arange(M), pos] = 1
+    a_d = np.full((M, K // 32), 0x3C00, np.uint16)
+    y = oracle.mmvq_iq4_xs(w_qs, hdr, a_qs, a_d)
+    T = iq4_table()
+    expect = np.array([[T[n] * (ls[p // 32] - 32) for n in range(N)] for p in pos], np.float64)
+    assert np.array_equal(y, expect)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 7, 256), (4, 37, 1024), (8, 16, 4096)])
+def test_iq4_xs_vs_fp64_bruteforce(M, N, K):
+    w_qs, w_hdr = inputs.iq4_xs_weights(N, K, 700 + K)
+    x = inputs.normal_f32(M, K, 800 + K)
+    a_qs, a_d, _ = oracle.quantize_q8_1(x)
+    y = oracle.mmvq_iq4_xs(w_qs, w_hdr, a_qs, a_d)
+    y_bf = brute_iq4_xs(w_qs, w_hdr, a_qs, a_d)
+    d, ls = iq4_xs_scales(w_hdr)
+    W = np.abs(iq4_table()[unpack_q4_0(w_qs)] * np.repeat(np.repeat(d, 8, axis=1) * (ls - 32), 32, axis=1))
+    mag = (np.abs(a_qs.astype(np.float64)) * np.repeat(f16_bits_to_f64(a_d), 32, axis=1)) @ W.T
+    # block sums are exact integers: only binary64 rounding remains
+    assert np.all(np.abs(y - y_bf) <= (K // 32 + 3) * 2.0 ** -52 * mag + 1e-300)
+
+
+def test_iq4_xs_unit_scale_exact():
+    # d = 1, ls = 33 (scale 1), integer activations with d8 = 1:
+    # y = sum T[q] q8 exactly
+    M, N, K = 3, 11, 2048
+    x = inputs.q8_1_unit_scale_source(M, K, 71)
+    a_qs, a_d, _ = oracle.quantize_q8_1(x)
+    w_qs, _ = inputs.iq4_xs_weights(N, K, 72)
+    hdr = iq4_xs_header(np.full((N, K // 256), 0x3C00), np.full((N, K // 256, 8), 33))
+    y = oracle.mmvq_iq4_xs(w_qs, hdr, a_qs, a_d)
+    exact = a_qs.astype(np.int64) @ iq4_table()[unpack_q4_0(w_qs)].T
+    assert np.array_equal(y, exact.astype(np.float64))
+
+
+def test_iq4_xs_bruteforce_is_sensitive():
+    M, N, K = 2, 9, 512
+    x = inputs.normal_f32(M, K, 81)
+    a_qs, a_d, _ = oracle.quantize_q8_1(x)
+    w_qs, w_hdr = inputs.iq4_xs_weights(N, K, 82)
+    y = oracle.mmvq_iq4_xs(w_qs, w_hdr, a_qs, a_d)
+    tol = 1e-2 * np.max(np.abs(y))
+    # swapped nibbles, a dropped -32, high scale bits read from the other
+    # header byte, or the table read backwards are all noticed
+    swapped = ((w_qs >> 4) | (w_qs << 4)).astype(np.uint8)
+    assert np.max(np.abs(brute_iq4_xs(swapped, w_hdr, a_qs, a_d) - y)) > tol
+    d, ls = iq4_xs_scales(w_hdr)
+    no_offset = iq4_xs_header(w_hdr[:, :, 0:2].copy().view(np.uint16)[:, :, 0],
+                              (ls.reshape(N, -1, 8) + 32) % 64)
+    assert np.max(np.abs(brute_iq4_xs(w_qs, no_offset, a_qs, a_d) - y)) > tol
+    hswap = w_hdr.copy()
+    hswap[:, :, 2], hswap[:, :, 3] = w_hdr[:, :, 3], w_hdr[:, :, 2]
+    assert np.max(np.abs(brute_iq4_xs(w_qs, hswap, a_qs, a_d) - y)) > tol
+    assert np.max(np.abs(brute_iq4_xs(w_qs, w_hdr, a_qs, a_d, iq4_table()[::-1]) - y)) > tol
+
+
 def test_nvfp4_golden_row():
     rec = read_golden("nvfp4_row.txt")[0]
     codes = np.array([[int(v, 16) for v in rec["codes"]]], np.uint8)
