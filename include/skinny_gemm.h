@@ -59,7 +59,7 @@ extern "C" {
  * work-items, well inside the 2^32 that one dispatch can hold. */
 #define SKINNY_MAX_K  (1 << 20)
 #define SKINNY_MAX_N  (1 << 24)
-#define SKINNY_MAX_M_GEMV   8    /* mmvq_q4_0, mmvq_q4_k, mmvq_q6_k */
+#define SKINNY_MAX_M_GEMV   8    /* mmvq_q4_0, mmvq_q4_k, mmvq_q6_k, mmvq_iq4_xs */
 /* gemv_nvfp4_w4a16: two 8-row verification tiles. */
 #define SKINNY_MAX_M_F16ACT 16
 /* gemv_fp8_w8a16: also the "chunked" band up to 96 rows. */
@@ -190,6 +190,31 @@ int mmvq_q4_k(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
 int mmvq_q6_k(const uint8_t *w_ql, const uint8_t *w_qh, const int8_t *w_sc,
               const uint16_t *w_d, int N, int K, const int8_t *a_qs,
               const uint16_t *a_d, int M, float *y, void *stream);
+
+/*
+ * mmvq_iq4_xs -- y = A * W^T for IQ4_XS weights and Q8_1 activations.
+ *
+ * "Machine Learning on NVIDIA CMP", "llama.cpp results": an IQ4_XS model
+ * decodes through the same MMVQ 4-way int8 dot as Q4_0.  The pages do not
+ * define the format; this is the published GGUF IQ4_XS arithmetic in a
+ * planar layout of our own (4.25 bits per weight, as the original):
+ *   w_qs  [N][K/2] bytes, 4-bit indices q in Q4_0 nibble order per block of
+ *         32 (byte j: element j low nibble, element j+16 high nibble).
+ *   w_hdr [N][K/256][8] bytes per super-block of 256: bytes 0-1 d
+ *         (binary16), bytes 2-3 a little-endian word H, bytes 4-7 a
+ *         little-endian word L; sub-block j = 0..7 of 32 has the 6-bit scale
+ *         ls_j = ((L >> 4j) & 15) | (((H >> 2j) & 3) << 4).
+ *   weight = d * (ls_j - 32) * T[q], T = {-127, -104, -83, -65, -49, -35,
+ *         -22, -10, 1, 13, 25, 38, 53, 69, 89, 113} (the IQ4_NL table).
+ * For each m, n:  y = sum_b d (ls - 32) d8_b isum_b, isum_b = sum_{i<32}
+ * T[q] q8 (exact int32; T is signed, so the Q8_1 sum term is not used).
+ * Accumulated in float32.
+ *   w_qs, a_qs, a_d 16-byte aligned; w_hdr 8-byte aligned; y float32
+ *   [M][N], 4-byte aligned.  0 <= M <= SKINNY_MAX_M_GEMV; K % 256 == 0.
+ */
+int mmvq_iq4_xs(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
+                const int8_t *a_qs, const uint16_t *a_d, int M, float *y,
+                void *stream);
 
 /*
  * gemv_nvfp4_w4a16 -- y = x * W^T for NVFP4 weights and binary16 activations.

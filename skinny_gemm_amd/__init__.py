@@ -1,6 +1,6 @@
 """skinny_gemm_amd -- block-quantized matrix x vector and skinny GEMM
-(M = 1..16) for AMD Instinct MI355X (gfx950): Q4_0, Q4_K and Q6_K weights
-with Q8_1 activations, NVFP4 and FP8 weights with binary16 activations.
+(M = 1..16) for AMD Instinct MI355X (gfx950): Q4_0, Q4_K, Q6_K and IQ4_XS
+weights with Q8_1 activations, NVFP4 and FP8 weights with binary16 activations.
 
 The computation lives in libskinny_gemm.so (hand-written HIP kernels behind
 the C ABI declared in include/skinny_gemm.h).  This package is its thin
@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     gemv_nvfp4_w4a16_packed,
     lib,
     library_path,
+    mmvq_iq4_xs,
     mmvq_q4_0,
     mmvq_q4_0_f32act,
     mmvq_q4_0_packed,

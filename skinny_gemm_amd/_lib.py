@@ -28,7 +28,7 @@ EXPORTS = ("skinny_status_string", "quantize_act_q8_1", "mmvq_q4_0", "mmvq_q4_0_
            "gemv_nvfp4_w4a16", "prepack_nvfp4_size", "prepack_nvfp4",
            "gemv_nvfp4_w4a16_packed", "gemv_fp8_w8a16", "prepack_fp8_size", "prepack_fp8",
            "gemv_fp8_w8a16_packed", "prepack_q4_k_size", "prepack_q4_k", "mmvq_q4_k_packed",
-           "prepack_q6_k_size", "prepack_q6_k", "mmvq_q6_k_packed")
+           "prepack_q6_k_size", "prepack_q6_k", "mmvq_q6_k_packed", "mmvq_iq4_xs")
 
 _lib = None
 
@@ -66,6 +66,8 @@ def lib():
     L.mmvq_q4_k.restype = I
     L.mmvq_q6_k.argtypes = [P, P, P, P, I, I, P, P, I, P, P]
     L.mmvq_q6_k.restype = I
+    L.mmvq_iq4_xs.argtypes = [P, P, I, I, P, P, I, P, P]
+    L.mmvq_iq4_xs.restype = I
     L.gemv_nvfp4_w4a16.argtypes = [P, P, ctypes.c_float, I, I, P, I, P, P]
     L.gemv_nvfp4_w4a16.restype = I
     L.prepack_q4_0_size.argtypes = [I, I, ctypes.POINTER(ctypes.c_size_t)]
@@ -261,6 +263,26 @@ def mmvq_q6_k(w_ql, w_qh, w_sc, w_d, a_qs, a_d, y=None, stream=None):
     _req(y, "y", (torch.float32,), (M, N))
     _run("mmvq_q6_k", (w_ql, w_qh, w_sc, w_d, a_qs, a_d, y), stream, _ptr(w_ql), _ptr(w_qh),
          _ptr(w_sc), _ptr(w_d), N, K, _ptr(a_qs), _ptr(a_d), M, _ptr(y))
+    return y
+
+
+def mmvq_iq4_xs(w_qs, w_hdr, a_qs, a_d, y=None, stream=None):
+    """IQ4_XS weights (qs [N][K/2], hdr [N][K/256][8]), Q8_1 activations
+    (codes and d8) -> y float32 [M][N]."""
+    torch = _torch()
+    _req(w_qs, "w_qs", (torch.uint8,))
+    N, K2 = w_qs.shape
+    K = 2 * K2
+    _req(w_hdr, "w_hdr", (torch.uint8,), (N, K // 256, 8))
+    _req(a_qs, "a_qs", (torch.int8,))
+    M = a_qs.shape[0]
+    _req(a_qs, "a_qs", (torch.int8,), (M, K))
+    _req(a_d, "a_d", _f16_bits_dtypes(), (M, K // 32))
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=w_qs.device)
+    _req(y, "y", (torch.float32,), (M, N))
+    _run("mmvq_iq4_xs", (w_qs, w_hdr, a_qs, a_d, y), stream, _ptr(w_qs), _ptr(w_hdr), N, K,
+         _ptr(a_qs), _ptr(a_d), M, _ptr(y))
     return y
 
 

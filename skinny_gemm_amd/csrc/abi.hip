@@ -110,6 +110,20 @@ int mmvq_q6_k(const uint8_t *w_ql, const uint8_t *w_qh, const int8_t *w_sc, cons
                                            (hipStream_t)stream));
 }
 
+int mmvq_iq4_xs(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K, const int8_t *a_qs,
+                const uint16_t *a_d, int M, float *y, void *stream) {
+  int st = gemv_m_status(M, SKINNY_MAX_M_GEMV);
+  if (st) return st;
+  if ((st = shape_status(N, K, 256))) return st;
+  if (M == 0 || N == 0) return SKINNY_OK;
+  if (!w_qs || !w_hdr || !a_qs || !a_d || !y) return SKINNY_ERR_NULL;
+  if (!aligned(w_qs, 16) || !aligned(w_hdr, 8) || !aligned(a_qs, 16) || !aligned(a_d, 16) ||
+      !aligned(y, 4))
+    return SKINNY_ERR_ALIGN;
+  return launched(skinny::launch_mmvq_iq4_xs(w_qs, w_hdr, N, K, a_qs, a_d, M, y,
+                                             (hipStream_t)stream));
+}
+
 int gemv_nvfp4_w4a16(const uint8_t *w_codes, const uint8_t *w_scales, float global_scale,
                      int N, int K, const uint16_t *x, int M, uint16_t *y, void *stream) {
   int st = gemv_m_status(M, SKINNY_MAX_M_F16ACT);

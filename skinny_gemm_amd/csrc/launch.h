@@ -34,6 +34,10 @@ hipError_t launch_mmvq_q6_k(const uint8_t *w_ql, const uint8_t *w_qh, const int8
                             const uint16_t *w_d, int N, int K, const int8_t *a_qs,
                             const uint16_t *a_d, int M, float *y, hipStream_t stream);
 
+hipError_t launch_mmvq_iq4_xs(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
+                              const int8_t *a_qs, const uint16_t *a_d, int M, float *y,
+                              hipStream_t stream);
+
 hipError_t launch_gemv_nvfp4(const uint8_t *w_codes, const uint8_t *w_scales,
                              float g, int N, int K, const uint16_t *x, int M,
                              uint16_t *y, hipStream_t stream);

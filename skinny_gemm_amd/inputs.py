@@ -129,15 +129,17 @@ def iq4_xs_weights(N: int, K: int, base_seed: int):
     return w_qs, hdr
 
 
-def q8_1_unit_scale_source(M: int, K: int, s: int) -> np.ndarray:
+def q8_1_unit_scale_source(M: int, K: int, s: int, spread: int = 60) -> np.ndarray:
     """float32 integer-valued activations for the exact-integer gate.
 
-    Every 32-block holds one entry of +-127 and 31 entries in [-60, 60], so
-    its Q8_1 scale is exactly 1, its codes equal the inputs, and the code
-    sum (|sum| <= 127 + 31*60 = 1987) is an integer binary16 holds exactly.
+    Every 32-block holds one entry of +-127 and 31 entries in [-spread,
+    spread] (spread <= 60), so its Q8_1 scale is exactly 1, its codes equal
+    the inputs, and the code sum (|sum| <= 127 + 31*60 = 1987) is an integer
+    binary16 holds exactly.
     """
+    assert 0 <= spread <= 60
     r = _rng(s)
-    x = r.integers(-60, 61, size=(M, K)).astype(np.float32)
+    x = r.integers(-spread, spread + 1, size=(M, K)).astype(np.float32)
     nb = K // 32
     pos = r.integers(0, 32, size=(M, nb))
     sign = np.where(r.integers(0, 2, size=(M, nb)) == 0, -127.0, 127.0)

@@ -39,7 +39,7 @@ def test_header_declares_the_entry_points():
                                            "prepack_q4_0", "mmvq_q4_0_packed", "prepack_fp8_size",
                                            "prepack_fp8", "gemv_fp8_w8a16_packed", "prepack_q4_k_size",
                                            "prepack_q4_k", "mmvq_q4_k_packed", "prepack_q6_k_size",
-                                           "prepack_q6_k", "mmvq_q6_k_packed"])
+                                           "prepack_q6_k", "mmvq_q6_k_packed", "mmvq_iq4_xs"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -86,11 +86,15 @@ def q6k(L, ql=A, qh=A, sc=A, d=A, N=64, K=256, aq=A, ad=A, M=1, y=A):
     return L.mmvq_q6_k(V(ql), V(qh), V(sc), V(d), N, K, V(aq), V(ad), M, V(y), None)
 
 
+def iq4(L, w=A, h=A, N=64, K=256, aq=A, ad=A, M=1, y=A):
+    return L.mmvq_iq4_xs(V(w), V(h), N, K, V(aq), V(ad), M, V(y), None)
+
+
 def qa(L, x=A, M=1, K=256, qs=A, d=A, s=A):
     return L.quantize_act_q8_1(V(x), M, K, V(qs), V(d), V(s), None)
 
 
-@pytest.mark.parametrize("fn,max_m", [(q4, 8), (q4k, 8), (q6k, 8), (nv, 16), (f8, 96)])
+@pytest.mark.parametrize("fn,max_m", [(q4, 8), (q4k, 8), (q6k, 8), (iq4, 8), (nv, 16), (f8, 96)])
 def test_gemv_rejects_m_out_of_range(L, fn, max_m):
     assert fn(L, M=max_m + 1) == -4
     assert fn(L, M=-1) == -4
@@ -220,7 +224,7 @@ def test_f32act_validation(L):
     assert call(x=V(A + 4)) == -3 and call(w=V(A + 8)) == -3 and call(y=V(A + 2)) == -3
 
 
-@pytest.mark.parametrize("fn", [q4k, q6k])
+@pytest.mark.parametrize("fn", [q4k, q6k, iq4])
 def test_k_quant_validation(L, fn):
     # K must be a whole number of 256-weight super-blocks
     for K in (0, 32, 128, 256 + 32, 4096 + 128, (1 << 20) + 256):
@@ -244,6 +248,11 @@ def test_k_quant_null_and_alignment(L):
     # the weaker requirements really are weaker
     assert q6k(L, qh=A + 8, y=0) == -1
     assert q6k(L, sc=A + 2, y=0) == -1
+    for kw in ("w", "h", "aq", "ad", "y"):
+        assert iq4(L, **{kw: 0}) == -1, kw
+    for kw, off in (("w", 8), ("h", 4), ("aq", 8), ("ad", 8), ("y", 2)):
+        assert iq4(L, **{kw: A + off}) == -3, kw
+    assert iq4(L, h=A + 8, y=0) == -1
 
 
 def nvp(L, w=A, N=64, K=256, x=A, M=1, y=A):

@@ -780,6 +780,102 @@ def test_k_quant_pipeline_device_quantize():
               q6_k_mag(w_ql, w_qh, w_sc, w_d, a_qs, a_d), K, "q6_k pipeline")
 
 
+# ------------------------------------------------------------------ IQ4_XS
+
+def iq4_table():
+    from conftest import read_golden
+
+    return np.array([int(v) for v in read_golden("iq4_nl_table.txt")[0]["table"]], np.int64)
+
+
+def iq4_xs_abs_weights(w_qs, w_hdr):
+    """|d (ls - 32) T[q]| per weight, [N][K] float64."""
+    N, ns, _ = w_hdr.shape
+    d = f16(w_hdr[:, :, 0:2].copy().view(np.uint16)[:, :, 0])
+    H = w_hdr[:, :, 2].astype(np.int64) | (w_hdr[:, :, 3].astype(np.int64) << 8)
+    L = w_hdr[:, :, 4:8].astype(np.int64)
+    ls = np.stack([((L[:, :, j // 2] >> (4 * (j % 2))) & 15) | (((H >> (2 * j)) & 3) << 4)
+                   for j in range(8)], axis=2).reshape(N, ns * 8)
+    scale = np.repeat(np.repeat(np.abs(d), 8, axis=1) * np.abs(ls - 32), 32, axis=1)
+    return np.abs(iq4_table()[unpack_q4_0(w_qs)]) * scale
+
+
+def iq4_xs_mag(w_qs, w_hdr, a_qs, a_d):
+    A = np.abs(a_qs.astype(np.float64)) * np.repeat(np.abs(f16(a_d)), 32, axis=1)
+    return A @ iq4_xs_abs_weights(w_qs, w_hdr).T
+
+
+def run_iq4_xs(w_qs, w_hdr, a_qs, a_d):
+    import skinny_gemm_amd as sk
+
+    return host(sk.mmvq_iq4_xs(dev(w_qs), dev(w_hdr), dev(a_qs), dev(a_d)))
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("N,K", KQ_SHAPES)
+def test_mmvq_iq4_xs_vs_oracle(M, N, K):
+    w_qs, w_hdr = inputs.iq4_xs_weights(N, K, 17 * N + K)
+    x = inputs.normal_f32(M, K, 7 * M + K)
+    a_qs, a_d, _ = oracle.quantize_q8_1(x)
+    y = run_iq4_xs(w_qs, w_hdr, a_qs, a_d)
+    ref = oracle.mmvq_iq4_xs(w_qs, w_hdr, a_qs, a_d)
+    check_f32(y, ref, iq4_xs_mag(w_qs, w_hdr, a_qs, a_d), K,
+              "iq4_xs M=%d N=%d K=%d" % (M, N, K))
+
+
+# (M, N, K) of the IQ4_XS exact-integer gate, one or more per route
+IQ4_GATE = [
+    (1, 300, 4096), (2, 300, 4096),             # vector kernel, two blocks per lane
+    (1, 16400, 4096),                           # ... four rows per wave
+    (1, 300, 8192), (2, 300, 12288),            # ... four and six blocks per lane
+    (1, 300, 16384),                            # ... eight blocks per lane
+    (2, 300, 20480),                            # ... rounds of six blocks
+    (3, 300, 4096), (8, 300, 4096),             # staged activations, two rows x 8 waves
+    (8, 300, 16384),                            # ... the largest staging batch
+    (4, 16400, 4096),                           # ... four rows x 4 waves
+    (8, 77, 20480), (8, 16400, 20480),          # vector kernel at M = 8 (past the LDS)
+]
+
+
+@pytest.mark.parametrize("M,N,K", IQ4_GATE)
+def test_mmvq_iq4_xs_integer_gate_bit_exact(M, N, K):
+    # d = 1, every scale ls = 33 (weight = T[q]), integer activations with
+    # d8 = 1: every block sum and every partial sum is an integer below 2^24,
+    # so the result is exact in any summation order
+    x = inputs.q8_1_unit_scale_source(M, K, 90 + M + K, spread=60 if K <= 4096 else 6)
+    a_qs, a_d, _ = oracle.quantize_q8_1(x)
+    w_qs, w_hdr = inputs.iq4_xs_weights(N, K, 91 + N)
+    w_hdr[:, :, 0:2] = np.array([0x3C00], np.uint16).view(np.uint8)
+    w_hdr[:, :, 2:4] = 0xAA                       # high bits 2 in every sub-block
+    w_hdr[:, :, 4:8] = 0x11                       # low bits 1: ls = 33
+    W = np.abs(iq4_table()[unpack_q4_0(w_qs)]).astype(np.float64)
+    assert (np.abs(a_qs.astype(np.float64)) @ W.T).max() < 2 ** 24
+    y = run_iq4_xs(w_qs, w_hdr, a_qs, a_d)
+    ref = oracle.mmvq_iq4_xs(w_qs, w_hdr, a_qs, a_d)
+    assert np.array_equal(ref, np.round(ref))
+    assert np.array_equal(y.astype(np.float64), ref)
+
+
+def test_mmvq_iq4_xs_device_quantize_and_zero_sizes():
+    import skinny_gemm_amd as sk
+    import torch
+
+    M, N, K = 5, 3000 + 7, 5120
+    x = inputs.normal_f32(M, K, 93)
+    qs, d, _ = sk.quantize_act_q8_1(dev(x))
+    a_qs, a_d, _ = oracle.quantize_q8_1(x)
+    w_qs, w_hdr = inputs.iq4_xs_weights(N, K, 94)
+    y = host(sk.mmvq_iq4_xs(dev(w_qs), dev(w_hdr), qs, d))
+    check_f32(y, oracle.mmvq_iq4_xs(w_qs, w_hdr, a_qs, a_d), iq4_xs_mag(w_qs, w_hdr, a_qs, a_d),
+              K, "iq4_xs pipeline")
+    # M = 0 and N = 0 enqueue nothing and leave y untouched
+    y0 = torch.full((0, N), 1.0, device="cuda")
+    sk.mmvq_iq4_xs(dev(w_qs), dev(w_hdr), qs[:0], d[:0], y0)
+    yn = torch.full((M, 0), 1.0, device="cuda")
+    sk.mmvq_iq4_xs(dev(w_qs[:0]), dev(w_hdr[:0]), qs, d, yn)
+    torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------------ NVFP4
 
 def run_nvfp4(codes, scales, g, x):
@@ -1436,6 +1532,21 @@ def test_q6_k_packed_full_sizes_sampled(M):
         ref = oracle.mmvq_q6_k(w_ql[rows], w_qh[rows], w_sc[rows], w_d[rows], a_qs, a_d)
         mag = q6_k_mag(w_ql[rows], w_qh[rows], w_sc[rows], w_d[rows], a_qs, a_d)
         check_f32(y[:, rows], ref, mag, K, "q6_k packed full M=%d %dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_iq4_xs_full_sizes_sampled(M):
+    # the Qwen3-8B projection shapes (K x N: 4096 x 6144, 4096 x 4096,
+    # 4096 x 24576, 12288 x 4096), launched as the benchmark launches them
+    for si, (N, K) in enumerate([(6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288)]):
+        w_qs, w_hdr = inputs.iq4_xs_weights(N, K, inputs.seed(7, si, 0))
+        x = inputs.normal_f32(M, K, inputs.seed(7, si, 2) + M)
+        a_qs, a_d, _ = oracle.quantize_q8_1(x)
+        y = run_iq4_xs(w_qs, w_hdr, a_qs, a_d)
+        rows = sample_rows(N, seed=si)
+        ref = oracle.mmvq_iq4_xs(w_qs[rows], w_hdr[rows], a_qs, a_d)
+        mag = iq4_xs_mag(w_qs[rows], w_hdr[rows], a_qs, a_d)
+        check_f32(y[:, rows], ref, mag, K, "iq4_xs full M=%d %dx%d" % (M, N, K))
 
 
 @pytest.mark.parametrize("M", [1, 2])
