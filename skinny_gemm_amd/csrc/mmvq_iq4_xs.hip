@@ -47,21 +47,34 @@ constexpr uint32_t iq4_word(int i) {
          ((uint32_t)(uint8_t)kIq4Table[4 * i + 3] << 24);
 }
 
-// low3: the low three bits of four indices, one per byte; bit3: each
-// index's fourth bit moved to bit 2 of its byte.  A byte permute selector
-// s < 4 takes byte s of its second operand, 4 <= s < 8 byte s - 4 of its
-// first.
-__device__ __forceinline__ uint32_t iq4_lookup(uint32_t low3, uint32_t bit3) {
-  const uint32_t e0 = __builtin_amdgcn_perm(iq4_word(1), iq4_word(0), low3);   // entries 0-7
-  const uint32_t e8 = __builtin_amdgcn_perm(iq4_word(3), iq4_word(2), low3);   // entries 8-15
-  return __builtin_amdgcn_perm(e8, e0, bit3 | 0x03020100u);
+// The table words and the two byte masks the decode uses, held in vector
+// registers for the kernel's lifetime (the empty asm hides their values from
+// the compiler): as register operands they let each selector be formed with
+// one and-or, where a literal mask would take a separate and and or.
+struct Iq4Regs {
+  uint32_t m7, m4, t0, t1, t2, t3;
+  __device__ __forceinline__ Iq4Regs()
+      : m7(0x07070707u), m4(0x04040404u), t0(iq4_word(0)), t1(iq4_word(1)), t2(iq4_word(2)),
+        t3(iq4_word(3)) {
+    asm volatile("" : "+v"(m7), "+v"(m4), "+v"(t0), "+v"(t1), "+v"(t2), "+v"(t3));
+  }
+};
+
+// low3: the low three bits of four indices, one per byte; sel: each byte k
+// set to k + 4 * (the index's fourth bit).  A byte permute selector s < 4
+// takes byte s of its second operand, 4 <= s < 8 byte s - 4 of its first.
+__device__ __forceinline__ uint32_t iq4_lookup(uint32_t low3, uint32_t sel, const Iq4Regs &k) {
+  const uint32_t e0 = __builtin_amdgcn_perm(k.t1, k.t0, low3);   // entries 0-7
+  const uint32_t e8 = __builtin_amdgcn_perm(k.t3, k.t2, low3);   // entries 8-15
+  return __builtin_amdgcn_perm(e8, e0, sel);
 }
 
 // One word of a block's index bytes -> the int8 table values of its low
 // nibbles (elements i..i+3 of the block) and of its high nibbles (16+i..).
-__device__ __forceinline__ void iq4_decode(uint32_t w, uint32_t &lo, uint32_t &hi) {
-  lo = iq4_lookup(w & 0x07070707u, (w >> 1) & 0x04040404u);
-  hi = iq4_lookup((w >> 4) & 0x07070707u, (w >> 5) & 0x04040404u);
+__device__ __forceinline__ void iq4_decode(uint32_t w, uint32_t &lo, uint32_t &hi,
+                                           const Iq4Regs &k) {
+  lo = iq4_lookup(w & k.m7, ((w >> 1) & k.m4) | 0x03020100u, k);
+  hi = iq4_lookup((w >> 4) & k.m7, ((w >> 5) & k.m4) | 0x03020100u, k);
 }
 
 // d * (ls_j - 32) of sub-block j from the two header words (x: d | H << 16,
@@ -101,6 +114,7 @@ __global__ __launch_bounds__(256) void mmvq_iq4_xs_kernel(
   if (n0 >= N) return;
   const int nb = K >> 5;
   const int j = lane & 7;
+  const Iq4Regs kr;
 
   const uint8_t *wrow[R];
   const uint8_t *hrow[R];
@@ -148,7 +162,7 @@ __global__ __launch_bounds__(256) void mmvq_iq4_xs_kernel(
         const float dls = iq4_scale(hd[u][r], j);
         uint32_t lo[4], hi[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) iq4_decode(wq[u][r][i], lo[i], hi[i]);
+        for (int i = 0; i < 4; ++i) iq4_decode(wq[u][r][i], lo[i], hi[i], kr);
 #pragma unroll
         for (int m = 0; m < M; ++m) {
           int32_t isum = 0;
@@ -184,6 +198,7 @@ __global__ __launch_bounds__(64 * W) void mmvq_iq4_xs_lds_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // row addresses stay scalar
   const int nb = K >> 5;
   const int j = lane & 7;
+  const Iq4Regs kr;
   float *ld8 = reinterpret_cast<float *>(lq + M * K);
   const int n0 = (blockIdx.x * W + wave) * R;
   // 16-byte pieces: codes (M K / 16), then d8 (M nb / 8, eight blocks each)
@@ -257,7 +272,7 @@ __global__ __launch_bounds__(64 * W) void mmvq_iq4_xs_lds_kernel(
       const float dls = iq4_scale(rd.hd[r], j);
       uint32_t lo[4], hi[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) iq4_decode(rd.wq[r][i], lo[i], hi[i]);
+      for (int i = 0; i < 4; ++i) iq4_decode(rd.wq[r][i], lo[i], hi[i], kr);
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         const uint4_t aq0 = *reinterpret_cast<const uint4_t *>(lq + (size_t)m * K + 32 * b);
@@ -295,21 +310,32 @@ hipError_t launch_iq4_mru(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int 
   return hipGetLastError();
 }
 
-// At M <= 2 a lane takes its whole share of a row in one round up to 8
-// blocks (K <= 16384; longer rows take rounds of 6), two rows per wave, four
-// on wide matrices; wider M one block per round.
+// Launch shapes measured on MI355X over the Qwen3-8B projections (K x N
+// 4096 x 6144, 4096 x 4096, 4096 x 24576, 12288 x 4096) at M = 1, 2, 4, 8
+// with weights rotating over > 1 GiB.  At M = 1 a lane takes its whole share
+// of a row in one round up to 8 blocks (K <= 16384; longer rows take rounds
+// of 6), but wide matrices with short rows one block per round (4096 x
+// 24576: 12.3 -> 11.4 us against two blocks and four rows per wave); at M = 2
+// rounds of two blocks up to K = 12288 (12288 x 4096 8.8 -> 8.4 us against
+// one round of six), four rows per wave on wide matrices; wider M one block
+// per round, four rows per wave on wide matrices.
 template <int M>
 hipError_t launch_iq4_m(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
                         const int8_t *a_qs, const uint16_t *a_d, float *y, hipStream_t stream) {
   const int per_lane = ((K >> 5) + kWave - 1) / kWave;
 #define SKINNY_IQ4(R, U) return launch_iq4_mru<M, R, U>(w_qs, w_hdr, N, K, a_qs, a_d, y, stream)
-  if constexpr (M <= 2) {
+  if constexpr (M == 1) {
     if (per_lane <= 2) {
-      if (N >= 16384) SKINNY_IQ4(4, 2);
+      if (N >= 16384) SKINNY_IQ4(2, 1);
       SKINNY_IQ4(2, 2);
     }
     if (per_lane <= 4) SKINNY_IQ4(2, 4);
     if (per_lane <= 6 || per_lane > 8) SKINNY_IQ4(2, 6);
+    SKINNY_IQ4(2, 8);
+  } else if constexpr (M == 2) {
+    if (per_lane <= 2 && N >= 16384) SKINNY_IQ4(4, 2);
+    if (per_lane <= 6) SKINNY_IQ4(2, 2);
+    if (per_lane > 8) SKINNY_IQ4(2, 6);
     SKINNY_IQ4(2, 8);
   } else {
     if (N >= 16384) SKINNY_IQ4(4, 1);
@@ -352,11 +378,7 @@ hipError_t launch_iq4_lds_rw(const uint8_t *w_qs, const uint8_t *w_hdr, int N, i
 template <int M>
 hipError_t launch_iq4_lds(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
                           const int8_t *a_qs, const uint16_t *a_d, float *y, hipStream_t stream) {
-#define SKINNY_IQ4RW(R, W) \
-  return launch_iq4_lds_rw<M, R, W>(w_qs, w_hdr, N, K, a_qs, a_d, y, stream)
-  if (N >= 16384) SKINNY_IQ4RW(4, 4);
-  SKINNY_IQ4RW(2, 8);
-#undef SKINNY_IQ4RW
+  return launch_iq4_lds_rw<M, 2, 8>(w_qs, w_hdr, N, K, a_qs, a_d, y, stream);
 }
 
 }  // namespace
@@ -364,7 +386,13 @@ hipError_t launch_iq4_lds(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int 
 hipError_t launch_mmvq_iq4_xs(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
                               const int8_t *a_qs, const uint16_t *a_d, int M, float *y,
                               hipStream_t stream) {
-  if (M >= 3 && iq4_lds_bytes(M, K) <= kIq4LdsMaxBytes) {
+  // From M = 3 the staged kernel where the activation re-reads weigh most:
+  // long rows (12288 x 4096 at M = 4: 10.2 -> 9.4 us, at M = 8: 15.7 -> 12.6
+  // us) and, from M = 6, narrow matrices (4096 x 4096 at M = 8); the vector
+  // kernel elsewhere (4096 x 6144 at M = 8: 9.4 -> 7.8 us, 4096 x 24576:
+  // 23.4 -> 22.4 us against staging).
+  if (M >= 3 && (K >= 8192 || (M >= 6 && N <= 4096)) &&
+      iq4_lds_bytes(M, K) <= kIq4LdsMaxBytes) {
     switch (M) {
 #define SKINNY_IQ4L(MM) \
   case MM: return launch_iq4_lds<MM>(w_qs, w_hdr, N, K, a_qs, a_d, y, stream);

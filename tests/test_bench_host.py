@@ -38,6 +38,9 @@ def test_byte_counts_match_block_sizes():
     assert bench.q4_k_bytes(M, K, N) == N * K // 256 * 144 + M * K // 32 * 36 + out_f32
     # the Q6_K kernel reads only d of each Q8_1 block, not s
     assert bench.q6_k_bytes(M, K, N) == N * K // 256 * 210 + M * K // 32 * 34 + out_f32
+    # IQ4_XS: 128 bytes of indices + an 8-byte header per 256 weights; the
+    # kernel reads only d of each Q8_1 block
+    assert bench.iq4_xs_bytes(M, K, N) == N * K // 256 * 136 + M * K // 32 * 34 + out_f32
     assert bench.nvfp4_bytes(M, K, N) == N * K // 16 * 9 + 4 + 2 * M * K + 2 * M * N
     assert bench.fp8_bytes(M, K, N) == N * K + 4 * N + 2 * M * K + 2 * M * N
 

@@ -826,14 +826,18 @@ def test_mmvq_iq4_xs_vs_oracle(M, N, K):
 # (M, N, K) of the IQ4_XS exact-integer gate, one or more per route
 IQ4_GATE = [
     (1, 300, 4096), (2, 300, 4096),             # vector kernel, two blocks per lane
-    (1, 16400, 4096),                           # ... four rows per wave
-    (1, 300, 8192), (2, 300, 12288),            # ... four and six blocks per lane
-    (1, 300, 16384),                            # ... eight blocks per lane
-    (2, 300, 20480),                            # ... rounds of six blocks
-    (3, 300, 4096), (8, 300, 4096),             # staged activations, two rows x 8 waves
+    (1, 16400, 4096),                           # ... one block per round (M = 1, wide)
+    (2, 16400, 4096),                           # ... four rows per wave (M = 2, wide)
+    (1, 300, 8192), (1, 300, 12288),            # ... four and six blocks per lane
+    (2, 300, 12288),                            # ... rounds of two blocks (M = 2)
+    (1, 300, 16384), (2, 300, 16384),           # ... eight blocks per lane
+    (1, 300, 20480), (2, 300, 20480),           # ... rounds of six blocks
+    (3, 300, 4096), (5, 6000, 4096),            # vector kernel, M >= 3, two rows per wave
+    (4, 16400, 4096), (8, 16400, 4096),         # ... four rows per wave (wide)
+    (3, 300, 8192),                             # staged activations (long rows)
+    (8, 300, 4096), (6, 4096, 4096),            # ... narrow matrices from M = 6
     (8, 300, 16384),                            # ... the largest staging batch
-    (4, 16400, 4096),                           # ... four rows x 4 waves
-    (8, 77, 20480), (8, 16400, 20480),          # vector kernel at M = 8 (past the LDS)
+    (8, 77, 20480), (8, 16400, 20480),          # vector kernel past the LDS limit
 ]
 
 
