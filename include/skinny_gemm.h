@@ -209,8 +209,9 @@ int mmvq_q6_k(const uint8_t *w_ql, const uint8_t *w_qh, const int8_t *w_sc,
  * For each m, n:  y = sum_b d (ls - 32) d8_b isum_b, isum_b = sum_{i<32}
  * T[q] q8 (exact int32; T is signed, so the Q8_1 sum term is not used).
  * Accumulated in float32.
- *   w_qs, a_qs, a_d 16-byte aligned; w_hdr 8-byte aligned; y float32
- *   [M][N], 4-byte aligned.  0 <= M <= SKINNY_MAX_M_GEMV; K % 256 == 0.
+ *   w_qs, w_hdr, a_qs, a_d 16-byte aligned (the headers are read with
+ *   128-bit loads on some paths); y float32 [M][N], 4-byte aligned.
+ *   0 <= M <= SKINNY_MAX_M_GEMV; K % 256 == 0.
  */
 int mmvq_iq4_xs(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
                 const int8_t *a_qs, const uint16_t *a_d, int M, float *y,

@@ -117,7 +117,7 @@ int mmvq_iq4_xs(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K, const i
   if ((st = shape_status(N, K, 256))) return st;
   if (M == 0 || N == 0) return SKINNY_OK;
   if (!w_qs || !w_hdr || !a_qs || !a_d || !y) return SKINNY_ERR_NULL;
-  if (!aligned(w_qs, 16) || !aligned(w_hdr, 8) || !aligned(a_qs, 16) || !aligned(a_d, 16) ||
+  if (!aligned(w_qs, 16) || !aligned(w_hdr, 16) || !aligned(a_qs, 16) || !aligned(a_d, 16) ||
       !aligned(y, 4))
     return SKINNY_ERR_ALIGN;
   return launched(skinny::launch_mmvq_iq4_xs(w_qs, w_hdr, N, K, a_qs, a_d, M, y,

@@ -16,11 +16,11 @@
 //   acc += d (ls_j - 32) d8 isum,  isum = sum T[q] q8  (exact int32)
 // T is signed, so no Q8_1 sum term enters.
 //
-// Decode: a word of four indices (one per byte) becomes four int8 table
-// values with three byte permutes.  The low three bits of each index select
-// among entries 0-7 and, separately, among entries 8-15 (the table lives in
-// four registers, eight entries per permute); the fourth bit then picks, per
-// byte, which of the two results to keep.
+// Decode (iq4.h): a word of four indices becomes four int8 table values
+// with three byte permutes.
+//
+// Large matrices at M >= 6 take the Q4_0 matrix-core kernel instead, with
+// the indices decoded through the table into its int8 operands.
 //
 // Mapping, as the Q4_K vector kernel: one wave = R weight rows over the full
 // K; lane l takes blocks l, l + 64, ... in rounds of U blocks, all loaded
@@ -32,57 +32,10 @@
 // Bytes per call: N*K*(1/2 + 1/32) weights, M*K*(1 + 2/32) activations (codes
 // and d8), 4*M*N output.
 #include "device.h"
+#include "iq4.h"
 #include "launch.h"
 
 namespace skinny {
-namespace {
-
-constexpr int8_t kIq4Table[16] = {-127, -104, -83, -65, -49, -35, -22, -10,
-                                  1,    13,   25,  38,  53,  69,  89,  113};
-
-// Entries 4i..4i+3 of the table as one little-endian word of int8 bytes.
-constexpr uint32_t iq4_word(int i) {
-  return (uint32_t)(uint8_t)kIq4Table[4 * i] | ((uint32_t)(uint8_t)kIq4Table[4 * i + 1] << 8) |
-         ((uint32_t)(uint8_t)kIq4Table[4 * i + 2] << 16) |
-         ((uint32_t)(uint8_t)kIq4Table[4 * i + 3] << 24);
-}
-
-// The table words and the two byte masks the decode uses, held in vector
-// registers for the kernel's lifetime (the empty asm hides their values from
-// the compiler): as register operands they let each selector be formed with
-// one and-or, where a literal mask would take a separate and and or.
-struct Iq4Regs {
-  uint32_t m7, m4, t0, t1, t2, t3;
-  __device__ __forceinline__ Iq4Regs()
-      : m7(0x07070707u), m4(0x04040404u), t0(iq4_word(0)), t1(iq4_word(1)), t2(iq4_word(2)),
-        t3(iq4_word(3)) {
-    asm volatile("" : "+v"(m7), "+v"(m4), "+v"(t0), "+v"(t1), "+v"(t2), "+v"(t3));
-  }
-};
-
-// low3: the low three bits of four indices, one per byte; sel: each byte k
-// set to k + 4 * (the index's fourth bit).  A byte permute selector s < 4
-// takes byte s of its second operand, 4 <= s < 8 byte s - 4 of its first.
-__device__ __forceinline__ uint32_t iq4_lookup(uint32_t low3, uint32_t sel, const Iq4Regs &k) {
-  const uint32_t e0 = __builtin_amdgcn_perm(k.t1, k.t0, low3);   // entries 0-7
-  const uint32_t e8 = __builtin_amdgcn_perm(k.t3, k.t2, low3);   // entries 8-15
-  return __builtin_amdgcn_perm(e8, e0, sel);
-}
-
-// One word of a block's index bytes -> the int8 table values of its low
-// nibbles (elements i..i+3 of the block) and of its high nibbles (16+i..).
-__device__ __forceinline__ void iq4_decode(uint32_t w, uint32_t &lo, uint32_t &hi,
-                                           const Iq4Regs &k) {
-  lo = iq4_lookup(w & k.m7, ((w >> 1) & k.m4) | 0x03020100u, k);
-  hi = iq4_lookup((w >> 4) & k.m7, ((w >> 5) & k.m4) | 0x03020100u, k);
-}
-
-// d * (ls_j - 32) of sub-block j from the two header words (x: d | H << 16,
-// y: L).
-__device__ __forceinline__ float iq4_scale(uint2_t h, int j) {
-  const int ls = (int)((h.y >> (4 * j)) & 15u) | (int)(((h.x >> (16 + 2 * j)) & 3u) << 4);
-  return f16_bits_to_f32((uint16_t)(h.x & 0xFFFFu)) * (float)(ls - 32);
-}
 
 constexpr int iq4_pow2(int v) { return v <= 1 ? 1 : 2 * iq4_pow2((v + 1) / 2); }
 
@@ -302,7 +255,7 @@ __global__ __launch_bounds__(64 * W) void mmvq_iq4_xs_lds_kernel(
 }
 
 template <int M, int R, int U>
-hipError_t launch_iq4_mru(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
+static hipError_t launch_iq4_mru(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
                           const int8_t *a_qs, const uint16_t *a_d, float *y, hipStream_t stream) {
   const int waves = (N + R - 1) / R;
   hipLaunchKernelGGL((mmvq_iq4_xs_kernel<M, R, U>), dim3((waves + 3) / 4), dim3(256), 0, stream,
@@ -320,7 +273,7 @@ hipError_t launch_iq4_mru(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int 
 // one round of six), four rows per wave on wide matrices; wider M one block
 // per round, four rows per wave on wide matrices.
 template <int M>
-hipError_t launch_iq4_m(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
+static hipError_t launch_iq4_m(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
                         const int8_t *a_qs, const uint16_t *a_d, float *y, hipStream_t stream) {
   const int per_lane = ((K >> 5) + kWave - 1) / kWave;
 #define SKINNY_IQ4(R, U) return launch_iq4_mru<M, R, U>(w_qs, w_hdr, N, K, a_qs, a_d, y, stream)
@@ -346,10 +299,10 @@ hipError_t launch_iq4_m(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
 
 constexpr int kIq4LdsMaxBytes = 160 * 1024;
 
-int iq4_lds_bytes(int M, int K) { return M * K + 4 * M * (K >> 5); }
+static int iq4_lds_bytes(int M, int K) { return M * K + 4 * M * (K >> 5); }
 
 template <int M, int R, int W, int A>
-hipError_t launch_iq4_lds_a(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
+static hipError_t launch_iq4_lds_a(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
                             const int8_t *a_qs, const uint16_t *a_d, float *y,
                             hipStream_t stream) {
   const int lds = iq4_lds_bytes(M, K);
@@ -362,7 +315,7 @@ hipError_t launch_iq4_lds_a(const uint8_t *w_qs, const uint8_t *w_hdr, int N, in
 }
 
 template <int M, int R, int W>
-hipError_t launch_iq4_lds_rw(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
+static hipError_t launch_iq4_lds_rw(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
                              const int8_t *a_qs, const uint16_t *a_d, float *y,
                              hipStream_t stream) {
   const int pieces = M * K / 16 + M * (K >> 5) / 8;
@@ -376,16 +329,21 @@ hipError_t launch_iq4_lds_rw(const uint8_t *w_qs, const uint8_t *w_hdr, int N, i
 }
 
 template <int M>
-hipError_t launch_iq4_lds(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
+static hipError_t launch_iq4_lds(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
                           const int8_t *a_qs, const uint16_t *a_d, float *y, hipStream_t stream) {
   return launch_iq4_lds_rw<M, 2, 8>(w_qs, w_hdr, N, K, a_qs, a_d, y, stream);
 }
 
-}  // namespace
-
 hipError_t launch_mmvq_iq4_xs(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
                               const int8_t *a_qs, const uint16_t *a_d, int M, float *y,
                               hipStream_t stream) {
+  // From M = 6 large matrices take the matrix cores (the Q4_0 kernel with
+  // table-decoded operands; measured on MI355X at M = 8: 4096 x 24576
+  // 22.2 -> 18.8 us, 5120 x 13824 21.9 -> 15.9 us, 13824 x 5120 27.0 -> 20.7
+  // us, 8192 x 8192 16.9 -> 14.9 us; up to 48M weights the vector and
+  // staged kernels stay ahead at every M, 4096 x 6144 7.8 against 9.0 us)
+  if (M >= 6 && K % 512 == 0 && (long long)N * K >= (60ll << 20))
+    return launch_mmvq_iq4_xs_mfma(w_qs, w_hdr, N, K, a_qs, a_d, M, y, stream);
   // From M = 3 the staged kernel where the activation re-reads weigh most:
   // long rows (12288 x 4096 at M = 4: 10.2 -> 9.4 us, at M = 8: 15.7 -> 12.6
   // us) and, from M = 6, narrow matrices (4096 x 4096 at M = 8); the vector

@@ -20,6 +20,8 @@
 //     finished output per lane; no atomics, fully deterministic.
 // Bytes per call: N*K*(1/2 + 2/32) weights + M*K*(1 + 4/32) activations +
 // 4*M*N output.
+#include <type_traits>
+
 #include "device.h"
 #include "q4_mfma.h"
 #include "launch.h"
@@ -182,7 +184,7 @@ __global__ __launch_bounds__(256) void mmvq_q4_0_kernel(
 // issued in the order they are consumed, so each wait covers one chunk.
 // The KS partial tiles are summed in LDS.
 namespace q4 {
-template <int T, int WR, int KS, int S, int MP>
+template <int T, int WR, int KS, int S, int MP, int WSB = 4>
 struct Cfg {
   static constexpr int kWaves = WR * KS;
   static constexpr int kRows = 16 * T;              // weight rows per wave
@@ -190,7 +192,7 @@ struct Cfg {
   static constexpr int kRpi = 1024 / kCB;           // code rows per 1 KB block
   static constexpr int kSwz = S / 2 - 1;            // code column swizzle mask
   static constexpr int kCi = kRows / kRpi;          // code loads per chunk
-  static constexpr int kWsB = kRows * 4 * S;        // weight-scale bytes per chunk
+  static constexpr int kWsB = kRows * WSB * S;      // weight-scale bytes per chunk
   static constexpr int kWst = kCi * 1024 + kWsB;    // wave weight buffer
   static constexpr int kRpa = 16 / S;               // activation rows per 1 KB block
   static constexpr int kAi = MP / kRpa;             // activation code loads per chunk
@@ -219,15 +221,24 @@ struct Chunk {
 // (No __restrict__ on the inputs: the issue fence below must be able to
 // order their loads.)
 //
-// KQ selects Q4_K weights: the same 4-bit codes, and in place of the block
-// scales w_d a header array of the same geometry (K/16 bytes per row: one
-// 16-byte header {d, dmin, 12 scale/min bytes} per 8 blocks), so staging is
-// unchanged and only the epilogue decodes the lane's sub-block scale and min.
-template <int T, int WR, int KS, int S, int MP, int D, bool KQ = false>
+// FMT selects the weight format.  kFmtQ4K: Q4_K weights, the same 4-bit
+// codes, and in place of the block scales w_d a header array of the same
+// geometry (K/16 bytes per row: one 16-byte header {d, dmin, 12 scale/min
+// bytes} per 8 blocks), so staging is unchanged and only the epilogue
+// decodes the lane's sub-block scale and min.  kFmtIQ4: IQ4_XS weights, the
+// 4-bit indices in the same nibble order decoded through the IQ4_NL table
+// into signed int8 operands, and an 8-byte header {d, H, L} per 8 blocks
+// (K/32 bytes per row: 16 bytes per row per 8-step chunk, so only S = 8).
+constexpr int kFmtQ40 = 0, kFmtQ4K = 1, kFmtIQ4 = 2;
+struct NoRegs {};
+
+template <int T, int WR, int KS, int S, int MP, int D, int FMT = kFmtQ40>
 __global__ __launch_bounds__(64 * WR * KS) void mmvq_q4_0_mfma_kernel(
     const uint8_t *w_qs, const uint16_t *w_d, int N, int K, const int8_t *a_qs,
     const uint16_t *a_d, const uint16_t *a_s, int M, float *y) {
-  using C = q4::Cfg<T, WR, KS, S, MP>;
+  constexpr int kWsb = FMT == kFmtIQ4 ? 2 : 4;   // scale bytes per row per step
+  static_assert(FMT != kFmtIQ4 || S == 8, "IQ4_XS headers come in 16-byte pieces of 8 steps");
+  using C = q4::Cfg<T, WR, KS, S, MP, kWsb>;
   using R = q4::Chunk<T, S, C::kApw>;
   static_assert(D == 1 || D == 2, "chunks in flight");
   extern __shared__ uint4_t smem4[];
@@ -256,8 +267,10 @@ __global__ __launch_bounds__(64 * WR * KS) void mmvq_q4_0_mfma_kernel(
   }
   const bool wsact = lane < C::kWsB / 16;
   const int wl = lane % (C::kWsB / 16);     // lanes past the scale bytes repeat one
-  const uint8_t *wssrc = reinterpret_cast<const uint8_t *>(
-      w_d + (size_t)min(n0 + wl % C::kRows, N - 1) * nb) + 16 * (wl / C::kRows);
+  const uint8_t *wssrc = reinterpret_cast<const uint8_t *>(w_d) +
+                         (size_t)min(n0 + wl % C::kRows, N - 1) * (size_t)(kWsb * (K >> 6)) +
+                         16 * (wl / C::kRows);
+  const std::conditional_t<FMT == kFmtIQ4, Iq4Regs, NoRegs> kr{};
   // activation pieces of this wave: p = wr, wr + WR, ... (the last repeated);
   // pieces 0 .. kAi-1 are code blocks, piece kAi the scales (lanes [0, kNd)
   // d8, [kNd, 2 kNd) s8, 16-byte pieces of 8 blocks of row am)
@@ -283,7 +296,7 @@ __global__ __launch_bounds__(64 * WR * KS) void mmvq_q4_0_mfma_kernel(
   auto load = [&](int c, R &rg) {
 #pragma unroll
     for (int q = 0; q < C::kCi; ++q) rg.c[q] = load16_nt(csrc[q] + (size_t)c * C::kCB);
-    rg.ws = load16_nt(wssrc + (size_t)c * (4 * S));
+    rg.ws = load16_nt(wssrc + (size_t)c * (kWsb * S));
 #pragma unroll
     for (int u = 0; u < C::kApw; ++u)
       rg.a[u] = load16(asrc[u] + (size_t)c * (apiece[u] < C::kAi ? 64 * S : 4 * S));
@@ -342,7 +355,10 @@ __global__ __launch_bounds__(64 * WR * KS) void mmvq_q4_0_mfma_kernel(
         const int col = (2 * st + hb) ^ (q & C::kSwz);
         const uint2_t wq = *reinterpret_cast<const uint2_t *>(
             wbuf + 1024 * q + 16 * (C::kRpi * col + r % C::kRpi) + 8 * bh);
-        isum[st][t] = q4_mfma_isum(wq, aop);
+        if constexpr (FMT == kFmtIQ4)
+          isum[st][t] = iq4_mfma_isum(wq, aop, kr);
+        else
+          isum[st][t] = q4_mfma_isum(wq, aop);
       }
     }
 #pragma unroll
@@ -353,7 +369,11 @@ __global__ __launch_bounds__(64 * WR * KS) void mmvq_q4_0_mfma_kernel(
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         const int r = 16 * t + j;
-        if constexpr (KQ) {
+        if constexpr (FMT == kFmtIQ4) {
+          const uint2_t hd = *reinterpret_cast<const uint2_t *>(
+              wbuf + C::kCi * 1024 + 16 * r + 8 * (bl >> 3));
+          iq4_mfma_epilogue(isum[st][t], iq4_scale(hd, bl & 7), sa, sb, acc[t]);
+        } else if constexpr (FMT == kFmtQ4K) {
           const uint8_t *h = wbuf + C::kCi * 1024 + 16 * ((bl >> 3) * C::kRows + r);
           const int sj = bl & 7;                           // sub-block in the super-block
           const uint32_t dd = *reinterpret_cast<const uint32_t *>(h);
@@ -433,18 +453,18 @@ __global__ __launch_bounds__(64 * WR * KS) void mmvq_q4_0_mfma_kernel(
   }
 }
 
-template <int T, int WR, int KS, int S, int MP, int D, bool KQ>
+template <int T, int WR, int KS, int S, int MP, int D, int FMT>
 static hipError_t launch_mfma_cfg(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                                   const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
                                   int M, float *y, hipStream_t stream) {
-  using C = q4::Cfg<T, WR, KS, S, MP>;
+  using C = q4::Cfg<T, WR, KS, S, MP, FMT == kFmtIQ4 ? 2 : 4>;
   if (K % (64 * S) != 0) return hipErrorInvalidValue;   // chunks must tile K
   const hipError_t lds_ok =
-      allow_lds((const void *)mmvq_q4_0_mfma_kernel<T, WR, KS, S, MP, D, KQ>, C::kLds);
+      allow_lds((const void *)mmvq_q4_0_mfma_kernel<T, WR, KS, S, MP, D, FMT>, C::kLds);
   if (lds_ok != hipSuccess) return lds_ok;
   const int rows = C::kRows * WR;
   const int blocks = (N + rows - 1) / rows;
-  hipLaunchKernelGGL((mmvq_q4_0_mfma_kernel<T, WR, KS, S, MP, D, KQ>), dim3(blocks),
+  hipLaunchKernelGGL((mmvq_q4_0_mfma_kernel<T, WR, KS, S, MP, D, FMT>), dim3(blocks),
                      dim3(64 * C::kWaves), C::kLds, stream, w_qs, w_d, N, K, a_qs, a_d, a_s,
                      M, y);
   return hipGetLastError();
@@ -463,60 +483,71 @@ static hipError_t launch_mfma_cfg(const uint8_t *w_qs, const uint16_t *w_d, int 
 // (13824 x 5120 23.9 -> 17.6 us), four-way below 256 tiles; chunks of 4
 // steps (K % 512 == 256) keep the eight-way split there.  Q4_K has rows of
 // its own below 1100 tiles.
-template <int MP, bool KQ>
+template <int MP, int FMT>
 static hipError_t launch_mfma_mp(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                                  const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
                                  int M, float *y, hipStream_t stream) {
   const int tiles = (N + 15) / 16;
   const bool s8 = K % 512 == 0;
 #define SKINNY_Q4(T, WR, KS, S) \
-  return launch_mfma_cfg<T, WR, KS, S, MP, 1, KQ>(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream)
-  if constexpr (KQ) {
-    // Q4_K (its per-step header decode makes shorter chunks pay below 800
-    // tiles; measured as above: 7168 x 7168 at M = 8 13.6 -> 12.9 us,
-    // 2560 x 10240 8.5 -> 7.9 us against the Q4_0 choices)
-    if (tiles < 1100) {
-      if (tiles >= 800) {
-        if (s8) SKINNY_Q4(1, 2, 2, 8);
-        SKINNY_Q4(1, 2, 2, 4);
+  return launch_mfma_cfg<T, WR, KS, S, MP, 1, FMT>(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream)
+  if constexpr (FMT == kFmtIQ4) {
+    // IQ4_XS, 8-step chunks only (measured on MI355X at M = 3, 4, 6, 8 over
+    // 20 configurations: 4096 x 24576 at M = 8 18.8 us with two waves
+    // sharing activations and a two-way split, 21.6 without sharing;
+    // 5120 x 13824 15.9 us with the split alone; 8192 x 8192 and 13824 x
+    // 5120 14.9 and 20.7 us with a four-way split)
+    if (tiles >= 1100) SKINNY_Q4(1, 2, 2, 8);
+    if (tiles >= 600) SKINNY_Q4(1, 1, 2, 8);
+    SKINNY_Q4(1, 1, 4, 8);
+  } else {
+    if constexpr (FMT == kFmtQ4K) {
+      // Q4_K (its per-step header decode makes shorter chunks pay below 800
+      // tiles; measured as above: 7168 x 7168 at M = 8 13.6 -> 12.9 us,
+      // 2560 x 10240 8.5 -> 7.9 us against the Q4_0 choices)
+      if (tiles < 1100) {
+        if (tiles >= 800) {
+          if (s8) SKINNY_Q4(1, 2, 2, 8);
+          SKINNY_Q4(1, 2, 2, 4);
+        }
+        if (tiles >= 600) SKINNY_Q4(1, 1, 2, 4);
+        if (tiles > 256) SKINNY_Q4(1, 1, 4, 4);
+        if (s8) SKINNY_Q4(1, 1, 4, 8);
+        SKINNY_Q4(1, 1, 8, 4);
       }
-      if (tiles >= 600) SKINNY_Q4(1, 1, 2, 4);
-      if (tiles > 256) SKINNY_Q4(1, 1, 4, 4);
-      if (s8) SKINNY_Q4(1, 1, 4, 8);
-      SKINNY_Q4(1, 1, 8, 4);
     }
+    if (tiles >= 1800) {
+      if (s8) SKINNY_Q4(1, 4, 1, 8);
+      SKINNY_Q4(1, 4, 1, 4);
+    }
+    if (tiles >= 1100) {
+      if (s8) SKINNY_Q4(1, 2, 1, 8);
+      SKINNY_Q4(1, 2, 1, 4);
+    }
+    if (tiles >= 800) {
+      if (s8) SKINNY_Q4(1, 2, 2, 8);
+      SKINNY_Q4(1, 2, 2, 4);
+    }
+    if (tiles >= 512) {
+      if (s8) SKINNY_Q4(1, 1, 2, 8);
+      SKINNY_Q4(1, 1, 2, 4);
+    }
+    if (s8) {
+      if (tiles <= 256) SKINNY_Q4(1, 1, 4, 8);
+      if (K >= 8192) SKINNY_Q4(2, 1, 4, 8);
+      SKINNY_Q4(1, 1, 2, 8);
+    }
+    SKINNY_Q4(1, 1, 8, 4);
   }
-  if (tiles >= 1800) {
-    if (s8) SKINNY_Q4(1, 4, 1, 8);
-    SKINNY_Q4(1, 4, 1, 4);
-  }
-  if (tiles >= 1100) {
-    if (s8) SKINNY_Q4(1, 2, 1, 8);
-    SKINNY_Q4(1, 2, 1, 4);
-  }
-  if (tiles >= 800) {
-    if (s8) SKINNY_Q4(1, 2, 2, 8);
-    SKINNY_Q4(1, 2, 2, 4);
-  }
-  if (tiles >= 512) {
-    if (s8) SKINNY_Q4(1, 1, 2, 8);
-    SKINNY_Q4(1, 1, 2, 4);
-  }
-  if (s8) {
-    if (tiles <= 256) SKINNY_Q4(1, 1, 4, 8);
-    if (K >= 8192) SKINNY_Q4(2, 1, 4, 8);
-    SKINNY_Q4(1, 1, 2, 8);
-  }
-  SKINNY_Q4(1, 1, 8, 4);
 #undef SKINNY_Q4
 }
 
-template <bool KQ>
+template <int FMT>
 static hipError_t launch_mfma(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                               const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
                               int M, float *y, hipStream_t stream) {
-  if (M <= 4) return launch_mfma_mp<4, KQ>(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream);
-  return launch_mfma_mp<8, KQ>(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream);
+  if (M <= 4) return launch_mfma_mp<4, FMT>(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream);
+  return launch_mfma_mp<8, FMT>(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream);
 }
 
 // Vector kernel with the activation rows staged in LDS (any M <= 8, one round
@@ -1002,7 +1033,7 @@ hipError_t launch_mmvq_q4_0(const uint8_t *w_qs, const uint16_t *w_d, int N, int
   }
   const bool small = M <= kQ4VectorMaxM && N < 8192 && K < 8192;
   if (M >= kQ4MfmaMinM && K % 256 == 0 && !small)
-    return launch_mfma<false>(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream);
+    return launch_mfma<kFmtQ40>(w_qs, w_d, N, K, a_qs, a_d, a_s, M, y, stream);
   // Two rows re-read twice the activation bytes per weight byte of one: on
   // wide matrices staging them in LDS once per workgroup pays (measured on
   // MI355X: 4096 x 22016 10.8 -> 10.2 us, 4096 x 32000 15.0 -> 13.4 us); at
@@ -1032,8 +1063,20 @@ hipError_t launch_mmvq_q4_0_f32act(const uint8_t *w_qs, const uint16_t *w_d, int
 hipError_t launch_mmvq_q4_k_mfma(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
                                  const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
                                  int M, float *y, hipStream_t stream) {
-  return launch_mfma<true>(w_qs, reinterpret_cast<const uint16_t *>(w_hdr), N, K, a_qs, a_d, a_s,
-                           M, y, stream);
+  return launch_mfma<kFmtQ4K>(w_qs, reinterpret_cast<const uint16_t *>(w_hdr), N, K, a_qs, a_d,
+                              a_s, M, y, stream);
+}
+
+// IQ4_XS weights on the matrix-core kernel (3 <= M <= 8, K % 512 == 0, the
+// headers 16-byte aligned): the 8-byte super-block headers take the place
+// of the Q4_0 block scales; the Q8_1 sum term is not used, so d8 stands in
+// for it in the staging.
+hipError_t launch_mmvq_iq4_xs_mfma(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
+                                   const int8_t *a_qs, const uint16_t *a_d, int M, float *y,
+                                   hipStream_t stream) {
+  if (K % 512 != 0) return hipErrorInvalidValue;
+  return launch_mfma<kFmtIQ4>(w_qs, reinterpret_cast<const uint16_t *>(w_hdr), N, K, a_qs, a_d,
+                              a_d, M, y, stream);
 }
 
 }  // namespace skinny

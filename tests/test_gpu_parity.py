@@ -811,8 +811,15 @@ def run_iq4_xs(w_qs, w_hdr, a_qs, a_d):
     return host(sk.mmvq_iq4_xs(dev(w_qs), dev(w_hdr), dev(a_qs), dev(a_d)))
 
 
+# KQ_SHAPES, and matrices of 60M+ weights that take the matrix cores from
+# M = 6 (four-way split; two-way split; two waves sharing activations), and
+# one whose K is not a multiple of 512 and stays on the vector kernel
+IQ4_SHAPES = KQ_SHAPES + [(5000 + 3, 12800), (16384 + 9, 4096), (20000 + 3, 4096),
+                          (16000, 4352)]
+
+
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
-@pytest.mark.parametrize("N,K", KQ_SHAPES)
+@pytest.mark.parametrize("N,K", IQ4_SHAPES)
 def test_mmvq_iq4_xs_vs_oracle(M, N, K):
     w_qs, w_hdr = inputs.iq4_xs_weights(N, K, 17 * N + K)
     x = inputs.normal_f32(M, K, 7 * M + K)
@@ -838,6 +845,10 @@ IQ4_GATE = [
     (8, 300, 4096), (6, 4096, 4096),            # ... narrow matrices from M = 6
     (8, 300, 16384),                            # ... the largest staging batch
     (8, 77, 20480), (8, 16400, 20480),          # vector kernel past the LDS limit
+    (6, 5003, 12800), (8, 5003, 12800),         # matrix cores: four-way K split
+    (7, 16393, 4096),                           # ... two-way split
+    (6, 20003, 4096), (8, 20003, 4096),         # ... two waves share activations
+    (8, 16000, 4352),                           # vector kernel (K % 512 != 0)
 ]
 
 
