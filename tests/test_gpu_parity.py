@@ -1473,6 +1473,22 @@ def test_k_quants_random_shapes(M, N, K):
               q6_k_mag(w_ql, w_qh, w_sc, w_d, a_qs, a_d), K, "q6_k M=%d N=%d K=%d" % (M, N, K))
 
 
+def iq4_random_big():
+    # matrices of 60M+ weights at M >= 6 (the matrix-core route), drawn the
+    # same way with a larger size budget
+    return [s for s in random_shapes(107, 400, 512, 16384, 8, nk_max=1.2e8, mnk_max=1e9)
+            if s[0] >= 6 and s[1] * s[2] >= 63e6]
+
+
+@pytest.mark.parametrize("M,N,K", random_shapes(106, 32, 256, 16384, 8) + iq4_random_big())
+def test_mmvq_iq4_xs_random_shapes(M, N, K):
+    w_qs, w_hdr = inputs.iq4_xs_weights(N, K, 13 * N + K)
+    x = inputs.normal_f32(M, K, 17 * M + K)
+    a_qs, a_d, _ = oracle.quantize_q8_1(x)
+    check_f32(run_iq4_xs(w_qs, w_hdr, a_qs, a_d), oracle.mmvq_iq4_xs(w_qs, w_hdr, a_qs, a_d),
+              iq4_xs_mag(w_qs, w_hdr, a_qs, a_d), K, "iq4_xs M=%d N=%d K=%d" % (M, N, K))
+
+
 # ------------------------------------------------------------------ full sizes (sampled rows)
 
 LLAMA_Q4 = [(12288, 4096), (4096, 4096), (22016, 4096), (4096, 11008), (32000, 4096)]
@@ -1731,6 +1747,8 @@ def test_graph_replays_match_eager():
     w_qs, w_d = inputs.q4_0_weights_torch(N, K, 21, d)
     k_qs, k_hdr = inputs.q4_k_weights_torch(N, K, 22, d)
     ql, qh, sc, dd = inputs.q6_k_weights_torch(N, K, 23, d)
+    i_qs, i_hdr = inputs.iq4_xs_weights_torch(N, K, 28, d)
+    bi_qs, bi_hdr = inputs.iq4_xs_weights_torch(16400, K, 29, d)   # IQ4_XS matrix cores (M = 8)
     codes, scales = inputs.nvfp4_weights_torch(N, K, 24, d)
     w8, cs = inputs.fp8_weights_torch(N, K, 25, d)
     fc, fs = inputs.nvfp4_weights_torch(8192, 5120, 26, d)   # the flat NVFP4 mapping (M = 1)
@@ -1751,6 +1769,8 @@ def test_graph_replays_match_eager():
             outs.append(sk.mmvq_q4_0(w_qs, w_d, *q8[M]))
             outs.append(sk.mmvq_q4_k(k_qs, k_hdr, *q8[M]))
             outs.append(sk.mmvq_q6_k(ql, qh, sc, dd, q8[M][0], q8[M][1]))
+            outs.append(sk.mmvq_iq4_xs(i_qs, i_hdr, q8[M][0], q8[M][1]))
+        outs.append(sk.mmvq_iq4_xs(bi_qs, bi_hdr, q8[8][0], q8[8][1]))
         for M in (1, 2):
             outs.append(sk.mmvq_q4_0_f32act(w_qs, w_d, xf[M]))
         for M in (1, 2, 4, 8):
