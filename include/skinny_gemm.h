@@ -319,6 +319,39 @@ int mmvq_q4_k_packed(const uint8_t *w_packed, int N, int K, const int8_t *a_qs,
                      const uint16_t *a_d, const uint16_t *a_s, int M, float *y, void *stream);
 
 /*
+ * IQ4_XS weights pre-permuted into matrix-core operand order: the codes
+ * plane of the Q4_0 layout above (IQ4_XS indices have the Q4_0 nibble
+ * order), then a header plane of U*(K/256) blocks of 128 bytes, block (u, q)
+ * at byte 1024*U*P + 128*(u*(K/256) + q), whose bytes 8j .. 8j + 7 are
+ * w_hdr[16u + j][8q .. 8q + 7] (the header of super-block q of that row);
+ * bytes for rows >= N are zero.  The calls below give the same product as
+ * mmvq_iq4_xs from such a copy.
+ */
+
+/* prepack_iq4_xs_size -- bytes of the packed copy: 1024*U*P + U*K/2.  Host
+ * only.  0 <= N <= SKINNY_MAX_N; K % 256 == 0 (else SKINNY_ERR_SHAPE). */
+int prepack_iq4_xs_size(int N, int K, size_t *bytes);
+
+/*
+ * prepack_iq4_xs -- write the packed copy of planar IQ4_XS weights.
+ *   w_qs, w_hdr as for mmvq_iq4_xs (16-byte aligned); w_packed:
+ *   prepack_iq4_xs_size bytes, 16-byte aligned, caller-owned, not
+ *   overlapping the inputs.  Every byte of it is written.  K % 256 == 0.
+ */
+int prepack_iq4_xs(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K, uint8_t *w_packed,
+                   void *stream);
+
+/*
+ * mmvq_iq4_xs_packed -- mmvq_iq4_xs on the packed copy.
+ *   w_packed from prepack_iq4_xs for the same N and K, 16-byte aligned;
+ *   a_qs, a_d, y, M as for mmvq_iq4_xs (0 <= M <= SKINNY_MAX_M_GEMV).
+ *   Block sums are exact integers; the float result matches the definition
+ *   to float32 summation-order rounding.
+ */
+int mmvq_iq4_xs_packed(const uint8_t *w_packed, int N, int K, const int8_t *a_qs,
+                       const uint16_t *a_d, int M, float *y, void *stream);
+
+/*
  * Q6_K weights pre-permuted into matrix-core operand order.
  *
  * The matrix cores take one 16-element sub-block per K slot (lane

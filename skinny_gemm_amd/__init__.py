@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     lib,
     library_path,
     mmvq_iq4_xs,
+    mmvq_iq4_xs_packed,
     mmvq_q4_0,
     mmvq_q4_0_f32act,
     mmvq_q4_0_packed,
@@ -25,6 +26,8 @@ from ._lib import (  # noqa: F401
     mmvq_q6_k,
     mmvq_q6_k_packed,
     prepack_fp8,
+    prepack_iq4_xs,
+    prepack_iq4_xs_size,
     prepack_fp8_size,
     prepack_nvfp4,
     prepack_q4_0,

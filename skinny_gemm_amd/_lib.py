@@ -28,7 +28,8 @@ EXPORTS = ("skinny_status_string", "quantize_act_q8_1", "mmvq_q4_0", "mmvq_q4_0_
            "gemv_nvfp4_w4a16", "prepack_nvfp4_size", "prepack_nvfp4",
            "gemv_nvfp4_w4a16_packed", "gemv_fp8_w8a16", "prepack_fp8_size", "prepack_fp8",
            "gemv_fp8_w8a16_packed", "prepack_q4_k_size", "prepack_q4_k", "mmvq_q4_k_packed",
-           "prepack_q6_k_size", "prepack_q6_k", "mmvq_q6_k_packed", "mmvq_iq4_xs")
+           "prepack_q6_k_size", "prepack_q6_k", "mmvq_q6_k_packed", "mmvq_iq4_xs",
+           "prepack_iq4_xs_size", "prepack_iq4_xs", "mmvq_iq4_xs_packed")
 
 _lib = None
 
@@ -82,6 +83,12 @@ def lib():
     L.prepack_q4_k.restype = I
     L.mmvq_q4_k_packed.argtypes = [P, I, I, P, P, P, I, P, P]
     L.mmvq_q4_k_packed.restype = I
+    L.prepack_iq4_xs_size.argtypes = [I, I, ctypes.POINTER(ctypes.c_size_t)]
+    L.prepack_iq4_xs_size.restype = I
+    L.prepack_iq4_xs.argtypes = [P, P, I, I, P, P]
+    L.prepack_iq4_xs.restype = I
+    L.mmvq_iq4_xs_packed.argtypes = [P, I, I, P, P, I, P, P]
+    L.mmvq_iq4_xs_packed.restype = I
     L.prepack_q6_k_size.argtypes = [I, I, ctypes.POINTER(ctypes.c_size_t)]
     L.prepack_q6_k_size.restype = I
     L.prepack_q6_k.argtypes = [P, P, P, P, I, I, P, P]
@@ -485,6 +492,48 @@ def mmvq_q4_k_packed(w_packed, N, K, a_qs, a_d, a_s, y=None, stream=None):
     _req(y, "y", (torch.float32,), (M, N))
     _run("mmvq_q4_k_packed", (w_packed, a_qs, a_d, a_s, y), stream, _ptr(w_packed), N, K,
          _ptr(a_qs), _ptr(a_d), _ptr(a_s), M, _ptr(y))
+    return y
+
+
+def prepack_iq4_xs_size(N: int, K: int) -> int:
+    """Bytes of the packed copy of an N x K IQ4_XS matrix (K % 256 == 0)."""
+    n = ctypes.c_size_t(0)
+    _check("prepack_iq4_xs_size", lib().prepack_iq4_xs_size(int(N), int(K), ctypes.byref(n)))
+    return n.value
+
+
+def prepack_iq4_xs(w_qs, w_hdr, w_packed=None, stream=None):
+    """Planar IQ4_XS weights w_qs [N][K/2], w_hdr [N][K/256][8] -> the packed
+    copy (uint8, prepack_iq4_xs_size(N, K) bytes)."""
+    torch = _torch()
+    _req(w_qs, "w_qs", (torch.uint8,))
+    N, K2 = w_qs.shape
+    K = 2 * K2
+    _req(w_hdr, "w_hdr", (torch.uint8,), (N, K // 256, 8))
+    nbytes = prepack_iq4_xs_size(N, K)
+    if w_packed is None:
+        w_packed = torch.empty((nbytes,), dtype=torch.uint8, device=w_qs.device)
+    _req(w_packed, "w_packed", (torch.uint8,), (nbytes,))
+    _run("prepack_iq4_xs", (w_qs, w_hdr, w_packed), stream, _ptr(w_qs), _ptr(w_hdr), N, K,
+         _ptr(w_packed))
+    return w_packed
+
+
+def mmvq_iq4_xs_packed(w_packed, N, K, a_qs, a_d, y=None, stream=None):
+    """Packed IQ4_XS weights (from prepack_iq4_xs, N x K) x Q8_1 activations
+    (codes and d8) -> float32 y [M][N]."""
+    torch = _torch()
+    N, K = int(N), int(K)
+    _req(w_packed, "w_packed", (torch.uint8,), (prepack_iq4_xs_size(N, K),))
+    _req(a_qs, "a_qs", (torch.int8,))
+    M = a_qs.shape[0]
+    _req(a_qs, "a_qs", (torch.int8,), (M, K))
+    _req(a_d, "a_d", _f16_bits_dtypes(), (M, K // 32))
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=a_qs.device)
+    _req(y, "y", (torch.float32,), (M, N))
+    _run("mmvq_iq4_xs_packed", (w_packed, a_qs, a_d, y), stream, _ptr(w_packed), N, K,
+         _ptr(a_qs), _ptr(a_d), M, _ptr(y))
     return y
 
 

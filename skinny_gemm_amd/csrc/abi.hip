@@ -190,6 +190,40 @@ int prepack_q4_k(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K, uint8_
   return launched(skinny::launch_prepack_q4_k(w_qs, w_hdr, N, K, w_packed, (hipStream_t)stream));
 }
 
+int prepack_iq4_xs_size(int N, int K, size_t *bytes) {
+  const int st = shape_status(N, K, 256);
+  if (st) return st;
+  if (!bytes) return SKINNY_ERR_NULL;
+  const size_t U = ((size_t)N + 15) / 16;
+  *bytes = 1024 * U * ((size_t)K / 128) + U * (size_t)K / 2;
+  return SKINNY_OK;
+}
+
+int prepack_iq4_xs(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K, uint8_t *w_packed,
+                   void *stream) {
+  const int st = shape_status(N, K, 256);
+  if (st) return st;
+  if (N == 0) return SKINNY_OK;
+  if (!w_qs || !w_hdr || !w_packed) return SKINNY_ERR_NULL;
+  if (!aligned(w_qs, 16) || !aligned(w_hdr, 16) || !aligned(w_packed, 16))
+    return SKINNY_ERR_ALIGN;
+  return launched(skinny::launch_prepack_iq4_xs(w_qs, w_hdr, N, K, w_packed,
+                                                (hipStream_t)stream));
+}
+
+int mmvq_iq4_xs_packed(const uint8_t *w_packed, int N, int K, const int8_t *a_qs,
+                       const uint16_t *a_d, int M, float *y, void *stream) {
+  int st = gemv_m_status(M, SKINNY_MAX_M_GEMV);
+  if (st) return st;
+  if ((st = shape_status(N, K, 256))) return st;
+  if (M == 0 || N == 0) return SKINNY_OK;
+  if (!w_packed || !a_qs || !a_d || !y) return SKINNY_ERR_NULL;
+  if (!aligned(w_packed, 16) || !aligned(a_qs, 16) || !aligned(a_d, 16) || !aligned(y, 4))
+    return SKINNY_ERR_ALIGN;
+  return launched(skinny::launch_mmvq_iq4_xs_packed(w_packed, N, K, a_qs, a_d, M, y,
+                                                    (hipStream_t)stream));
+}
+
 int mmvq_q4_k_packed(const uint8_t *w_packed, int N, int K, const int8_t *a_qs,
                      const uint16_t *a_d, const uint16_t *a_s, int M, float *y, void *stream) {
   int st = gemv_m_status(M, SKINNY_MAX_M_GEMV);

@@ -47,7 +47,7 @@ hipError_t launch_gemv_nvfp4(const uint8_t *w_codes, const uint8_t *w_scales,
                              float g, int N, int K, const uint16_t *x, int M,
                              uint16_t *y, hipStream_t stream);
 
-// Pre-permuted Q4_0 and Q4_K (mmvq_q4_0_packed.hip).
+// Pre-permuted Q4_0, Q4_K and IQ4_XS (mmvq_q4_0_packed.hip).
 hipError_t launch_prepack_q4_0(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                                uint8_t *w_packed, hipStream_t stream);
 
@@ -61,6 +61,12 @@ hipError_t launch_prepack_q4_k(const uint8_t *w_qs, const uint8_t *w_hdr, int N,
 hipError_t launch_mmvq_q4_k_packed(const uint8_t *w_packed, int N, int K, const int8_t *a_qs,
                                    const uint16_t *a_d, const uint16_t *a_s, int M, float *y,
                                    hipStream_t stream);
+
+hipError_t launch_prepack_iq4_xs(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
+                                 uint8_t *w_packed, hipStream_t stream);
+
+hipError_t launch_mmvq_iq4_xs_packed(const uint8_t *w_packed, int N, int K, const int8_t *a_qs,
+                                     const uint16_t *a_d, int M, float *y, hipStream_t stream);
 
 // Pre-permuted Q6_K (mmvq_q6_k_packed.hip).
 hipError_t launch_prepack_q6_k(const uint8_t *ql, const uint8_t *qh, const int8_t *sc,

@@ -31,7 +31,7 @@
 // Size: 1024 U P + 512 U V bytes: the canonical bytes of 16 U rows, rounded
 // up to whole 512-element scale blocks.
 //
-// Q4_K (KQ) has the same 4-bit codes in the same nibble order, so its codes
+// Q4_K has the same 4-bit codes in the same nibble order, so its codes
 // plane is the same; its headers (16 bytes per row and 256-element
 // super-block: d, dmin, 12 bytes of 6-bit scales and mins) form the second
 // plane, tile-major: U K/256 blocks of 256 bytes, block (u, q) at byte
@@ -39,6 +39,13 @@
 // of super-block q of row 16 u + j, unchanged.  Size 1024 U P + U K bytes.
 // The four lanes of row j read the same 16 bytes; the epilogue takes its
 // sub-block's scale and min from them.
+//
+// IQ4_XS has the same 4-bit indices in the same nibble order (decoded
+// through the IQ4_NL table into signed int8 operands), so its codes plane is
+// the same too; its 8-byte super-block headers (d, H, L) form the second
+// plane: U K/256 blocks of 128 bytes, block (u, q) at byte 1024 U P +
+// 128 (u K/256 + q), whose bytes 8 j .. 8 j + 7 are the header of
+// super-block q of row 16 u + j, unchanged.  Size 1024 U P + U K / 2 bytes.
 // Bytes per call: 1024 U P + 512 U V weights + M K (1 + 4 / 32) activations
 // + 4 M N out.
 #include <type_traits>
@@ -48,6 +55,11 @@
 #include "q4_mfma.h"
 
 namespace skinny {
+
+// Weight formats of the packed kernel (as in the canonical matrix-core
+// kernel of mmvq_q4_0.hip).
+constexpr int kPkQ40 = 0, kPkQ4K = 1, kPkIQ4 = 2;
+struct PkNoRegs {};
 
 // Workgroup: WR x KS waves; WR waves own different tiles (T each) and share
 // one K slice's activation chunks, KS slices split K.  A chunk is S steps.
@@ -81,22 +93,25 @@ struct Cfg {
 };
 }  // namespace q4p
 
-template <int T, int S, int APW, bool KQ>
+template <int T, int S, int APW, int FMT>
 struct Q4pChunk {
   uint4_t c[T][S / 2];                                      // codes, two steps per load
   std::conditional_t<S == 8, uint4_t, uint2_t> s[T];        // Q4_0: 2 scale bytes per step
-  uint4_t h[KQ ? T : 1][KQ ? S / 4 : 1];                    // Q4_K: a header per 4 steps
+  // Q4_K: a 16-byte header per 4 steps; IQ4_XS: an 8-byte one
+  std::conditional_t<FMT == kPkIQ4, uint2_t, uint4_t> h[FMT != kPkQ40 ? T : 1]
+                                                        [FMT != kPkQ40 ? S / 4 : 1];
   uint4_t a[APW];                                           // activation pieces
 };
 
 // (No __restrict__ on the inputs: the issue fences below must be able to
 // order their loads.)
-template <int T, int WR, int KS, int S, int MP, bool KQ = false>
+template <int T, int WR, int KS, int S, int MP, int FMT = kPkQ40>
 __global__ __launch_bounds__(64 * WR * KS) void mmvq_q4_0_packed_kernel(
     const uint8_t *wp, int N, int K, const int8_t *a_qs, const uint16_t *a_d,
     const uint16_t *a_s, int M, float *y) {
   using C = q4p::Cfg<T, WR, KS, S, MP>;
-  using R = Q4pChunk<T, S, C::kApw, KQ>;
+  using R = Q4pChunk<T, S, C::kApw, FMT>;
+  const std::conditional_t<FMT == kPkIQ4, Iq4Regs, PkNoRegs> kr{};
   extern __shared__ uint4_t smem4[];
   uint8_t *smem = reinterpret_cast<uint8_t *>(smem4);
   const int lane = threadIdx.x & 63;
@@ -119,8 +134,12 @@ __global__ __launch_bounds__(64 * WR * KS) void mmvq_q4_0_packed_kernel(
   for (int t = 0; t < T; ++t) {
     const size_t u = (size_t)min(u0 + t, U - 1);
     cp[t] = wp + u * P * 1024 + 16 * lane;
-    if constexpr (KQ) sp[t] = wp + (size_t)U * P * 1024 + u * (size_t)(K >> 8) * 256 + 16 * j;
-    else sp[t] = wp + (size_t)U * P * 1024 + u * V * 512 + 256 * hb + 16 * j;
+    if constexpr (FMT == kPkQ4K)
+      sp[t] = wp + (size_t)U * P * 1024 + u * (size_t)(K >> 8) * 256 + 16 * j;
+    else if constexpr (FMT == kPkIQ4)
+      sp[t] = wp + (size_t)U * P * 1024 + u * (size_t)(K >> 8) * 128 + 8 * j;
+    else
+      sp[t] = wp + (size_t)U * P * 1024 + u * V * 512 + 256 * hb + 16 * j;
   }
   // activation pieces of this wave: p = wr, wr + WR, ... (the last repeated);
   // pieces 0 .. kAi-1 are code blocks, piece kAi the scales (lanes [0, kNd)
@@ -155,9 +174,12 @@ __global__ __launch_bounds__(64 * WR * KS) void mmvq_q4_0_packed_kernel(
     const int s0 = c * S;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      if constexpr (KQ) {
+      if constexpr (FMT == kPkQ4K) {
 #pragma unroll
         for (int q = 0; q < S / 4; ++q) rg.h[t][q] = load16(sp[t] + (size_t)(c * (S / 4) + q) * 256);
+      } else if constexpr (FMT == kPkIQ4) {
+#pragma unroll
+        for (int q = 0; q < S / 4; ++q) rg.h[t][q] = load8(sp[t] + (size_t)(c * (S / 4) + q) * 128);
       } else {
         const uint8_t *p = sp[t] + (size_t)(s0 >> 3) * 512 + 2 * (s0 & 7);
         if constexpr (S == 8) rg.s[t] = load16(p);
@@ -215,7 +237,10 @@ __global__ __launch_bounds__(64 * WR * KS) void mmvq_q4_0_packed_kernel(
       for (int t = 0; t < T; ++t) {
         const uint4_t &w2 = rg.c[t][st >> 1];
         const uint2_t wq = {w2[2 * (st & 1)], w2[2 * (st & 1) + 1]};
-        isum[st][t] = q4_mfma_isum(wq, aop);
+        if constexpr (FMT == kPkIQ4)
+          isum[st][t] = iq4_mfma_isum(wq, aop, kr);
+        else
+          isum[st][t] = q4_mfma_isum(wq, aop);
       }
     }
 #pragma unroll
@@ -225,7 +250,11 @@ __global__ __launch_bounds__(64 * WR * KS) void mmvq_q4_0_packed_kernel(
       const float4_t sa = asf[0], sb = asf[1];
 #pragma unroll
       for (int t = 0; t < T; ++t) {
-        if constexpr (KQ) {
+        if constexpr (FMT == kPkIQ4) {
+          // sub-block 2 (st % 4) + hb of the step's super-block
+          iq4_mfma_epilogue(isum[st][t], iq4_scale(rg.h[t][st >> 2], 2 * (st & 3) + hb), sa, sb,
+                            acc[t]);
+        } else if constexpr (FMT == kPkQ4K) {
           // sub-block sj = 2 (st % 4) + hb of the step's super-block: scale
           // byte 4 + sj, min high bits in nibble hb of byte 12 + st % 4
           const uint4_t &h = rg.h[t][st >> 2];
@@ -306,18 +335,18 @@ __global__ __launch_bounds__(64 * WR * KS) void mmvq_q4_0_packed_kernel(
   }
 }
 
-template <int T, int WR, int KS, int S, int MP, bool KQ = false>
+template <int T, int WR, int KS, int S, int MP, int FMT = kPkQ40>
 static hipError_t launch_q4p_cfg(const uint8_t *wp, int N, int K, const int8_t *a_qs,
                                  const uint16_t *a_d, const uint16_t *a_s, int M, float *y,
                                  hipStream_t stream) {
   using C = q4p::Cfg<T, WR, KS, S, MP>;
   if (K % (64 * S) != 0) return hipErrorInvalidValue;   // chunks must tile K
   const hipError_t lds_ok =
-      allow_lds((const void *)mmvq_q4_0_packed_kernel<T, WR, KS, S, MP, KQ>, C::kLds);
+      allow_lds((const void *)mmvq_q4_0_packed_kernel<T, WR, KS, S, MP, FMT>, C::kLds);
   if (lds_ok != hipSuccess) return lds_ok;
   const int tiles = (N + 15) / 16;
   const int blocks = (tiles + T * WR - 1) / (T * WR);
-  hipLaunchKernelGGL((mmvq_q4_0_packed_kernel<T, WR, KS, S, MP, KQ>), dim3(blocks),
+  hipLaunchKernelGGL((mmvq_q4_0_packed_kernel<T, WR, KS, S, MP, FMT>), dim3(blocks),
                      dim3(64 * C::kWaves), C::kLds, stream, wp, N, K, a_qs, a_d, a_s, M, y);
   return hipGetLastError();
 }
@@ -331,19 +360,20 @@ static hipError_t launch_q4p_cfg(const uint8_t *wp, int N, int K, const int8_t *
 // K split of 2 (with sharing at M >= 5); narrower ones a split of 4 (two
 // tiles per wave at M >= 5, and at M = 3, 4 on rows of 8192 or more); up to
 // 256 tiles a split of 8.
-template <int MP, bool KQ>
+template <int MP, int FMT>
 static hipError_t launch_q4p_mp(const uint8_t *wp, int N, int K, const int8_t *a_qs,
                                 const uint16_t *a_d, const uint16_t *a_s, int M, float *y,
                                 hipStream_t stream) {
   const int tiles = (N + 15) / 16;
   const bool s8 = K % 512 == 0;
 #define SKINNY_Q4P(T, WR, KS, S) \
-  return launch_q4p_cfg<T, WR, KS, S, MP, KQ>(wp, N, K, a_qs, a_d, a_s, M, y, stream)
-  if constexpr (KQ) {
+  return launch_q4p_cfg<T, WR, KS, S, MP, FMT>(wp, N, K, a_qs, a_d, a_s, M, y, stream)
+  if constexpr (FMT != kPkQ40) {
     // Q4_K: its per-step header decode makes chunks of 4 steps pay at every
     // width (measured on the Qwen3-8B projections and six more matrices at
     // M = 1, 4, 5, 8: 4096 x 24576 at M = 8 15.2 -> 14.1 us against the
-    // Q4_0 rows, 4096 x 16384 11.7 -> 10.7 us)
+    // Q4_0 rows, 4096 x 16384 11.7 -> 10.7 us); IQ4_XS, with its table
+    // decode per step, takes the same rows
     if (tiles >= 1100) SKINNY_Q4P(1, 2, 2, 4);
     if (tiles >= 800) SKINNY_Q4P(1, 2, 4, 4);
     if (tiles > 256) SKINNY_Q4P(1, 1, 4, 4);
@@ -376,33 +406,48 @@ static hipError_t launch_q4p_mp(const uint8_t *wp, int N, int K, const int8_t *a
 hipError_t launch_mmvq_q4_0_packed(const uint8_t *wp, int N, int K, const int8_t *a_qs,
                                    const uint16_t *a_d, const uint16_t *a_s, int M, float *y,
                                    hipStream_t stream) {
-  if (M <= 1) return launch_q4p_mp<1, false>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
-  if (M <= 2) return launch_q4p_mp<2, false>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
-  if (M <= 4) return launch_q4p_mp<4, false>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
-  return launch_q4p_mp<8, false>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
+  if (M <= 1) return launch_q4p_mp<1, kPkQ40>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
+  if (M <= 2) return launch_q4p_mp<2, kPkQ40>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
+  if (M <= 4) return launch_q4p_mp<4, kPkQ40>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
+  return launch_q4p_mp<8, kPkQ40>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
 }
 
 hipError_t launch_mmvq_q4_k_packed(const uint8_t *wp, int N, int K, const int8_t *a_qs,
                                    const uint16_t *a_d, const uint16_t *a_s, int M, float *y,
                                    hipStream_t stream) {
-  if (M <= 1) return launch_q4p_mp<1, true>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
-  if (M <= 2) return launch_q4p_mp<2, true>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
-  if (M <= 4) return launch_q4p_mp<4, true>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
-  return launch_q4p_mp<8, true>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
+  if (M <= 1) return launch_q4p_mp<1, kPkQ4K>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
+  if (M <= 2) return launch_q4p_mp<2, kPkQ4K>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
+  if (M <= 4) return launch_q4p_mp<4, kPkQ4K>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
+  return launch_q4p_mp<8, kPkQ4K>(wp, N, K, a_qs, a_d, a_s, M, y, stream);
+}
+
+// IQ4_XS on the packed kernel: the Q8_1 sum term is not used, so d8 stands
+// in for it in the staging.
+hipError_t launch_mmvq_iq4_xs_packed(const uint8_t *wp, int N, int K, const int8_t *a_qs,
+                                     const uint16_t *a_d, int M, float *y, hipStream_t stream) {
+  if (M <= 1) return launch_q4p_mp<1, kPkIQ4>(wp, N, K, a_qs, a_d, a_d, M, y, stream);
+  if (M <= 2) return launch_q4p_mp<2, kPkIQ4>(wp, N, K, a_qs, a_d, a_d, M, y, stream);
+  if (M <= 4) return launch_q4p_mp<4, kPkIQ4>(wp, N, K, a_qs, a_d, a_d, M, y, stream);
+  return launch_q4p_mp<8, kPkIQ4>(wp, N, K, a_qs, a_d, a_d, M, y, stream);
 }
 
 // ------------------------------------------------------------------ prepack
 
 // One thread per 16 packed bytes, grid-stride over both planes: codes
 // pieces first (a lane's two 8-byte halves), then scale pieces (Q4_0: the 16
-// bytes at 256 h + 16 j of a scale block; Q4_K: one row's header).
-template <bool KQ>
+// bytes at 256 h + 16 j of a scale block; Q4_K: one row's header; IQ4_XS:
+// the headers of two consecutive rows).
+constexpr size_t q4p_scale_pieces(int FMT, size_t U, size_t V, size_t nsb) {
+  return FMT == kPkQ4K ? U * nsb * 16 : FMT == kPkIQ4 ? U * nsb * 8 : U * V * 32;
+}
+
+template <int FMT>
 __global__ __launch_bounds__(256) void prepack_q4_0_kernel(
     const uint8_t *__restrict__ w_qs, const uint8_t *__restrict__ scl, int N, int K,
     uint8_t *__restrict__ wp) {
   const size_t U = (size_t)(N + 15) / 16, P = (size_t)K / 128, V = ((size_t)K + 511) / 512;
   const size_t nb = (size_t)K / 32, nsb = (size_t)K / 256;
-  const size_t nc = U * P * 64, total = nc + (KQ ? U * nsb * 16 : U * V * 32);
+  const size_t nc = U * P * 64, total = nc + q4p_scale_pieces(FMT, U, V, nsb);
   for (size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
        q += (size_t)gridDim.x * blockDim.x) {
     uint4_t v = uint4_t{0u, 0u, 0u, 0u};
@@ -416,10 +461,23 @@ __global__ __launch_bounds__(256) void prepack_q4_0_kernel(
         const uint2_t e1 = load8(src + 16 * (4 * p + 2 + h));
         v = uint4_t{e0.x, e0.y, e1.x, e1.y};
       }
-    } else if constexpr (KQ) {
+    } else if constexpr (FMT == kPkQ4K) {
       const size_t r = q - nc, blk = r >> 4, u = blk / nsb, sb = blk - u * nsb;
       const size_t row = 16 * u + (r & 15);
       if (row < (size_t)N) v = load16(scl + row * (nsb * 16) + 16 * sb);
+    } else if constexpr (FMT == kPkIQ4) {
+      const size_t r = q - nc, blk = r >> 3, u = blk / nsb, sb = blk - u * nsb;
+      const size_t row = 16 * u + 2 * (r & 7);
+      if (row < (size_t)N) {
+        const uint2_t h0 = load8(scl + row * (nsb * 8) + 8 * sb);
+        v[0] = h0.x;
+        v[1] = h0.y;
+      }
+      if (row + 1 < (size_t)N) {
+        const uint2_t h1 = load8(scl + (row + 1) * (nsb * 8) + 8 * sb);
+        v[2] = h1.x;
+        v[3] = h1.y;
+      }
     } else {
       const uint16_t *w_d = reinterpret_cast<const uint16_t *>(scl);
       const size_t r = q - nc, blk = r >> 5, u = blk / V, vb = blk - u * V;
@@ -437,26 +495,31 @@ __global__ __launch_bounds__(256) void prepack_q4_0_kernel(
   }
 }
 
-template <bool KQ>
+template <int FMT>
 static hipError_t launch_prepack(const uint8_t *w_qs, const uint8_t *scl, int N, int K,
                                  uint8_t *wp, hipStream_t stream) {
   const size_t U = (size_t)(N + 15) / 16, P = (size_t)K / 128, V = ((size_t)K + 511) / 512;
-  const size_t total = U * P * 64 + (KQ ? U * ((size_t)K / 256) * 16 : U * V * 32);
+  const size_t total = U * P * 64 + q4p_scale_pieces(FMT, U, V, (size_t)K / 256);
   size_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(prepack_q4_0_kernel<KQ>, dim3((unsigned)blocks), dim3(256), 0, stream, w_qs,
+  hipLaunchKernelGGL(prepack_q4_0_kernel<FMT>, dim3((unsigned)blocks), dim3(256), 0, stream, w_qs,
                      scl, N, K, wp);
   return hipGetLastError();
 }
 
 hipError_t launch_prepack_q4_0(const uint8_t *w_qs, const uint16_t *w_d, int N, int K,
                                uint8_t *wp, hipStream_t stream) {
-  return launch_prepack<false>(w_qs, reinterpret_cast<const uint8_t *>(w_d), N, K, wp, stream);
+  return launch_prepack<kPkQ40>(w_qs, reinterpret_cast<const uint8_t *>(w_d), N, K, wp, stream);
 }
 
 hipError_t launch_prepack_q4_k(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
                                uint8_t *wp, hipStream_t stream) {
-  return launch_prepack<true>(w_qs, w_hdr, N, K, wp, stream);
+  return launch_prepack<kPkQ4K>(w_qs, w_hdr, N, K, wp, stream);
+}
+
+hipError_t launch_prepack_iq4_xs(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
+                                 uint8_t *wp, hipStream_t stream) {
+  return launch_prepack<kPkIQ4>(w_qs, w_hdr, N, K, wp, stream);
 }
 
 }  // namespace skinny

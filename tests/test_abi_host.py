@@ -39,7 +39,9 @@ def test_header_declares_the_entry_points():
                                            "prepack_q4_0", "mmvq_q4_0_packed", "prepack_fp8_size",
                                            "prepack_fp8", "gemv_fp8_w8a16_packed", "prepack_q4_k_size",
                                            "prepack_q4_k", "mmvq_q4_k_packed", "prepack_q6_k_size",
-                                           "prepack_q6_k", "mmvq_q6_k_packed", "mmvq_iq4_xs"])
+                                           "prepack_q6_k", "mmvq_q6_k_packed", "mmvq_iq4_xs",
+                                           "prepack_iq4_xs_size", "prepack_iq4_xs",
+                                           "mmvq_iq4_xs_packed"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -401,6 +403,38 @@ def test_fp8_packed_validation(L):
 
 def q4kp(L, w=A, N=64, K=256, aq=A, ad=A, as_=A, M=1, y=A):
     return L.mmvq_q4_k_packed(V(w), N, K, V(aq), V(ad), V(as_), M, V(y), None)
+
+
+def iq4p(L, w=A, N=64, K=256, aq=A, ad=A, M=1, y=A):
+    return L.mmvq_iq4_xs_packed(V(w), N, K, V(aq), V(ad), M, V(y), None)
+
+
+def test_iq4_xs_packed_validation(L):
+    import skinny_gemm_amd
+
+    n = ctypes.c_size_t(0)
+    for N, K, want in ((1, 256, 1024 * 2 + 128), (17, 512, 2 * (1024 * 4 + 256)), (0, 256, 0)):
+        assert L.prepack_iq4_xs_size(N, K, ctypes.byref(n)) == 0
+        assert n.value == want
+        assert skinny_gemm_amd.prepack_iq4_xs_size(N, K) == want
+    # whole tiles: exactly the canonical bytes (codes + 8-byte headers)
+    assert skinny_gemm_amd.prepack_iq4_xs_size(4096, 12288) == 4096 * 12288 * 17 // 32
+    assert L.prepack_iq4_xs_size(16, 128, ctypes.byref(n)) == -2
+    assert L.prepack_iq4_xs_size(16, 256, None) == -1
+    assert iq4p(L, M=9) == -4
+    assert iq4p(L, M=8, y=0) == -1
+    for K in (0, 128, 384):
+        assert iq4p(L, K=K) == -2, K
+        assert L.prepack_iq4_xs(V(A), V(A), 64, K, V(A), None) == -2, K
+    for kw in ("w", "aq", "ad", "y"):
+        assert iq4p(L, **{kw: 0}) == -1, kw
+    assert L.prepack_iq4_xs(V(0), V(A), 64, 256, V(A), None) == -1
+    assert L.prepack_iq4_xs(V(A), V(A + 8), 64, 256, V(A), None) == -3
+    assert L.prepack_iq4_xs(V(A), V(A), 64, 256, V(A + 8), None) == -3
+    for kw, off in (("w", 8), ("aq", 8), ("ad", 8), ("y", 2)):
+        assert iq4p(L, **{kw: A + off}) == -3, kw
+    assert iq4p(L, w=0, aq=0, ad=0, y=0, M=0) == 0
+    assert L.prepack_iq4_xs(V(0), V(0), 0, 256, V(0), None) == 0
 
 
 def test_q4_k_packed_validation(L):

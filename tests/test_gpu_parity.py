@@ -891,6 +891,79 @@ def test_mmvq_iq4_xs_device_quantize_and_zero_sizes():
     torch.cuda.synchronize()
 
 
+# ------------------------------------------------------------------ IQ4_XS, pre-permuted
+
+def run_iq4_xs_packed(w_qs, w_hdr, a_qs, a_d):
+    import skinny_gemm_amd as sk
+
+    N, K = w_qs.shape[0], 2 * w_qs.shape[1]
+    wp = sk.prepack_iq4_xs(dev(w_qs), dev(w_hdr))
+    return host(sk.mmvq_iq4_xs_packed(wp, N, K, dev(a_qs), dev(a_d)))
+
+
+@pytest.mark.parametrize("N,K", [(40, 2304), (16, 256), (3, 768), (17, 512)])
+def test_prepack_iq4_xs_layout(N, K):
+    # code and header bytes carry 16-bit labels (index + 1) sent as two byte
+    # planes: codes as in the Q4_0 layout, each row's 8-byte headers in
+    # tile-major blocks of 128 bytes, zeros in the padding
+    import skinny_gemm_amd as sk
+
+    nc, nh = N * K // 2, N * K // 32
+    label = np.arange(1, nc + nh + 1, dtype=np.int64)
+    assert label[-1] < 1 << 16
+    U, P, SB = (N + 15) // 16, K // 128, K // 256
+    got = np.zeros(sk.prepack_iq4_xs_size(N, K), np.int64)
+    for shift in (0, 8):
+        plane = ((label >> shift) & 255).astype(np.uint8)
+        w_qs = plane[:nc].reshape(N, K // 2)
+        w_hdr = plane[nc:].reshape(N, SB, 8)
+        got |= host(sk.prepack_iq4_xs(dev(w_qs), dev(w_hdr))).astype(np.int64) << shift
+    want_codes, _ = q4_packed_layout_source(N, K)
+    assert np.array_equal(got[:1024 * U * P] - 1, want_codes)
+    hdr = np.full(128 * U * SB, -1, np.int64)
+    for u in range(U):
+        for q in range(SB):
+            for j in range(16):
+                n = 16 * u + j
+                if n < N:
+                    at = 128 * (u * SB + q) + 8 * j
+                    hdr[at:at + 8] = nc + n * (K // 32) + 8 * q + np.arange(8)
+    assert np.array_equal(got[1024 * U * P:] - 1, hdr)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("N,K", Q4P_SHAPES)
+def test_mmvq_iq4_xs_packed_vs_oracle(M, N, K):
+    w_qs, w_hdr = inputs.iq4_xs_weights(N, K, 23 * N + K)
+    x = inputs.normal_f32(M, K, 29 * M + K)
+    a_qs, a_d, _ = oracle.quantize_q8_1(x)
+    y = run_iq4_xs_packed(w_qs, w_hdr, a_qs, a_d)
+    ref = oracle.mmvq_iq4_xs(w_qs, w_hdr, a_qs, a_d)
+    check_f32(y, ref, iq4_xs_mag(w_qs, w_hdr, a_qs, a_d), K,
+              "iq4_xs packed M=%d N=%d K=%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M", [1, 3, 5, 8])
+@pytest.mark.parametrize("N,K", [(30000, 1024), (25000, 768), (16393, 4096), (16000, 1280),
+                                 (9000, 1280), (5000, 8192), (3000, 4096), (5000, 1280),
+                                 (40, 768)])
+def test_mmvq_iq4_xs_packed_integer_gate_bit_exact(M, N, K):
+    # d = 1, ls = 33, integer activations with d8 = 1, as for the canonical
+    # layout: exact in any summation order
+    x = inputs.q8_1_unit_scale_source(M, K, 190 + M + K, spread=60 if K <= 4096 else 6)
+    a_qs, a_d, _ = oracle.quantize_q8_1(x)
+    w_qs, w_hdr = inputs.iq4_xs_weights(N, K, 191 + N)
+    w_hdr[:, :, 0:2] = np.array([0x3C00], np.uint16).view(np.uint8)
+    w_hdr[:, :, 2:4] = 0xAA
+    w_hdr[:, :, 4:8] = 0x11
+    W = np.abs(iq4_table()[unpack_q4_0(w_qs)]).astype(np.float64)
+    assert (np.abs(a_qs.astype(np.float64)) @ W.T).max() < 2 ** 24
+    y = run_iq4_xs_packed(w_qs, w_hdr, a_qs, a_d)
+    ref = oracle.mmvq_iq4_xs(w_qs, w_hdr, a_qs, a_d)
+    assert np.array_equal(ref, np.round(ref))
+    assert np.array_equal(y.astype(np.float64), ref), "M=%d N=%d K=%d" % (M, N, K)
+
+
 # ------------------------------------------------------------------ NVFP4
 
 def run_nvfp4(codes, scales, g, x):
@@ -1578,6 +1651,8 @@ def test_iq4_xs_full_sizes_sampled(M):
         ref = oracle.mmvq_iq4_xs(w_qs[rows], w_hdr[rows], a_qs, a_d)
         mag = iq4_xs_mag(w_qs[rows], w_hdr[rows], a_qs, a_d)
         check_f32(y[:, rows], ref, mag, K, "iq4_xs full M=%d %dx%d" % (M, N, K))
+        y = run_iq4_xs_packed(w_qs, w_hdr, a_qs, a_d)
+        check_f32(y[:, rows], ref, mag, K, "iq4_xs packed full M=%d %dx%d" % (M, N, K))
 
 
 @pytest.mark.parametrize("M", [1, 2])
@@ -1760,6 +1835,7 @@ def test_graph_replays_match_eager():
     p_q4, p_q4k = sk.prepack_q4_0(w_qs, w_d), sk.prepack_q4_k(k_qs, k_hdr)
     p_nv, p_f8 = sk.prepack_nvfp4(codes, scales), sk.prepack_fp8(w8)
     p_q6k = sk.prepack_q6_k(ql, qh, sc, dd)
+    p_iq4 = sk.prepack_iq4_xs(i_qs, i_hdr)
     outs = []
 
     def run():
@@ -1782,6 +1858,7 @@ def test_graph_replays_match_eager():
             outs.append(sk.mmvq_q4_0_packed(p_q4, N, K, *q8[M]))
             outs.append(sk.mmvq_q4_k_packed(p_q4k, N, K, *q8[M]))
             outs.append(sk.mmvq_q6_k_packed(p_q6k, N, K, q8[M][0], q8[M][1]))
+            outs.append(sk.mmvq_iq4_xs_packed(p_iq4, N, K, q8[M][0], q8[M][1]))
         for M in (1, 2, 4, 8):
             outs.append(sk.gemv_nvfp4_w4a16_packed(p_nv, N, K, 1.0, xh[M]))
         for M in (1, 2, 4, 8, 32):
