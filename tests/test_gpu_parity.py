@@ -1562,6 +1562,46 @@ def test_mmvq_iq4_xs_random_shapes(M, N, K):
               iq4_xs_mag(w_qs, w_hdr, a_qs, a_d), K, "iq4_xs M=%d N=%d K=%d" % (M, N, K))
 
 
+@pytest.mark.parametrize("M,N,K", random_shapes(108, 24, 256, 16384, 8))
+def test_packed_q4_family_random_shapes(M, N, K):
+    # Q4_0, Q4_K, Q6_K and IQ4_XS through their pre-permuted copies (K % 256
+    # == 0), against the oracle on the canonical weights
+    x = inputs.normal_f32(M, K, 19 * M + K)
+    a_qs, a_d, a_s = oracle.quantize_q8_1(x)
+    w_qs, w_d = inputs.q4_0_weights(N, K, 2 * N + K)
+    check_f32(run_q4_packed(w_qs, w_d, a_qs, a_d, a_s), oracle.mmvq_q4_0(w_qs, w_d, a_qs, a_d, a_s),
+              q4_mag(w_qs, w_d, a_qs, a_d, a_s), K, "q4_0 packed M=%d N=%d K=%d" % (M, N, K))
+    k_qs, k_hdr = inputs.q4_k_weights(N, K, 3 * N + K)
+    check_f32(run_q4_k_packed(k_qs, k_hdr, a_qs, a_d, a_s),
+              oracle.mmvq_q4_k(k_qs, k_hdr, a_qs, a_d, a_s),
+              q4_k_mag(k_qs, k_hdr, a_qs, a_d, a_s), K, "q4_k packed M=%d N=%d K=%d" % (M, N, K))
+    ql, qh, sc, d6 = inputs.q6_k_weights(N, K, 5 * N + K)
+    check_f32(run_q6_k_packed(ql, qh, sc, d6, a_qs, a_d),
+              oracle.mmvq_q6_k(ql, qh, sc, d6, a_qs, a_d),
+              q6_k_mag(ql, qh, sc, d6, a_qs, a_d), K, "q6_k packed M=%d N=%d K=%d" % (M, N, K))
+    i_qs, i_hdr = inputs.iq4_xs_weights(N, K, 7 * N + K)
+    check_f32(run_iq4_xs_packed(i_qs, i_hdr, a_qs, a_d), oracle.mmvq_iq4_xs(i_qs, i_hdr, a_qs, a_d),
+              iq4_xs_mag(i_qs, i_hdr, a_qs, a_d), K, "iq4_xs packed M=%d N=%d K=%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M,N,K", random_shapes(110, 24, 256, 20480, 16))
+def test_packed_nvfp4_random_shapes(M, N, K):
+    codes, scales, g = inputs.nvfp4_weights(N, K, 11 * N + K)
+    x = inputs.normal_f16_bits(M, K, 13 * M + K)
+    y_acc, _ = oracle.gemv_nvfp4_w4a16(codes, scales, g, x)
+    check_f16(run_nvfp4_packed(codes, scales, g, x), y_acc, nvfp4_mag(codes, scales, g, x), K,
+              "nvfp4 packed M=%d N=%d K=%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M,N,K", random_shapes(111, 24, 256, 20480, 96))
+def test_packed_fp8_random_shapes(M, N, K):
+    w, cs = inputs.fp8_weights(N, K, 17 * N + K)
+    x = inputs.normal_f16_bits(M, K, 19 * M + K)
+    y_acc, _ = oracle.gemv_fp8_w8a16(w, cs, x)
+    check_f16(run_fp8_packed(w, cs, x), y_acc, fp8_mag(w, cs, x), K,
+              "fp8 packed M=%d N=%d K=%d" % (M, N, K))
+
+
 # ------------------------------------------------------------------ full sizes (sampled rows)
 
 LLAMA_Q4 = [(12288, 4096), (4096, 4096), (22016, 4096), (4096, 11008), (32000, 4096)]
