@@ -30,7 +30,7 @@ hipError_t launch_mmvq_q4_k_mfma(const uint8_t *w_qs, const uint8_t *w_hdr, int 
                                  const int8_t *a_qs, const uint16_t *a_d, const uint16_t *a_s,
                                  int M, float *y, hipStream_t stream);
 
-// IQ4_XS on the Q4_0 matrix-core kernel (3 <= M <= 8, K % 512 == 0).
+// IQ4_XS on the Q4_0 matrix-core kernel (3 <= M <= 8, K % 256 == 0).
 hipError_t launch_mmvq_iq4_xs_mfma(const uint8_t *w_qs, const uint8_t *w_hdr, int N, int K,
                                    const int8_t *a_qs, const uint16_t *a_d, int M, float *y,
                                    hipStream_t stream);

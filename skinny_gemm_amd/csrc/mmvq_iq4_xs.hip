@@ -339,10 +339,11 @@ hipError_t launch_mmvq_iq4_xs(const uint8_t *w_qs, const uint8_t *w_hdr, int N, 
                               hipStream_t stream) {
   // From M = 6 large matrices take the matrix cores (the Q4_0 kernel with
   // table-decoded operands; measured on MI355X at M = 8: 4096 x 24576
-  // 22.2 -> 18.8 us, 5120 x 13824 21.9 -> 15.9 us, 13824 x 5120 27.0 -> 20.7
-  // us, 8192 x 8192 16.9 -> 14.9 us; up to 48M weights the vector and
-  // staged kernels stay ahead at every M, 4096 x 6144 7.8 against 9.0 us)
-  if (M >= 6 && K % 512 == 0 && (long long)N * K >= (60ll << 20))
+  // 22.2 -> 18.6 us, 5120 x 13824 21.9 -> 15.4 us, 13824 x 5120 27.0 -> 20.1
+  // us, 8192 x 8192 16.9 -> 14.4 us, 12288 x 4096 12.5 -> 11.9 us; below 48M
+  // weights the vector and staged kernels stay ahead at every M, 4096 x 6144
+  // 7.9 against 8.3 us)
+  if (M >= 6 && (long long)N * K >= (48ll << 20))
     return launch_mmvq_iq4_xs_mfma(w_qs, w_hdr, N, K, a_qs, a_d, M, y, stream);
   // From M = 3 the staged kernel where the activation re-reads weigh most:
   // long rows (12288 x 4096 at M = 4: 10.2 -> 9.4 us, at M = 8: 15.7 -> 12.6

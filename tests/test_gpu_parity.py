@@ -811,11 +811,11 @@ def run_iq4_xs(w_qs, w_hdr, a_qs, a_d):
     return host(sk.mmvq_iq4_xs(dev(w_qs), dev(w_hdr), dev(a_qs), dev(a_d)))
 
 
-# KQ_SHAPES, and matrices of 60M+ weights that take the matrix cores from
-# M = 6 (four-way split; two-way split; two waves sharing activations), and
-# one whose K is not a multiple of 512 and stays on the vector kernel
+# KQ_SHAPES, and matrices of 48M+ weights that take the matrix cores from
+# M = 6 (four-way split; two-way split; two waves sharing activations; an
+# eight-way split at 256 tiles; K % 512 == 256)
 IQ4_SHAPES = KQ_SHAPES + [(5000 + 3, 12800), (16384 + 9, 4096), (20000 + 3, 4096),
-                          (16000, 4352)]
+                          (4096, 12288), (16000, 4352)]
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
@@ -848,7 +848,10 @@ IQ4_GATE = [
     (6, 5003, 12800), (8, 5003, 12800),         # matrix cores: four-way K split
     (7, 16393, 4096),                           # ... two-way split
     (6, 20003, 4096), (8, 20003, 4096),         # ... two waves share activations
-    (8, 16000, 4352),                           # vector kernel (K % 512 != 0)
+    (6, 4096, 12288),                           # ... eight-way split (256 tiles)
+    (8, 4100, 12288),                           # ... four-way split, ragged tile
+    (8, 16000, 4352),                           # ... K % 512 == 256
+    (8, 4000, 12288),                           # staged kernel just below 48M weights
 ]
 
 
@@ -1547,10 +1550,10 @@ def test_k_quants_random_shapes(M, N, K):
 
 
 def iq4_random_big():
-    # matrices of 60M+ weights at M >= 6 (the matrix-core route), drawn the
+    # matrices of 48M+ weights at M >= 6 (the matrix-core route), drawn the
     # same way with a larger size budget
     return [s for s in random_shapes(107, 400, 512, 16384, 8, nk_max=1.2e8, mnk_max=1e9)
-            if s[0] >= 6 and s[1] * s[2] >= 63e6]
+            if s[0] >= 6 and s[1] * s[2] >= 51e6]
 
 
 @pytest.mark.parametrize("M,N,K", random_shapes(106, 32, 256, 16384, 8) + iq4_random_big())
