@@ -278,13 +278,23 @@ static hipError_t launch_iq4_m(const uint8_t *w_qs, const uint8_t *w_hdr, int N,
   const int per_lane = ((K >> 5) + kWave - 1) / kWave;
 #define SKINNY_IQ4(R, U) return launch_iq4_mru<M, R, U>(w_qs, w_hdr, N, K, a_qs, a_d, y, stream)
   if constexpr (M == 1) {
-    if (per_lane <= 2) {
-      if (N >= 16384) SKINNY_IQ4(2, 1);
-      SKINNY_IQ4(2, 2);
+    // one round of exactly the lane's share of the row: a padding slot in
+    // the round would cost a block's decode for nothing (K = 5120 and 13824
+    // had a quarter and an eighth of their rounds padded with rounds of 4
+    // and 8)
+    switch (per_lane) {
+      case 1:
+      case 2:
+        if (N >= 16384) SKINNY_IQ4(2, 1);
+        SKINNY_IQ4(2, 2);
+      case 3: SKINNY_IQ4(2, 3);
+      case 4: SKINNY_IQ4(2, 4);
+      case 5: SKINNY_IQ4(2, 5);
+      case 6: SKINNY_IQ4(2, 6);
+      case 7: SKINNY_IQ4(2, 7);
+      case 8: SKINNY_IQ4(2, 8);
+      default: SKINNY_IQ4(2, 6);
     }
-    if (per_lane <= 4) SKINNY_IQ4(2, 4);
-    if (per_lane <= 6 || per_lane > 8) SKINNY_IQ4(2, 6);
-    SKINNY_IQ4(2, 8);
   } else if constexpr (M == 2) {
     if (per_lane <= 2 && N >= 16384) SKINNY_IQ4(4, 2);
     if (per_lane <= 6) SKINNY_IQ4(2, 2);

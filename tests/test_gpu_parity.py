@@ -835,7 +835,9 @@ IQ4_GATE = [
     (1, 300, 4096), (2, 300, 4096),             # vector kernel, two blocks per lane
     (1, 16400, 4096),                           # ... one block per round (M = 1, wide)
     (2, 16400, 4096),                           # ... four rows per wave (M = 2, wide)
-    (1, 300, 8192), (1, 300, 12288),            # ... four and six blocks per lane
+    (1, 300, 5120), (1, 300, 8192),             # ... three and four blocks per lane
+    (1, 300, 10240), (1, 300, 12288),           # ... five and six
+    (1, 301, 13824),                            # ... seven
     (2, 300, 12288),                            # ... rounds of two blocks (M = 2)
     (1, 300, 16384), (2, 300, 16384),           # ... eight blocks per lane
     (1, 300, 20480), (2, 300, 20480),           # ... rounds of six blocks
