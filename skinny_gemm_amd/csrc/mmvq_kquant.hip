@@ -557,8 +557,11 @@ static hipError_t launch_q6k_mru(const uint8_t *w_ql, const uint8_t *w_qh, const
 
 // Launch shapes measured on MI355X over the Qwen3-8B projections (K 4096 and
 // 12288, N 4096 to 24576) at M = 1, 2, 4, 8.  At M <= 2 a lane takes its
-// whole share of a row in one round up to 8 blocks (K <= 16384; longer rows
-// take rounds of 6), two rows per wave, four on wide matrices.  Wider M takes one or two blocks per
+// whole share of a row in one round of exactly that many blocks up to 8
+// (K <= 16384; longer rows take rounds of 6), two rows per wave, four on
+// wide matrices (rounds padded to 4 or 8 blocks had cost, measured against
+// exact rounds on MI355X: Q4_K 5120 x 13824 at M = 1 10.2 -> 8.8 us, Q6_K at
+// M = 2 17.1 -> 12.8 us, 5120 x 5120 8.6 -> 6.8 us).  Wider M takes one or two blocks per
 // round (the activation registers grow with M) and four rows per wave on
 // wide matrices (Q4_K at M = 4 on 12288 x 4096: 11.6 -> 10.1 us with two).
 template <int M>
@@ -568,13 +571,21 @@ static hipError_t launch_q4k_m(const uint8_t *w_qs, const uint8_t *w_hdr, int N,
   const int per_lane = ((K >> 5) + kWave - 1) / kWave;
 #define SKINNY_Q4K(R, U) return launch_q4k_mru<M, R, U>(w_qs, w_hdr, N, K, a_qs, a_d, a_s, y, stream)
   if constexpr (M <= 2) {
-    if (per_lane <= 2) {
-      if (N >= 16384) SKINNY_Q4K(4, 2);
-      SKINNY_Q4K(2, 2);
+    // one round of exactly the lane's share of the row up to 8 blocks (a
+    // padding slot costs a block's loads and dots for nothing)
+    switch (per_lane) {
+      case 1:
+      case 2:
+        if (N >= 16384) SKINNY_Q4K(4, 2);
+        SKINNY_Q4K(2, 2);
+      case 3: SKINNY_Q4K(2, 3);
+      case 4: SKINNY_Q4K(2, 4);
+      case 5: SKINNY_Q4K(2, 5);
+      case 6: SKINNY_Q4K(2, 6);
+      case 7: SKINNY_Q4K(2, 7);
+      case 8: SKINNY_Q4K(2, 8);
+      default: SKINNY_Q4K(2, 6);
     }
-    if (per_lane <= 4) SKINNY_Q4K(2, 4);
-    if (per_lane <= 6 || per_lane > 8) SKINNY_Q4K(2, 6);
-    SKINNY_Q4K(2, 8);
   } else {
     if (N >= 16384) SKINNY_Q4K(4, 1);
     SKINNY_Q4K(2, 1);
@@ -590,13 +601,19 @@ static hipError_t launch_q6k_m(const uint8_t *w_ql, const uint8_t *w_qh, const i
 #define SKINNY_Q6K(R, U) \
   return launch_q6k_mru<M, R, U>(w_ql, w_qh, w_sc, w_d, N, K, a_qs, a_d, y, stream)
   if constexpr (M <= 2) {
-    if (per_lane <= 2) {
-      if (M == 2 && N >= 16384) SKINNY_Q6K(4, 2);
-      SKINNY_Q6K(2, 2);
+    switch (per_lane) {           // as Q4_K: one round of exactly the lane's share
+      case 1:
+      case 2:
+        if (M == 2 && N >= 16384) SKINNY_Q6K(4, 2);
+        SKINNY_Q6K(2, 2);
+      case 3: SKINNY_Q6K(2, 3);
+      case 4: SKINNY_Q6K(2, 4);
+      case 5: SKINNY_Q6K(2, 5);
+      case 6: SKINNY_Q6K(2, 6);
+      case 7: SKINNY_Q6K(2, 7);
+      case 8: SKINNY_Q6K(2, 8);
+      default: SKINNY_Q6K(2, 6);
     }
-    if (per_lane <= 4) SKINNY_Q6K(2, 4);
-    if (per_lane <= 6 || per_lane > 8) SKINNY_Q6K(2, 6);
-    SKINNY_Q6K(2, 8);
   } else {
     if (N >= 16384) SKINNY_Q6K(4, 1);
     SKINNY_Q6K(2, 2);

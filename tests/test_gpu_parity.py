@@ -547,6 +547,8 @@ def _q4_k_gate_bound(w_qs, w_hdr, a_qs, a_s):
 # (M, N, K, sc_mask) of the Q4_K exact-integer gate, one or more per route
 Q4K_GATE = [
     (1, 300, 4096, 7), (2, 300, 4096, 7),       # vector kernel
+    (1, 300, 5120, 7), (2, 300, 10240, 3),      # ... rounds of three and five blocks
+    (1, 301, 14336, 3),                         # ... seven
     (1, 1031, 13824, 3), (2, 300, 16384, 3),    # vector kernel, eight blocks per lane
     (1, 300, 20480, 3),                         # vector kernel, rounds of six blocks
     (1, 4096, 13824, 3), (2, 4096, 13824, 3),   # staged kernel, long rows at M <= 2
@@ -741,6 +743,8 @@ def test_mmvq_q6_k_packed_integer_gate_bit_exact(M, N, K, sc_max):
 
 @pytest.mark.parametrize("M,N,K,sc_max", [
     (1, 300, 4096, 2), (4, 300, 4096, 2), (8, 300, 4096, 2),
+    (1, 300, 5120, 2), (2, 300, 10240, 1),      # vector kernel, rounds of three and five
+    (1, 301, 14336, 1),                         # ... seven
     (1, 1031, 13824, 1), (2, 300, 13824, 1),    # vector kernel, eight blocks per lane
     (2, 4100, 13824, 1),                        # staged, long rows at M = 2
     (3, 6000, 4096, 2),                         # staged, one row per wave (mid-width)
