@@ -964,7 +964,9 @@ static hipError_t launch_mru(const uint8_t *w_qs, const uint16_t *w_d, int N, in
 // row in one round (U = blocks per lane, up to 8 = K 16384) -- long rows are
 // otherwise bound by successive memory round trips (7.8 -> 6.3 us for an
 // 11008 x 4096 matrix; with U = 8, 14336 x 4096 9.7 -> 7.7 us and
-// 13824 x 5120 11.9 -> 9.8 us at M = 1).  Up to 12 blocks per lane (K 24576)
+// 13824 x 5120 11.9 -> 9.8 us at M = 1).  The round holds exactly the lane's
+// share (5 or 7 blocks too: a padded slot costs a block's loads and dots;
+// 14336 x 4096 8.2 -> 6.9 us, 10240 x 4096 6.3 -> 5.7 us at M = 1).  Up to 12 blocks per lane (K 24576)
 // two waves split each row, one round of up to 6 blocks each (17408 x 5120
 // 12.8 -> 11.2 us at M = 1, 16.1 -> 14.6 at M = 2); longer rows take rounds
 // of 6, which measured as fast as a split or rounds of 8 there (28672 x 4096
@@ -977,8 +979,10 @@ static hipError_t launch_m(const uint8_t *w_qs, const uint16_t *w_d, int N, int 
     const int per_lane = ((K >> 5) + kWave - 1) / kWave;
     if (per_lane > 12) return launch_mru<M, 2, 6>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
     if (per_lane > 8) return launch_mru<M, 2, 6, 2>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
-    if (per_lane > 6) return launch_mru<M, 2, 8>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
-    if (per_lane > 4) return launch_mru<M, 2, 6>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+    if (per_lane > 7) return launch_mru<M, 2, 8>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+    if (per_lane > 6) return launch_mru<M, 2, 7>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+    if (per_lane > 5) return launch_mru<M, 2, 6>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
+    if (per_lane > 4) return launch_mru<M, 2, 5>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
     if (per_lane > 3) return launch_mru<M, 2, 4>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
     if (per_lane > 2) return launch_mru<M, 2, 3>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);
     return launch_mru<M, 2, 2>(w_qs, w_d, N, K, a_qs, a_d, a_s, y, stream);

@@ -310,7 +310,9 @@ Q4_GATE = [
     (1, 1031, 4096),      # vector kernel, one round of two blocks per lane
     (1, 25000, 4096),     # vector kernel, many workgroups
     (1, 300, 11008),      # vector kernel, six blocks per lane
-    (1, 1031, 13824),     # vector kernel, one round of eight blocks per lane
+    (1, 1031, 13824),     # vector kernel, one round of seven blocks per lane
+    (1, 300, 10240),      # vector kernel, five blocks per lane
+    (2, 301, 14336),      # vector kernel at M = 2, seven blocks per lane
     (1, 300, 20480),      # vector kernel, K split over two waves (six blocks each)
     (1, 1031, 28672),     # vector kernel, rounds of six blocks per lane
     (2, 1031, 4096),      # vector kernel at M = 2
