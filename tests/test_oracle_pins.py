@@ -766,6 +766,9 @@ def test_oracle_thread_count_invariance():
     codes, scales, _ = inputs.nvfp4_weights(N, K, 3)
     w8, cs = inputs.fp8_weights(N, K, 4)
     x = inputs.normal_f16_bits(M, K, 5)
+    k_qs, k_hdr = inputs.q4_k_weights(N, K, 6)
+    q6 = inputs.q6_k_weights(N, K, 7)
+    i_qs, i_hdr = inputs.iq4_xs_weights(N, K, 8)
     prev = oracle.num_threads()
     try:
         outs = []
@@ -773,7 +776,10 @@ def test_oracle_thread_count_invariance():
             oracle.set_num_threads(t)
             outs.append((oracle.mmvq_q4_0(w_qs, w_d, a_qs, a_d, a_s),
                          oracle.gemv_nvfp4_w4a16(codes, scales, 0.75, x)[0],
-                         oracle.gemv_fp8_w8a16(w8, cs, x)[0]))
+                         oracle.gemv_fp8_w8a16(w8, cs, x)[0],
+                         oracle.mmvq_q4_k(k_qs, k_hdr, a_qs, a_d, a_s),
+                         oracle.mmvq_q6_k(*q6, a_qs, a_d),
+                         oracle.mmvq_iq4_xs(i_qs, i_hdr, a_qs, a_d)))
         for a, b in zip(*outs):
             assert np.array_equal(a, b)
     finally:
